@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs for tree attention and the E2E-TV loss.
+
+The generator only draws numbers and lays them out; it performs none of the
+scoring method's arithmetic.  Tensors are drawn with ``torch`` on the device
+they are requested on (CPU for oracle-only tests, ``cuda`` for GPU runs, where
+multi-GB logits would be slow to draw on the host).  The same (config, seed,
+device) always yields the same bytes; a GPU parity test that needs oracle
+values copies the generated inputs to the host, so both sides see identical
+bytes.
+
+Distributions (the workload descriptions give sizes and value laws, no data):
+  * trunk K/V, branch q/k/v: i.i.d. N(0, 1), rounded to the workload dtype.
+    The trunk key cache is taken to hold keys already rotated at their trunk
+    positions; an i.i.d. isotropic Gaussian is invariant under the pairwise
+    rotations, so drawing it directly is distributionally identical to
+    rotating raw N(0, 1) keys.
+  * anchors: per trunk, B distinct positions drawn uniformly without
+    replacement from the response part [P, L-1), left unsorted.
+  * parent map / semantic positions: the config's literal tree shape;
+    pos = anchor + 1 + depth.
+  * logits: see ``LossConfig.recipe``.
+bf16 values are round-to-nearest-even conversions of fp32 draws.
+"""
+
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+import torch
+
+from .configs import AttnConfig, LossConfig
+
+_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+# tensor ids for seed derivation
+_T_TRUNK_K, _T_TRUNK_V, _T_Q, _T_K, _T_V, _T_ANCH = 1, 2, 3, 4, 5, 6
+_T_DRAFT, _T_TARGET, _T_PERM, _T_PEAK = 11, 12, 13, 14
+
+
+def derive_seed(seed: int, cid: int, tensor: int) -> int:
+    """63-bit seed for one tensor of one workload."""
+    st = np.random.SeedSequence([seed, cid, tensor]).generate_state(2, dtype=np.uint32)
+    return int((int(st[0]) << 31) ^ int(st[1])) & ((1 << 63) - 1)
+
+
+def _gen(device, seed: int, cid: int, tensor: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(derive_seed(seed, cid, tensor))
+    return g
+
+
+def _normal(shape, dtype, device, g, chunk_rows: int = 0) -> torch.Tensor:
+    """N(0,1) draws in fp32, rounded to dtype; drawn in row chunks along dim 0
+    so huge tensors never need an fp32 copy of themselves."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    if chunk_rows <= 0 or shape[0] <= chunk_rows:
+        out.copy_(torch.randn(shape, generator=g, device=device, dtype=torch.float32))
+        return out
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        sub = (r1 - r0,) + tuple(shape[1:])
+        out[r0:r1].copy_(torch.randn(sub, generator=g, device=device, dtype=torch.float32))
+    return out
+
+
+def anchors_for(cfg: AttnConfig, seed: int, cid: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(derive_seed(seed, cid, _T_ANCH)))
+    a = np.empty((cfg.T, cfg.B), dtype=np.int32)
+    for t in range(cfg.T):
+        a[t] = rng.choice(np.arange(cfg.P, cfg.L - 1), size=cfg.B, replace=False)
+    return a
+
+
+def gen_attn(cfg: AttnConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[str, torch.Tensor]:
+    """Tree-attention inputs.
+
+    Layouts (row-major): trunk_k/trunk_v [T][L][Hkv][D]; q [T][B][Wn][Hq][D];
+    k/v [T][B][Wn][Hkv][D]; anchors [T][B]; parent/pos [T][B][Wn] (int32).
+    """
+    dt = _DT[cfg.dtype]
+    T, L, B, Wn, Hq, Hkv, D = cfg.T, cfg.L, cfg.B, cfg.Wn, cfg.Hq, cfg.Hkv, cfg.D
+    out = {
+        "trunk_k": _normal((T * L, Hkv, D), dt, device, _gen(device, seed, cid, _T_TRUNK_K), 8192).view(T, L, Hkv, D),
+        "trunk_v": _normal((T * L, Hkv, D), dt, device, _gen(device, seed, cid, _T_TRUNK_V), 8192).view(T, L, Hkv, D),
+        "q": _normal((T, B, Wn, Hq, D), dt, device, _gen(device, seed, cid, _T_Q)),
+        "k": _normal((T, B, Wn, Hkv, D), dt, device, _gen(device, seed, cid, _T_K)),
+        "v": _normal((T, B, Wn, Hkv, D), dt, device, _gen(device, seed, cid, _T_V)),
+    }
+    anch = anchors_for(cfg, seed, cid)
+    parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()
+    pos = (anch[:, :, None] + 1 + np.asarray(cfg.depth, np.int32)[None, None, :]).astype(np.int32)
+    out["anchors"] = torch.from_numpy(anch).to(device)
+    out["parent"] = torch.from_numpy(parent).to(device)
+    out["pos"] = torch.from_numpy(pos).to(device)
+    return out
+
+
+def stress_classes(cfg: LossConfig, seed: int, cid: int) -> np.ndarray:
+    """Row classes for the "stress" recipe: 0 identical, 1 disjoint, 2 noise."""
+    N = cfg.N
+    rng = np.random.Generator(np.random.PCG64(derive_seed(seed, cid, _T_PERM)))
+    perm = rng.permutation(N)
+    cls = np.full(N, 2, dtype=np.int8)
+    cls[perm[: N // 2]] = 0
+    cls[perm[N // 2: N // 2 + N // 4]] = 1
+    return cls
+
+
+def gen_loss(cfg: LossConfig, seed: int = 0, device="cpu", cid: int = 0,
+             chunk_rows: int = 256) -> Dict[str, torch.Tensor]:
+    """E2E-TV inputs: draft/target logits [R][Wn][V] and parent [R][Wn].
+
+    Row n = r*Wn + j holds the drafter's (draft) and the target's (target)
+    next-token logits for node j of branch r."""
+    dt = _DT[cfg.dtype]
+    N, V = cfg.N, cfg.V
+    gz = _gen(device, seed, cid, _T_DRAFT)
+    gt = _gen(device, seed, cid, _T_TARGET)
+    draft = torch.empty((N, V), dtype=dt, device=device)
+    target = torch.empty((N, V), dtype=dt, device=device)
+    cls = stress_classes(cfg, seed, cid) if cfg.recipe == "stress" else None
+    peaks = None
+    if cls is not None:
+        rng = np.random.Generator(np.random.PCG64(derive_seed(seed, cid, _T_PEAK)))
+        a = rng.integers(0, V, size=N)
+        b = (a + 1 + rng.integers(0, V - 1, size=N)) % V  # b != a
+        peaks = (a, b)
+    for r0 in range(0, N, chunk_rows):
+        r1 = min(N, r0 + chunk_rows)
+        n = r1 - r0
+        e1 = torch.randn((n, V), generator=gz, device=device, dtype=torch.float32)
+        e2 = torch.randn((n, V), generator=gt, device=device, dtype=torch.float32)
+        if cfg.recipe == "indep":
+            z, t = cfg.sd * e1, cfg.sd * e2
+        elif cfg.recipe == "noise":
+            z, t = e1, e1 + e2
+        elif cfg.recipe == "rho":
+            z = cfg.sd * e1
+            t = cfg.rho * z + cfg.sd * float(np.sqrt(1.0 - cfg.rho ** 2)) * e2
+        elif cfg.recipe == "stress":
+            z, t = e1, e1 + e2
+            c = torch.from_numpy(cls[r0:r1]).to(device)
+            dis = torch.nonzero(c == 1).flatten()
+            if dis.numel():
+                t[dis] = e2[dis]
+                ia = torch.from_numpy(peaks[0][r0:r1]).to(device)[dis]
+                ib = torch.from_numpy(peaks[1][r0:r1]).to(device)[dis]
+                z[dis, ia] += cfg.peak
+                t[dis, ib] += cfg.peak
+        else:
+            raise ValueError(cfg.recipe)
+        draft[r0:r1] = z.to(dt)
+        target[r0:r1] = t.to(dt)
+        if cls is not None:
+            same = torch.nonzero(torch.from_numpy(cls[r0:r1]).to(device) == 0).flatten()
+            if same.numel():
+                target[r0 + same] = draft[r0 + same]
+    parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (cfg.R, cfg.Wn)).copy()
+    return {
+        "draft": draft.view(cfg.R, cfg.Wn, V),
+        "target": target.view(cfg.R, cfg.Wn, V),
+        "parent": torch.from_numpy(parent).to(device),
+    }
