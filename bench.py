@@ -1,0 +1,216 @@
+"""Benchmark of one SpecOPD branch-scoring step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic inputs already
+resident in HBM: tree-masked attention of every branch node against the trunk
+cache (specopd_tree_attn_fwd), then the E2E-TV surrogate forward and gradient
+over the scored rows (specopd_e2etv_fwd_bwd).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+Prints one JSON line.  `value` is scored branch rows per second through the
+whole step.  `roofline` describes the kernel that takes most of the step,
+timed with HIP events on the stream it runs on; `roofline_attn` /
+`roofline_loss` give both parts.  `cpu_baseline` times the fp64 CPU oracle on
+a bounded sample of the same workload (reported, not a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "branch scoring rows/s (tree attn, MFMA util) + E2E-TV rows/s (HBM GB/s)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+
+
+def attn_flops(cfg, anchors):
+    """Algorithmic attention FLOPs: QK^T and PV over unmasked keys only,
+    4*D*Hq per (row, visible key); node j sees a_b + 1 trunk keys and
+    depth(j) + 1 branch keys."""
+    import numpy as np
+    depth = np.asarray(cfg.depth, np.float64)
+    a = anchors.astype(np.float64)                       # [T][B]
+    keys = (a[:, :, None] + 2.0 + depth[None, None, :]).sum()
+    return 4.0 * cfg.D * cfg.Hq * keys
+
+
+def loss_bytes(cfg, grad_bytes=4):
+    """Algorithmic E2E-TV bytes: read draft and target once, write the
+    gradient once, plus 12 bytes of per-row scalars."""
+    s_in = 2 if cfg.dtype == "bf16" else 4
+    return cfg.N * cfg.V * (2 * s_in + grad_bytes) + 12 * cfg.N
+
+
+def cpu_baseline(wl, attn_inp_cpu, loss_inp_cpu, budget_s=20.0):
+    """The fp64 oracle as it stands, single BLAS thread, on a bounded sample:
+    whole branches (every node, every head) of attention and their loss rows.
+    Returns scored rows per second."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    rows = 0
+    t_total = 0.0
+    nb = 0
+    with threadpool_limits(limits=1):
+        cfg = wl.attn if wl.attn is not None else None
+        lc = wl.loss
+        R = lc.R
+        order = np.random.default_rng(0).permutation(R)
+        for r in order:
+            t0 = time.perf_counter()
+            if cfg is not None:
+                t, b = divmod(int(r), cfg.B)
+                if t < cfg.T:
+                    c = attn_inp_cpu
+                    oracle.tree_attention(c["trunk_k"], c["trunk_v"], c["q"], c["k"], c["v"],
+                                          c["anchors"], c["parent"], c["pos"], branches=[(t, b)])
+            d = loss_inp_cpu
+            oracle.e2etv_branch(d["draft"][r], d["target"][r], d["parent"][r].numpy(), float(lc.N))
+            t_total += time.perf_counter() - t0
+            rows += lc.Wn
+            nb += 1
+            if t_total >= budget_s or nb >= R:
+                break
+    return rows / t_total, nb, t_total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="1..5 (default: the 8B-shaped layer)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU: trunks and whole branches would shard across GPUs, "
+              "see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import speculative_decoding_drafter_amd as sd
+    from synthetic import WORKLOADS, gen_attn, gen_loss
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    wl = WORKLOADS[args.workload]
+    torch.manual_seed(args.seed)
+
+    ai = gen_attn(wl.attn, args.seed, device=dev, cid=wl.cid) if wl.attn is not None else None
+    li = gen_loss(wl.loss, args.seed, device=dev, cid=wl.cid)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    if ai is not None:
+        ac = wl.attn
+        adesc = sd.tree_attn_desc(ac.T, ac.L, ac.B, ac.Wn, ac.Hq, ac.Hkv, ac.D, ai["q"].dtype)
+        aws = sd.workspace(sd.specopd_tree_attn_workspace_size(adesc), dev)
+        aout = torch.empty_like(ai["q"])
+    lc = wl.loss
+    ldesc = sd.e2etv_desc(lc.R, lc.Wn, lc.V, li["draft"].dtype, torch.float32)
+    lws = sd.workspace(sd.specopd_e2etv_workspace_size(ldesc), dev)
+    alpha = torch.empty((lc.R, lc.Wn), dtype=torch.float32, device=dev)
+    prefix = torch.empty_like(alpha)
+    loss = torch.empty(3, dtype=torch.float64, device=dev)
+    grad = torch.empty((lc.R, lc.Wn, lc.V), dtype=torch.float32, device=dev)
+
+    def attn_call():
+        sd.specopd_tree_attn_fwd(adesc, ai["trunk_k"], ai["trunk_v"], ai["q"], ai["k"], ai["v"],
+                                 ai["anchors"], ai["parent"], ai["pos"], aout, aws)
+
+    def loss_call():
+        sd.specopd_e2etv_fwd_bwd(ldesc, li["draft"], li["target"], li["parent"], alpha, prefix,
+                                 loss, grad, lws)
+
+    def step(ev=None):
+        if ai is not None:
+            if ev is not None:
+                ev[0].record(stream)
+            attn_call()
+            if ev is not None:
+                ev[1].record(stream)
+        loss_call()
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if ai is not None else 0.0
+    loss_ms = float(np.mean([(e[1] if ai is not None else e[0]).elapsed_time(e[2]) for e in evs])) \
+        if ai is not None else float(np.mean([t_start.elapsed_time(t_end) / args.steps]))
+
+    N = lc.N
+    rows_per_s = N / (ms_step / 1e3)
+    res = {
+        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if lc.dtype == "bf16" else "f32", "data": "synthetic",
+    }
+    conf = {"workload": f"{wl.name} (workload {wl.cid})", "scored_rows": N,
+            "loss": {"R": lc.R, "Wn": lc.Wn, "V": lc.V, "logits": lc.dtype, "grad": "f32"}}
+    lb = loss_bytes(lc)
+    loss_gbs = lb / (loss_ms / 1e3) / 1e9
+    roof_loss = {"bound": "hbm", "achieved": loss_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": loss_gbs / HBM_PEAK_GBS, "traffic": None,
+                 "kernel": "specopd_e2etv_fwd_bwd", "ms": loss_ms, "alg_bytes": lb}
+    roofs = {"loss": roof_loss}
+    if ai is not None:
+        ac = wl.attn
+        conf["attn"] = {"T": ac.T, "L": ac.L, "B": ac.B, "Wn": ac.Wn, "Hq": ac.Hq, "Hkv": ac.Hkv,
+                        "D": ac.D, "dtype": ac.dtype}
+        fl = attn_flops(ac, ai["anchors"].cpu().numpy())
+        tf = fl / (attn_ms / 1e3) / 1e12
+        peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
+        roofs["attn"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                         "frac": tf / peak, "traffic": None, "kernel": "specopd_tree_attn_fwd",
+                         "ms": attn_ms, "alg_flops": fl}
+        res["attn_rows_per_s"] = ac.rows / (attn_ms / 1e3)
+    res["loss_rows_per_s"] = N / (loss_ms / 1e3)
+    res["config"] = conf
+    dom = max(roofs, key=lambda k: roofs[k]["ms"])
+    res["roofline"] = roofs[dom]
+    res["roofline_loss"] = roofs["loss"]
+    if "attn" in roofs:
+        res["roofline_attn"] = roofs["attn"]
+
+    if not args.no_cpu:
+        ai_c = {k: v.cpu() for k, v in ai.items()} if ai is not None else None
+        li_c = {k: v.cpu() for k, v in li.items()}
+        v_cpu, nb, secs = cpu_baseline(wl, ai_c, li_c, args.cpu_budget)
+        res["cpu_baseline"] = {
+            "value": v_cpu, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nb} whole branches ({nb * lc.Wn} scored rows: tree attention over all "
+                      f"heads + E2E-TV fwd/grad), fp64 numpy, 1 BLAS thread, {secs:.1f} s",
+        }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+"""MI355X-native branch-parallel target scoring for SpecOPD.
+
+The computation lives in libspecopd.so (HIP kernels for gfx950 behind the C
+ABI of include/specopd.h); this package is its thin Python binding.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTS, LIB, LIB_PATH, SpecopdError, TreeAttnDesc, E2etvDesc, SPECOPD_OK,
+    SPECOPD_ERR_INVALID_ARGUMENT, SPECOPD_ERR_UNSUPPORTED, SPECOPD_ERR_WORKSPACE, SPECOPD_ERR_HIP,
+    SPECOPD_ERR_DEVICE_VALIDATION, SPECOPD_F32, SPECOPD_BF16, status_string, specopd_version,
+    tree_attn_desc, e2etv_desc, specopd_tree_attn_workspace_size, specopd_tree_attn_fwd,
+    specopd_tree_attn_device_status, specopd_e2etv_workspace_size, specopd_e2etv_fwd_bwd,
+    specopd_e2etv_device_status, workspace, tree_attn, e2etv,
+)

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI front end (specopd_api.cpp) and the
+// kernel launchers (*.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/specopd.h"
+
+namespace specopd {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- tree attention
+// Workspace layout (offsets in bytes, each 256-aligned):
+//   anc        uint64 [T*B*Wn]   ancestor bitmask of every node (self included)
+//   branch_ok  int32  [T*B]      1 = well formed, 0 = malformed (outputs NaN)
+//   split      fp32 partials for the split-key path (see tree_attn_mfma.hip)
+struct TreeAttnWs {
+  size_t anc, branch_ok, order, partial_o, partial_ml, total;
+};
+TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d);
+
+struct TreeAttnArgs {
+  const void *trunk_k, *trunk_v, *q, *k, *v;
+  const int32_t *anchors, *parent, *pos;
+  void* out;
+  char* ws;
+  float rope_base, scale;
+};
+hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- E2E-TV
+// Workspace layout:
+//   rowstat    float4 [N]  (-lse2 draft, -lse2 target, alpha, G) per row
+//   coef       float  [N]  grad_scale * dLoss/dalpha per row
+//   numer      double [R]  sum of prefix products of each branch
+//   branch_ok  int32  [R]
+struct E2etvWs {
+  size_t rowstat, coef, numer, branch_ok, total;
+};
+E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d);
+
+struct E2etvArgs {
+  const void *draft, *target;
+  const int32_t* parent;
+  float *alpha_out, *prefix_out;
+  double* loss_out;
+  void* grad;
+  char* ws;
+};
+hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s);
+
+}  // namespace specopd

@@ -1,0 +1,234 @@
+// Tree-masked GQA attention of branch nodes against a prefilled trunk cache:
+// planning, rotary embedding of the branch queries/keys, and the fp32-math
+// path (used for fp32 inputs, and for bf16 inputs whose head size the matrix
+// core path does not cover).
+//
+// Mask (jaehun.me review of SpecOPD, §3.2(a), Eq. 5): node j of branch b
+// reads trunk positions 0..a_b and the nodes on its own parent chain, itself
+// included.  Rotary embedding at the semantic position a_b + 1 + depth(j)
+// (rustineverything.app summary, §2.1), rotate-half pairing (i, i + D/2),
+// angle pos * base^(-2i/D).
+#include <math.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace specopd {
+
+// ---------------------------------------------------------------- planning
+
+// One thread per branch: validate the anchor, the parent map and the semantic
+// positions, and record each node's ancestor bitmask (bit k set when node k
+// is the node itself or one of its ancestors; depth = popcount - 1).
+__global__ void tree_plan_kernel(const int32_t* __restrict__ anchors,
+                                 const int32_t* __restrict__ parent,
+                                 const int32_t* __restrict__ pos, int TB, int Wn, int L,
+                                 uint64_t* __restrict__ anc, int32_t* __restrict__ branch_ok) {
+  const int tb = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tb >= TB) return;
+  const int a = anchors[tb];
+  bool ok = (a >= 0) && (a < L);
+  const int32_t* par = parent + size_t(tb) * Wn;
+  const int32_t* ps = pos + size_t(tb) * Wn;
+  uint64_t* an = anc + size_t(tb) * Wn;
+  for (int j = 0; j < Wn; ++j) {
+    const int p = par[j];
+    uint64_t m = uint64_t(1) << j;
+    if (p >= 0 && p < j) {
+      m |= an[p];
+    } else if (p != -1) {
+      ok = false;
+    }
+    an[j] = m;
+    const int depth = __popcll(m) - 1;
+    if (ps[j] != a + 1 + depth) ok = false;
+  }
+  branch_ok[tb] = ok ? 1 : 0;
+}
+
+// ---------------------------------------------------------------- rotary
+
+// Rotates every branch query and key at its node's semantic position.  One
+// thread per (node, head, pair i).  The angle is formed and reduced in fp64:
+// positions reach tens of thousands of radians, where an fp32 angle would be
+// off by ~1e-3.  Queries are also multiplied by `qmul`.
+template <typename T, typename O>
+__global__ void rope_branch_kernel(const T* __restrict__ x, const int32_t* __restrict__ pos,
+                                   int nodes, int H, int D, double log2_base, float qmul,
+                                   O* __restrict__ out) {
+  const int half = D >> 1;
+  const size_t total = size_t(nodes) * H * half;
+  for (size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
+       idx += size_t(gridDim.x) * blockDim.x) {
+    const int i = int(idx % half);
+    const size_t nh = idx / half;                 // node * H + head
+    const size_t node = nh / H;
+    const double theta = exp2(-(2.0 * i / D) * log2_base);
+    const double ang = double(pos[node]) * theta;
+    double sn, cs;
+    sincos(ang, &sn, &cs);
+    const T* src = x + nh * D;
+    const float x1 = load_f32(src + i), x2 = load_f32(src + i + half);
+    const float c = float(cs), s = float(sn);
+    O* dst = out + nh * D;
+    store_f32(dst + i, (x1 * c - x2 * s) * qmul);
+    store_f32(dst + i + half, (x2 * c + x1 * s) * qmul);
+  }
+}
+
+// ---------------------------------------------------------------- fp32 path
+
+// One workgroup per (trunk, branch, kv head); each wave takes rows
+// (node j, head h in the kv group) in turn; lanes take keys 64 at a time for
+// the scores and dimensions for the weighted sum.  Online softmax in fp32.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tree_attn_generic_kernel(
+    const T* __restrict__ trunk_k, const T* __restrict__ trunk_v, const float* __restrict__ qr,
+    const float* __restrict__ kr, const T* __restrict__ v, const int32_t* __restrict__ anchors,
+    const uint64_t* __restrict__ anc, const int32_t* __restrict__ branch_ok, int B, int L,
+    int Wn, int Hq, int Hkv, T* __restrict__ out) {
+  constexpr int DL = D / 64;  // dims per lane
+  __shared__ float qs[4][D];
+  __shared__ float pb[4][64];
+  const int G = Hq / Hkv;
+  const int g = blockIdx.x % Hkv;
+  const int tb = blockIdx.x / Hkv;  // t*B + b
+  const int t = tb / B;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int a = anchors[tb];
+  const bool ok = branch_ok[tb] != 0;
+  const size_t kv_stride = size_t(Hkv) * D;  // between consecutive trunk positions
+  const T* tk = trunk_k + size_t(t) * L * kv_stride + size_t(g) * D;
+  const T* tv = trunk_v + size_t(t) * L * kv_stride + size_t(g) * D;
+  const float* kb = kr + size_t(tb) * Wn * kv_stride + size_t(g) * D;
+  const T* vb = v + size_t(tb) * Wn * kv_stride + size_t(g) * D;
+
+  for (int r = w; r < Wn * G; r += 4) {
+    const int j = r / G;
+    const int h = g * G + (r - j * G);
+    const size_t orow = (size_t(tb) * Wn + j) * Hq + h;
+    if (!ok) {
+      for (int i = 0; i < DL; ++i) store_f32(out + orow * D + lane + 64 * i, __builtin_nanf(""));
+      continue;
+    }
+    const float* qrow = qr + orow * D;
+    for (int i = 0; i < DL; ++i) qs[w][lane + 64 * i] = qrow[lane + 64 * i];
+    __builtin_amdgcn_wave_barrier();
+    float m = kNegInf, l = 0.f, o[DL];
+#pragma unroll
+    for (int i = 0; i < DL; ++i) o[i] = 0.f;
+    const uint64_t am = anc[size_t(tb) * Wn + j];
+    // key tiles: trunk 0..a, then the branch's own nodes (one tile, Wn <= 64)
+    const int ntrunk_tiles = (a + 1 + 63) / 64;
+    for (int tile = 0; tile <= ntrunk_tiles; ++tile) {
+      const bool branch_tile = tile == ntrunk_tiles;
+      const int key = branch_tile ? lane : tile * 64 + lane;
+      const bool valid = branch_tile ? (lane < Wn && ((am >> lane) & 1)) : (key <= a);
+      float sc = kNegInf;
+      if (valid) {
+        float acc = 0.f;
+        if (branch_tile) {
+          const float* kk = kb + size_t(key) * kv_stride;
+          for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qs[w][d], kk[d], acc);
+        } else {
+          const T* kk = tk + size_t(key) * kv_stride;
+          for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qs[w][d], load_f32(kk + d), acc);
+        }
+        sc = acc;  // queries carry the score scale
+      }
+      const float tmax = wave_max(sc);
+      const float mn = fmaxf(m, tmax);
+      const float p = valid ? __expf(sc - mn) : 0.f;
+      const float corr = (m == kNegInf) ? 0.f : __expf(m - mn);
+      l = l * corr + wave_sum(p);
+#pragma unroll
+      for (int i = 0; i < DL; ++i) o[i] *= corr;
+      m = mn;
+      pb[w][lane] = p;
+      __builtin_amdgcn_wave_barrier();
+      const int nk = branch_tile ? Wn : min(64, a + 1 - tile * 64);
+      for (int k = 0; k < nk; ++k) {
+        const float pk = pb[w][k];
+        if (pk != 0.f) {
+          const T* vv = branch_tile ? vb + size_t(k) * kv_stride : tv + size_t(tile * 64 + k) * kv_stride;
+#pragma unroll
+          for (int i = 0; i < DL; ++i) o[i] = __builtin_fmaf(pk, load_f32(vv + lane + 64 * i), o[i]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int i = 0; i < DL; ++i) store_f32(out + orow * D + lane + 64 * i, o[i] * inv);
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
+  const size_t TB = size_t(d.T) * d.B, nodes = TB * d.Wn;
+  TreeAttnWs w{};
+  size_t off = 0;
+  w.anc = off;        off = align_up(off + nodes * sizeof(uint64_t), 256);
+  w.branch_ok = off;  off = align_up(off + TB * sizeof(int32_t), 256);
+  w.order = off;      off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * sizeof(float), 256);
+  w.partial_o = off;  // rotated q then rotated k (fp32), see launch_tree_attn
+  w.partial_ml = off;
+  w.total = off;
+  return w;
+}
+
+template <typename T>
+static hipError_t launch_generic(const specopd_tree_attn_desc& d, const TreeAttnArgs& a,
+                                 const uint64_t* anc, const int32_t* ok, float* qr, float* kr,
+                                 hipStream_t s) {
+  const int TB = d.T * d.B;
+  const unsigned blocks = unsigned(TB) * d.Hkv;
+#define SPECOPD_GEN(DD)                                                                         \
+  tree_attn_generic_kernel<T, DD><<<blocks, 256, 0, s>>>(                                      \
+      static_cast<const T*>(a.trunk_k), static_cast<const T*>(a.trunk_v), qr, kr,              \
+      static_cast<const T*>(a.v), a.anchors, anc, ok, d.B, d.L, d.Wn, d.Hq, d.Hkv,             \
+      static_cast<T*>(a.out))
+  switch (d.D) {
+    case 64: SPECOPD_GEN(64); break;
+    case 128: SPECOPD_GEN(128); break;
+    case 256: SPECOPD_GEN(256); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef SPECOPD_GEN
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_rope_fp32(const specopd_tree_attn_desc& d, const TreeAttnArgs& a,
+                                   float* qr, float* kr, hipStream_t s) {
+  const int nodes = d.T * d.B * d.Wn;
+  const double lb = log2(double(a.rope_base));
+  auto grid = [](size_t n) { return unsigned(std::min<size_t>((n + 255) / 256, 65536)); };
+  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.Hq * d.D / 2), 256, 0, s>>>(
+      static_cast<const T*>(a.q), a.pos, nodes, d.Hq, d.D, lb, a.scale, qr);
+  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.Hkv * d.D / 2), 256, 0, s>>>(
+      static_cast<const T*>(a.k), a.pos, nodes, d.Hkv, d.D, lb, 1.0f, kr);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s) {
+  const TreeAttnWs L = tree_attn_ws_layout(d);
+  uint64_t* anc = reinterpret_cast<uint64_t*>(a.ws + L.anc);
+  int32_t* ok = reinterpret_cast<int32_t*>(a.ws + L.branch_ok);
+  const int TB = d.T * d.B;
+  tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);
+  float* qr = reinterpret_cast<float*>(a.ws + L.order);
+  float* kr = qr + size_t(TB) * d.Wn * d.Hq * d.D;
+  hipError_t e;
+  if (d.dtype == SPECOPD_BF16) {
+    if ((e = launch_rope_fp32<uint16_t>(d, a, qr, kr, s)) != hipSuccess) return e;
+    return launch_generic<uint16_t>(d, a, anc, ok, qr, kr, s);
+  }
+  if ((e = launch_rope_fp32<float>(d, a, qr, kr, s)) != hipSuccess) return e;
+  return launch_generic<float>(d, a, anc, ok, qr, kr, s);
+}
+
+}  // namespace specopd

@@ -1,0 +1,163 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function include/specopd.h declares, and rejects every host-detectable error
+before touching the GPU (so these calls are safe here).  No compute call is
+made: every call below carries at least one invalid argument."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_drafter_amd as sd
+from speculative_decoding_drafter_amd import _lib
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specopd.h")
+
+FAKE = 0x7f0000000000  # 16-byte aligned stand-in pointer, never dereferenced
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(specopd_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(sd.LIB, n), n
+        assert n in _lib.EXPORTS
+    assert set(_lib.EXPORTS) == set(names)
+
+
+def test_version_and_status_strings():
+    assert sd.specopd_version() == 1
+    assert sd.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert sd.status_string(s) not in ("ok", "unknown status")
+
+
+def _tdesc(**kw):
+    base = dict(T=1, L=128, B=4, Wn=4, Hq=8, Hkv=2, D=128, dtype=sd.SPECOPD_BF16)
+    base.update(kw)
+    return sd.tree_attn_desc(**base)
+
+
+def _tcall(desc, ws_bytes=1 << 30, **over):
+    args = dict(trunk_k=FAKE, trunk_v=FAKE + 16, q=FAKE + 32, k=FAKE + 48, v=FAKE + 64,
+                anchors=FAKE + 80, parent=FAKE + 96, pos=FAKE + 112, out=FAKE + 128,
+                ws=FAKE + 144)
+    args.update(over)
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_tree_attn_fwd(
+        ctypes.byref(desc), P(args["trunk_k"]), P(args["trunk_v"]), P(args["q"]), P(args["k"]),
+        P(args["v"]), P(args["anchors"]), P(args["parent"]), P(args["pos"]), P(args["out"]),
+        P(args["ws"]), ctypes.c_size_t(ws_bytes), P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 96, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("D", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("Hq", 7, sd.SPECOPD_ERR_INVALID_ARGUMENT),     # Hq % Hkv != 0
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("Wn", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("B", -3, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("dtype", 7, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("rope_base", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+])
+def test_tree_desc_errors(field, value, code):
+    d = _tdesc()
+    setattr(d, field, value)
+    assert _tcall(d) == code
+    n = ctypes.c_size_t(0)
+    assert sd.LIB.specopd_tree_attn_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(out=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(anchors=FAKE + 4), sd.SPECOPD_ERR_INVALID_ARGUMENT),   # misaligned
+    (dict(out=FAKE), sd.SPECOPD_ERR_INVALID_ARGUMENT),           # out aliases trunk_k
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+    (dict(ws=FAKE + 152), sd.SPECOPD_ERR_WORKSPACE),             # misaligned workspace
+])
+def test_tree_pointer_errors(over, code):
+    assert _tcall(_tdesc(), **over) == code
+
+
+def test_tree_workspace_too_small():
+    d = _tdesc()
+    need = sd.specopd_tree_attn_workspace_size(d)
+    assert need > 0
+    assert _tcall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+
+
+def test_null_desc():
+    n = ctypes.c_size_t(0)
+    assert sd.LIB.specopd_tree_attn_workspace_size(None, ctypes.byref(n)) == sd.SPECOPD_ERR_INVALID_ARGUMENT
+    assert sd.LIB.specopd_e2etv_workspace_size(None, ctypes.byref(n)) == sd.SPECOPD_ERR_INVALID_ARGUMENT
+
+
+def _edesc(**kw):
+    base = dict(R=4, Wn=7, V=151936, logits_dtype=sd.SPECOPD_BF16, grad_dtype=sd.SPECOPD_F32)
+    base.update(kw)
+    return sd.e2etv_desc(**base)
+
+
+def _ecall(desc, ws_bytes=1 << 30, **over):
+    args = dict(draft=FAKE, target=FAKE + 16, parent=FAKE + 32, alpha=FAKE + 48, prefix=FAKE + 64,
+                loss=FAKE + 80, grad=FAKE + 96, ws=FAKE + 112)
+    args.update(over)
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_e2etv_fwd_bwd(
+        ctypes.byref(desc), P(args["draft"]), P(args["target"]), P(args["parent"]),
+        P(args["alpha"]), P(args["prefix"]), P(args["loss"]), P(args["grad"]), P(args["ws"]),
+        ctypes.c_size_t(ws_bytes), P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("V", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("R", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("logits_dtype", 3, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("grad_dtype", -1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("grad_scale", float("inf"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+])
+def test_e2etv_desc_errors(field, value, code):
+    d = _edesc()
+    setattr(d, field, value)
+    assert _ecall(d) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(draft=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(loss=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(parent=FAKE + 36), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(grad=FAKE), sd.SPECOPD_ERR_INVALID_ARGUMENT),          # grad aliases draft
+    (dict(alpha=FAKE + 50), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+])
+def test_e2etv_pointer_errors(over, code):
+    assert _ecall(_edesc(), **over) == code
+
+
+def test_e2etv_workspace_size_and_too_small():
+    d = _edesc()
+    need = sd.specopd_e2etv_workspace_size(d)
+    assert need >= 4 * 7 * (16 + 4)
+    assert _ecall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+
+
+def test_status_readback_rejects_bad_workspace_before_gpu():
+    d = _tdesc()
+    bad = ctypes.c_int32(0)
+    assert sd.LIB.specopd_tree_attn_device_status(ctypes.byref(d), ctypes.c_void_p(None), 0,
+                                                  ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE
+    e = _edesc()
+    assert sd.LIB.specopd_e2etv_device_status(ctypes.byref(e), ctypes.c_void_p(FAKE), 1,
+                                              ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE

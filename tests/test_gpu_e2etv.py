@@ -1,0 +1,177 @@
+"""E2E-TV on the GPU through the C ABI against the fp64 oracle.
+
+Element-by-element at sizes the oracle finishes in seconds (full 151,936
+vocabulary rows, ragged vocabularies, every recipe, trees), and at the full
+workload sizes on sampled branches (a branch's alpha, prefix products and
+gradient depend only on that branch and the global count) plus the loss
+identity loss = 1 - sum(prefix)/count."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import speculative_decoding_drafter_amd as sd
+from parity import ALPHA_ATOL, check_grad_rows, check_loss
+from synthetic import WORKLOADS, gen_loss, shrink_loss, stress_classes
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _identical_rows(inp):
+    d = inp["draft"].reshape(-1, inp["draft"].shape[-1])
+    t = inp["target"].reshape(-1, inp["target"].shape[-1])
+    return (d == t).all(dim=1).cpu().numpy()
+
+
+def _oracle_q(rows):
+    return np.exp(oracle.log_softmax(rows.detach().cpu().double().numpy()))
+
+
+def _check_full(inp, out, norm_count=0.0, grad_scale=1.0, bf16_grad=False):
+    R, Wn, V = inp["draft"].shape
+    ref = oracle.e2etv(inp["draft"].cpu(), inp["target"].cpu(), inp["parent"].cpu(),
+                       norm_count=norm_count if norm_count > 0 else None, grad_scale=grad_scale)
+    a = out["alpha"].cpu().double().numpy()
+    p = out["prefix"].cpu().double().numpy()
+    loss = out["loss"].cpu().numpy()
+    assert np.abs(a - ref["alpha"]).max() <= ALPHA_ATOL
+    assert np.abs(p - ref["prefix"]).max() <= ALPHA_ATOL
+    check_loss(loss[0], ref["loss"])
+    assert loss[2] == ref["count"]
+    assert abs(loss[1] - ref["numer"]) <= 1e-5 * max(1.0, ref["numer"])
+    if out["grad"] is not None:
+        n = R * Wn
+        check_grad_rows(out["grad"].reshape(n, V).float().cpu().numpy(), ref["grad"].reshape(n, V),
+                        ref["margin"].reshape(n, V), _oracle_q(inp["draft"].reshape(n, V)),
+                        ref["dL_dalpha"].reshape(n), identical=_identical_rows(inp), bf16=bf16_grad)
+    return ref
+
+
+@pytest.mark.parametrize("cid", [1])
+def test_tiny_workload_full(gpu_ok, cid):
+    cfg = WORKLOADS[cid].loss
+    inp = gen_loss(cfg, 0, device=DEV, cid=cid)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)
+
+
+@pytest.mark.parametrize("cid,R,V", [
+    (2, 5, 151936),     # full-vocabulary rows, chains of 8
+    (3, 3, 151936),     # rho = 0.8, sd 3
+    (4, 12, 151936),    # identical / disjoint / noise rows
+    (5, 3, 40000),      # forked tree
+    (2, 4, 10007),      # ragged vocabulary: scalar path
+    (2, 3, 8),          # one vector per row
+    (2, 2, 1),          # single-token vocabulary
+])
+def test_reduced_workloads(gpu_ok, cid, R, V):
+    cfg = shrink_loss(WORKLOADS[cid].loss, R=R, V=V)
+    inp = gen_loss(cfg, 1, device=DEV, cid=cid)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)
+
+
+def test_fp32_ragged_and_scale_and_count(gpu_ok):
+    cfg = shrink_loss(WORKLOADS[1].loss, R=3, V=999)
+    inp = gen_loss(cfg, 2, device=DEV, cid=1)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"], norm_count=40.0, grad_scale=0.25)
+    torch.cuda.synchronize()
+    _check_full(inp, out, norm_count=40.0, grad_scale=0.25)
+
+
+def test_bf16_gradient_output(gpu_ok):
+    cfg = shrink_loss(WORKLOADS[2].loss, R=2, V=151936)
+    inp = gen_loss(cfg, 3, device=DEV, cid=2)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"], grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _check_full(inp, out, bf16_grad=True)
+
+
+def test_neg_inf_logits_and_eq13(gpu_ok):
+    # Eq. 13 worked example padded into a 24-token vocabulary of -inf logits
+    V = 24
+    z = torch.full((1, 2, V), float("-inf"), dtype=torch.float32)
+    t = torch.full((1, 2, V), float("-inf"), dtype=torch.float32)
+    z[0, :, 0] = np.log(0.5); z[0, :, 1] = np.log(0.5)
+    t[0, :, 0] = np.log(0.4); t[0, :, 1] = np.log(0.4); t[0, :, 2] = np.log(0.2)
+    par = torch.tensor([[-1, 0]], dtype=torch.int32)
+    out = sd.e2etv(z.to(DEV), t.to(DEV), par.to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out["alpha"].cpu().numpy(), 0.8, atol=1e-6)
+    assert out["loss"][0].item() == pytest.approx(1 - (0.8 + 0.64) / 2, abs=1e-6)
+    g = out["grad"].cpu().numpy()
+    assert np.all(np.isfinite(g)) and np.all(g[0, :, 3:] == 0.0)
+    inp = {"draft": z.bfloat16(), "target": t.bfloat16(), "parent": par}
+    outb = sd.e2etv(z.bfloat16().to(DEV), t.bfloat16().to(DEV), par.to(DEV))
+    torch.cuda.synchronize()
+    outb = {k: v for k, v in outb.items()}
+    _check_full(inp, outb)
+
+
+def test_malformed_parent_flags_branch(gpu_ok):
+    cfg = shrink_loss(WORKLOADS[2].loss, R=4, V=4096)
+    inp = gen_loss(cfg, 4, device=DEV, cid=2)
+    par = inp["parent"].clone()
+    par[2, 5] = 6          # parent after child
+    out = sd.e2etv(inp["draft"], inp["target"], par)
+    bad = sd.specopd_e2etv_device_status(out["desc"], out["ws"])
+    assert bad == 1
+    a = out["alpha"].cpu().numpy()
+    assert np.all(np.isnan(a[2])) and np.all(np.isfinite(a[[0, 1, 3]]))
+    assert np.isnan(out["loss"][0].item())
+    assert torch.isnan(out["grad"][2]).all() and torch.isfinite(out["grad"][[0, 1, 3]]).all()
+    ok = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    assert sd.specopd_e2etv_device_status(ok["desc"], ok["ws"]) == 0
+
+
+def test_deterministic_bitwise(gpu_ok):
+    cfg = shrink_loss(WORKLOADS[3].loss, R=8, V=151936)
+    inp = gen_loss(cfg, 5, device=DEV, cid=3)
+    a = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    b = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    for key in ("alpha", "prefix", "loss", "grad"):
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_workload2_full_size_full_parity(gpu_ok):
+    cfg = WORKLOADS[2].loss
+    inp = gen_loss(cfg, 0, device=DEV, cid=2)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_full_size_sampled_branches(gpu_ok, cid):
+    cfg = WORKLOADS[cid].loss
+    inp = gen_loss(cfg, 0, device=DEV, cid=cid)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    R, Wn, V = inp["draft"].shape
+    count = float(R * Wn)
+    prefix = out["prefix"].cpu().double().numpy()
+    loss = out["loss"].cpu().numpy()
+    assert np.all(np.isfinite(prefix))
+    # loss identity with the kernel's own prefix products (holds at any size)
+    assert loss[1] == pytest.approx(prefix.sum(), rel=1e-6)
+    assert loss[0] == pytest.approx(1 - loss[1] / count, rel=1e-12)
+    rng = np.random.default_rng(cid)
+    picks = sorted(rng.choice(R, size=6, replace=False).tolist())
+    if cid == 4:  # make sure every row class is sampled
+        cls = stress_classes(cfg, 0, cid).reshape(R, Wn)
+        for c in (0, 1, 2):
+            picks.append(int(np.argwhere((cls == c).any(axis=1))[0, 0]))
+    ident = _identical_rows(inp).reshape(R, Wn)
+    for r in sorted(set(picks)):
+        ref = oracle.e2etv_branch(inp["draft"][r].cpu(), inp["target"][r].cpu(),
+                                  inp["parent"][r].cpu().numpy(), count)
+        assert np.abs(out["alpha"][r].cpu().double().numpy() - ref["alpha"][0]).max() <= ALPHA_ATOL
+        assert np.abs(prefix[r] - ref["prefix"][0]).max() <= ALPHA_ATOL
+        check_grad_rows(out["grad"][r].float().cpu().numpy(), ref["grad"][0], ref["margin"][0],
+                        _oracle_q(inp["draft"][r]), ref["dL_dalpha"][0], identical=ident[r],
+                        what=f"grad branch {r}")
