@@ -16,9 +16,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace layout (offsets in bytes, each 256-aligned):
 //   anc        uint64 [T*B*Wn]   ancestor bitmask of every node (self included)
 //   branch_ok  int32  [T*B]      1 = well formed, 0 = malformed (outputs NaN)
-//   split      fp32 partials for the split-key path (see tree_attn_mfma.hip)
+//   order      int32  [T*B]      branches of each trunk by anchor, longest first
+//   rot        rotated branch queries and keys
 struct TreeAttnWs {
-  size_t anc, branch_ok, order, partial_o, partial_ml, total;
+  size_t anc, branch_ok, order, rot, total;
 };
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d);
 
@@ -30,6 +31,26 @@ struct TreeAttnArgs {
   float rope_base, scale;
 };
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
+
+// Matrix-core path (tree_attn_mfma.hip).  bf16 tensors are passed as uint16_t.
+struct MfmaParams {
+  const uint16_t *trunk_k, *trunk_v;  // [T][L][Hkv][D]
+  const uint16_t* qr;                 // rotated, scaled queries [T][B][Wn][Hq][D]
+  const uint16_t* kr;                 // rotated branch keys [T][B][Wn][Hkv][D]
+  const uint16_t* v;                  // branch values [T][B][Wn][Hkv][D]
+  const int32_t* anchors;             // [T][B]
+  const uint64_t* anc;                // ancestor bitmasks [T][B][Wn]
+  const int32_t* branch_ok;           // [T][B]
+  const int32_t* order;               // [T][B] branches by anchor, longest first
+  uint16_t* out;                      // [T][B][Wn][Hq][D]
+  int B, L, Wn, Hq, Hkv, G;
+  int bpp;     // branches per pack
+  int npacks;  // packs per (trunk, kv head)
+  int nunits;  // T * Hkv * npacks
+  int per;     // units per XCD (grid = 8 * per)
+};
+int mfma_rows_per_wg(int D, int KS);
+hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- E2E-TV
 // Workspace layout:

@@ -48,6 +48,23 @@ __global__ void tree_plan_kernel(const int32_t* __restrict__ anchors,
   branch_ok[tb] = ok ? 1 : 0;
 }
 
+// One workgroup per trunk: branch order by anchor, longest first (malformed
+// branches last), ties by index.  Rank sort, O(B^2) comparisons.
+__global__ void tree_sort_kernel(const int32_t* __restrict__ anchors,
+                                 const int32_t* __restrict__ branch_ok, int B,
+                                 int32_t* __restrict__ order) {
+  const size_t tB = size_t(blockIdx.x) * B;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int kb = branch_ok[tB + b] ? anchors[tB + b] : -1;
+    int rank = 0;
+    for (int o = 0; o < B; ++o) {
+      const int ko = branch_ok[tB + o] ? anchors[tB + o] : -1;
+      rank += (ko > kb) || (ko == kb && o < b);
+    }
+    order[tB + rank] = b;
+  }
+}
+
 // ---------------------------------------------------------------- rotary
 
 // Rotates every branch query and key at its node's semantic position.  One
@@ -173,9 +190,10 @@ TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   size_t off = 0;
   w.anc = off;        off = align_up(off + nodes * sizeof(uint64_t), 256);
   w.branch_ok = off;  off = align_up(off + TB * sizeof(int32_t), 256);
-  w.order = off;      off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * sizeof(float), 256);
-  w.partial_o = off;  // rotated q then rotated k (fp32), see launch_tree_attn
-  w.partial_ml = off;
+  w.order = off;      off = align_up(off + TB * sizeof(int32_t), 256);
+  // rotated branch queries then keys: fp32 for the fp32 path, bf16 for the
+  // matrix-core path (sized for fp32)
+  w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * sizeof(float), 256);
   w.total = off;
   return w;
 }
@@ -214,15 +232,67 @@ static hipError_t launch_rope_fp32(const specopd_tree_attn_desc& d, const TreeAt
   return hipGetLastError();
 }
 
+// Matrix-core layout choice: rows per workgroup shrink (more waves split the
+// keys instead) until there are enough workgroups to cover the chip.
+static bool pick_mfma(const specopd_tree_attn_desc& d, int* KS_out, int* bpp_out) {
+  const int rows_per_branch = d.Wn * (d.Hq / d.Hkv);
+  const int ks_max = d.D == 256 ? 2 : 4;
+  int best = -1, best_bpp = 0;
+  for (int KS = 1; KS <= ks_max; KS *= 2) {
+    const int bpp = mfma_rows_per_wg(d.D, KS) / rows_per_branch;
+    if (bpp < 1) break;
+    const long units = long(d.T) * d.Hkv * ((d.B + bpp - 1) / bpp);
+    best = KS;
+    best_bpp = bpp;
+    if (units >= 512) break;
+  }
+  if (best < 0) return false;
+  *KS_out = best;
+  *bpp_out = best_bpp;
+  return true;
+}
+
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s) {
   const TreeAttnWs L = tree_attn_ws_layout(d);
   uint64_t* anc = reinterpret_cast<uint64_t*>(a.ws + L.anc);
   int32_t* ok = reinterpret_cast<int32_t*>(a.ws + L.branch_ok);
+  int32_t* order = reinterpret_cast<int32_t*>(a.ws + L.order);
   const int TB = d.T * d.B;
+  const int nodes = TB * d.Wn;
   tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);
-  float* qr = reinterpret_cast<float*>(a.ws + L.order);
-  float* kr = qr + size_t(TB) * d.Wn * d.Hq * d.D;
   hipError_t e;
+  int KS = 0, bpp = 0;
+  if (d.dtype == SPECOPD_BF16 && pick_mfma(d, &KS, &bpp)) {
+    tree_sort_kernel<<<d.T, 256, 0, s>>>(a.anchors, ok, d.B, order);
+    uint16_t* qr = reinterpret_cast<uint16_t*>(a.ws + L.rot);
+    uint16_t* kr = qr + size_t(nodes) * d.Hq * d.D;
+    const double lb = log2(double(a.rope_base));
+    auto grid = [](size_t n) { return unsigned(std::min<size_t>((n + 255) / 256, 65536)); };
+    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.Hq * d.D / 2), 256, 0, s>>>(
+        static_cast<const uint16_t*>(a.q), a.pos, nodes, d.Hq, d.D, lb, a.scale * kLog2e, qr);
+    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.Hkv * d.D / 2), 256, 0, s>>>(
+        static_cast<const uint16_t*>(a.k), a.pos, nodes, d.Hkv, d.D, lb, 1.0f, kr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    MfmaParams p{};
+    p.trunk_k = static_cast<const uint16_t*>(a.trunk_k);
+    p.trunk_v = static_cast<const uint16_t*>(a.trunk_v);
+    p.qr = qr;
+    p.kr = kr;
+    p.v = static_cast<const uint16_t*>(a.v);
+    p.anchors = a.anchors;
+    p.anc = anc;
+    p.branch_ok = ok;
+    p.order = order;
+    p.out = static_cast<uint16_t*>(a.out);
+    p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
+    p.bpp = bpp;
+    p.npacks = (d.B + bpp - 1) / bpp;
+    p.nunits = d.T * d.Hkv * p.npacks;
+    p.per = (p.nunits + 7) / 8;
+    return launch_tree_attn_mfma(d.D, KS, p, s);
+  }
+  float* qr = reinterpret_cast<float*>(a.ws + L.rot);
+  float* kr = qr + size_t(nodes) * d.Hq * d.D;
   if (d.dtype == SPECOPD_BF16) {
     if ((e = launch_rope_fp32<uint16_t>(d, a, qr, kr, s)) != hipSuccess) return e;
     return launch_generic<uint16_t>(d, a, anc, ok, qr, kr, s);

@@ -98,9 +98,11 @@ def test_malformed_trees_are_flagged(gpu_ok):
     assert sd.specopd_tree_attn_device_status(desc, ws) == 3
     for b in (1, 3, 4):
         assert torch.isnan(out[0, b].float()).all()
-    good, _, _ = _run(inp)
+    # well-formed branches are still right (packing partners changed, so
+    # compare with the oracle rather than bitwise with the clean call)
+    ref = _ref(inp, branches=[(0, 0), (0, 2)])
     for b in (0, 2):
-        assert torch.equal(out[0, b], good[0, b])
+        check_attention(out[0, b].float().cpu().numpy(), ref[0, b], what=f"branch {b}")
 
 
 @pytest.mark.parametrize("cid", [2, 3, 5])
