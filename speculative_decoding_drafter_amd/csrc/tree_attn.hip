@@ -68,30 +68,33 @@ __global__ void tree_sort_kernel(const int32_t* __restrict__ anchors,
 // ---------------------------------------------------------------- rotary
 
 // Rotates every branch query and key at its node's semantic position.  One
-// thread per (node, head, pair i).  The angle is formed and reduced in fp64:
-// positions reach tens of thousands of radians, where an fp32 angle would be
-// off by ~1e-3.  Queries are also multiplied by `qmul`.
+// thread per (node, pair i), looping over the heads, so each angle is formed
+// once.  The angle is formed and reduced in fp64: positions reach tens of
+// thousands of radians, where an fp32 angle would be off by ~1e-3.  Queries
+// are also multiplied by `qmul`.
 template <typename T, typename O>
 __global__ void rope_branch_kernel(const T* __restrict__ x, const int32_t* __restrict__ pos,
                                    int nodes, int H, int D, double log2_base, float qmul,
                                    O* __restrict__ out) {
   const int half = D >> 1;
-  const size_t total = size_t(nodes) * H * half;
+  const size_t total = size_t(nodes) * half;
   for (size_t idx = size_t(blockIdx.x) * blockDim.x + threadIdx.x; idx < total;
        idx += size_t(gridDim.x) * blockDim.x) {
     const int i = int(idx % half);
-    const size_t nh = idx / half;                 // node * H + head
-    const size_t node = nh / H;
+    const size_t node = idx / half;
     const double theta = exp2(-(2.0 * i / D) * log2_base);
     const double ang = double(pos[node]) * theta;
     double sn, cs;
     sincos(ang, &sn, &cs);
-    const T* src = x + nh * D;
-    const float x1 = load_f32(src + i), x2 = load_f32(src + i + half);
     const float c = float(cs), s = float(sn);
-    O* dst = out + nh * D;
-    store_f32(dst + i, (x1 * c - x2 * s) * qmul);
-    store_f32(dst + i + half, (x2 * c + x1 * s) * qmul);
+    for (int hd = 0; hd < H; ++hd) {
+      const size_t nh = node * H + hd;
+      const T* src = x + nh * D;
+      const float x1 = load_f32(src + i), x2 = load_f32(src + i + half);
+      O* dst = out + nh * D;
+      store_f32(dst + i, (x1 * c - x2 * s) * qmul);
+      store_f32(dst + i + half, (x2 * c + x1 * s) * qmul);
+    }
   }
 }
 
@@ -225,9 +228,9 @@ static hipError_t launch_rope_fp32(const specopd_tree_attn_desc& d, const TreeAt
   const int nodes = d.T * d.B * d.Wn;
   const double lb = log2(double(a.rope_base));
   auto grid = [](size_t n) { return unsigned(std::min<size_t>((n + 255) / 256, 65536)); };
-  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.Hq * d.D / 2), 256, 0, s>>>(
+  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
       static_cast<const T*>(a.q), a.pos, nodes, d.Hq, d.D, lb, a.scale, qr);
-  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.Hkv * d.D / 2), 256, 0, s>>>(
+  rope_branch_kernel<T, float><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
       static_cast<const T*>(a.k), a.pos, nodes, d.Hkv, d.D, lb, 1.0f, kr);
   return hipGetLastError();
 }
@@ -268,9 +271,9 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     uint16_t* kr = qr + size_t(nodes) * d.Hq * d.D;
     const double lb = log2(double(a.rope_base));
     auto grid = [](size_t n) { return unsigned(std::min<size_t>((n + 255) / 256, 65536)); };
-    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.Hq * d.D / 2), 256, 0, s>>>(
+    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
         static_cast<const uint16_t*>(a.q), a.pos, nodes, d.Hq, d.D, lb, a.scale * kLog2e, qr);
-    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.Hkv * d.D / 2), 256, 0, s>>>(
+    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
         static_cast<const uint16_t*>(a.k), a.pos, nodes, d.Hkv, d.D, lb, 1.0f, kr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MfmaParams p{};

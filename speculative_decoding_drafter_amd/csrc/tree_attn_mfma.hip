@@ -16,10 +16,12 @@
 // branches' own nodes form extra "tail" tiles masked by the ancestor bitmask
 // and by branch identity.
 //
-// Wave layout (4 waves): KS key slices x (4/KS) row groups.  A row group is
-// NB blocks of 32 rows.  Waves of the same slice share one double-buffered
-// K/V tile in LDS; waves of different slices take interleaved tiles and are
-// merged at the end through LDS in a fixed order (deterministic).
+// Wave layout (8 waves, two per SIMD so one wave's softmax overlaps the
+// other's matrix work): KS key slices x (8/KS) row groups.  A row group is NB
+// blocks of 32 rows (one wave).  Waves of the same slice share one
+// double-buffered K/V tile in LDS; waves of different slices take interleaved
+// tiles and are merged at the end through LDS in a fixed order
+// (deterministic).
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, lane l = r + 32h):
 //   S^T[key][row] = K[key][:] . Q[row][:]      A = K tile (LDS, 16 B reads),
@@ -42,6 +44,7 @@
 namespace specopd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -51,12 +54,18 @@ constexpr int KT = 32;            // keys per tile
 constexpr float kRescale = 8.0f;  // log2 headroom before the reference max moves
 constexpr float kFarNeg = -1.0e30f;
 
+// Waves per workgroup: 8 (two per SIMD) where a wave fits in 256 registers;
+// 4 for D = 256, whose accumulators and query operand need more.
+template <int D>
+constexpr int waves_for() { return D == 256 ? 4 : 8; }
+
 template <int D, int NB, int KS>
 struct Shape {
-  static constexpr int RG = 4 / KS;          // row groups per workgroup
-  static constexpr int ROWS_G = 32 * NB;     // rows per row group
+  static constexpr int NW = waves_for<D>();
+  static constexpr int RG = NW / KS;         // row groups per workgroup
+  static constexpr int ROWS_G = 32 * NB;     // rows per row group (one wave)
   static constexpr int RW = RG * ROWS_G;     // rows per workgroup
-  static constexpr int LDK = D + 8;          // LDS row stride (elements), +16 B breaks bank aliasing
+  static constexpr int LDK = D + 8;          // LDS row stride (elements); +16 B spreads banks
   static constexpr int TILE = KT * LDK;      // elements of one K (or V) tile
   static constexpr int SLICE = 2 * 2 * TILE; // double-buffered K and V
   static constexpr int TILES_BYTES = KS * SLICE * 2;
@@ -64,9 +73,10 @@ struct Shape {
   static constexpr int COMB_WORDS = (KS > 1) ? (KS - 1) * RG * (OREGS + 2 * NB) * 64 : 0;
   static constexpr int LDS_BYTES = TILES_BYTES > COMB_WORDS * 4 ? TILES_BYTES : COMB_WORDS * 4;
   static constexpr int CHUNKS = 2 * KT * D / 8;  // 16-byte pieces of a K+V tile
-  static constexpr int LOADERS = 64 * RG;        // threads filling one slice's tile
-  static constexpr int CPT = CHUNKS / LOADERS;
-  static_assert(CHUNKS % LOADERS == 0, "tile must split evenly over loaders");
+  // threads filling one slice's tile (capped so every loader has a K and a V piece)
+  static constexpr int LOADERS = 64 * RG < CHUNKS / 2 ? 64 * RG : CHUNKS / 2;
+  static constexpr int CPT = CHUNKS / LOADERS;   // pieces per loader (first half K)
+  static_assert(CHUNKS % LOADERS == 0 && CPT % 2 == 0, "tile must split evenly over loaders");
 };
 
 __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
@@ -74,8 +84,18 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
       (__attribute__((address_space(3))) s16x4*)(p));
 }
 
+// Visible tail keys of a row within tail tile [tau0, tau0 + 32): the row's own
+// branch occupies tail keys slot*Wn .. slot*Wn + Wn - 1 and it sees the nodes
+// set in its ancestor mask.  Bit q of the result = tail key tau0 + q.
+__device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int Wn, int tau0) {
+  const int base = slot * Wn - tau0;  // tile position of the row's node 0
+  if (anc == 0 || base >= KT || base <= -64) return 0u;
+  const uint64_t w = base >= 0 ? (anc << base) : (anc >> (-base));
+  return uint32_t(w);
+}
+
 template <int D, int NB, int KS>
-__global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams p) {
+__global__ __launch_bounds__(waves_for<D>() * 64, 1) void tree_attn_mfma_kernel(const MfmaParams p) {
   using S = Shape<D, NB, KS>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_BYTES / 2];
 
@@ -124,13 +144,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
     rmask[nb] = ok ? p.anc[(tB + b) * p.Wn + j] : 0ull;
     const uint16_t* qrow = p.qr + ((((tB + b) * p.Wn + j) * p.Hq) + size_t(g) * p.G + hh) * D;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      if (ok) {
-        qop[nb][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * h);
-      } else {
-        qop[nb][s] = bf16x8{};
-      }
-    }
+    for (int s = 0; s < D / 16; ++s)
+      qop[nb][s] = ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * h) : bf16x8{};
   }
 
   const int ntrunk = (amax + 1 + KT - 1) / KT;
@@ -139,16 +154,15 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
   const int nvt = ntrunk + ntail;
   const int iters = (nvt + KS - 1) / KS;
 
-  // ---- tile staging (global -> registers -> LDS)
+  // ---- tile staging (global -> registers -> LDS), two tiles ahead.  Piece c
+  // of a loader: the first CPT/2 are K, the rest V (compile-time split).
   uint16_t* sbase = smem + slice * S::SLICE;
-  const int li = rgrp * 64 + lane;  // index among this slice's loaders
-  u32x4 stage[S::CPT];
-
-  // Chunk c of a thread: the first CPT/2 chunks are K, the rest V (a
-  // compile-time split, so no pointer is selected at run time).
+  const int li = rgrp * 64 + lane;
   constexpr int HALF = S::CPT / 2;
+  u32x4 stage[S::CPT];
   auto load_tile = [&](int vt) {
     const bool trunk = vt < ntrunk;
+    if (li >= S::LOADERS) return;
 #pragma unroll
     for (int c = 0; c < S::CPT; ++c) {
       const int rem = li + (c % HALF) * S::LOADERS;
@@ -160,15 +174,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
       } else {
         int tau = (vt - ntrunk) * KT + key;
         if (tau >= nt_total) tau = 0;
-        const int slot = tau / p.Wn;
-        const int node = tau - slot * p.Wn;
-        row = ((tB + size_t(ord[b0 + slot])) * p.Wn + node) * p.Hkv + g;
+        const int sl = tau / p.Wn;
+        const int node = tau - sl * p.Wn;
+        row = ((tB + size_t(ord[b0 + sl])) * p.Wn + node) * p.Hkv + g;
       }
       const uint16_t* base = c < HALF ? (trunk ? p.trunk_k : p.kr) : (trunk ? p.trunk_v : p.v);
       stage[c] = *reinterpret_cast<const u32x4*>(base + row * D + part * 8);
     }
   };
   auto store_tile = [&](int buf) {
+    if (li >= S::LOADERS) return;
 #pragma unroll
     for (int c = 0; c < S::CPT; ++c) {
       const int rem = li + (c % HALF) * S::LOADERS;
@@ -198,6 +213,7 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
   __syncthreads();
 
   const int gi = lane >> 4, rq = lane & 15;
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   for (int it = 0; it < iters; ++it) {
     const int vt = it * KS + slice;
     const int buf = it & 1;
@@ -214,31 +230,27 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
         for (int nb = 0; nb < NB; ++nb)
           sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s], sacc[nb], 0, 0, 0);
       }
-      // masks: trunk keys beyond a row's anchor; tail keys of other branches
-      // or outside the row's ancestor chain
+      // masks: trunk keys beyond a row's anchor (edge tiles only); tail keys
+      // of other branches or outside the row's ancestor chain
       if (vt < ntrunk) {
         const int k0 = vt * KT;
         if (k0 + KT - 1 > amin) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb) {
+            const int lim = ra[nb] - k0 - 4 * h;  // element i visible iff 8(i/4)+(i%4) <= lim
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 8 * (i >> 2) + 4 * h + (i & 3);
-              if (key > ra[nb]) sacc[nb][i] = kNegInf;
-            }
+            for (int i = 0; i < 16; ++i)
+              if (8 * (i >> 2) + (i & 3) > lim) sacc[nb][i] = kNegInf;
+          }
         }
       } else {
         const int tau0 = (vt - ntrunk) * KT;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int tau = tau0 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const int slot = tau / p.Wn;
-          const int node = tau - slot * p.Wn;
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t vis = tail_window(rmask[nb], rslot[nb], p.Wn, tau0) >> (4 * h);
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const bool vis = tau < nt_total && slot == rslot[nb] && ((rmask[nb] >> node) & 1ull);
-            if (!vis) sacc[nb][i] = kNegInf;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (!((vis >> (8 * (i >> 2) + (i & 3))) & 1u)) sacc[nb][i] = kNegInf;
         }
       }
       // online softmax (log2 units), lazily rescaled
@@ -268,15 +280,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
       bf16x8 pop[NB][2];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float ps = 0.f;
+        float ps = lsum[nb];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float e = fast_exp2(sacc[nb][i] - mref[nb]);
-          const __bf16 eb = static_cast<__bf16>(e);
-          pop[nb][i >> 3][i & 7] = eb;
-          ps += static_cast<float>(eb);
+        for (int i = 0; i < 16; i += 2) {
+          const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(sacc[nb][i] - mref[nb])),
+                             static_cast<__bf16>(fast_exp2(sacc[nb][i + 1] - mref[nb]))};
+          pop[nb][i >> 3][i & 7] = e2[0];
+          pop[nb][i >> 3][(i & 7) + 1] = e2[1];
+          ps = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, ps, false);  // sums the bf16 weights used below
         }
-        lsum[nb] += ps;
+        lsum[nb] = ps;
       }
       // O^T += V^T P^T
 #pragma unroll
@@ -337,9 +350,8 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+            for (int i = 0; i < 16; ++i)
               oacc[nb][db][i] = oacc[nb][db][i] * a0 + src[(kk++) * 64 + lane] * a1;
-            }
           lsum[nb] = lsum[nb] * a0 + l2 * a1;
           mref[nb] = mn;
         }
@@ -376,15 +388,16 @@ __global__ __launch_bounds__(256, 1) void tree_attn_mfma_kernel(const MfmaParams
 
 template <int D, int NB, int KS>
 hipError_t launch_shape(const MfmaParams& p, hipStream_t s) {
-  tree_attn_mfma_kernel<D, NB, KS><<<8 * p.per, 256, 0, s>>>(p);
+  tree_attn_mfma_kernel<D, NB, KS><<<8 * p.per, waves_for<D>() * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int mfma_rows_per_wg(int D, int KS) {
-  const int NB = D == 256 ? 1 : 2;
-  return (4 / KS) * 32 * NB;
+  const int NB = D == 64 ? 2 : 1;
+  const int nw = D == 256 ? waves_for<256>() : waves_for<128>();
+  return (nw / KS) * 32 * NB;
 }
 
 hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t s) {
@@ -393,8 +406,8 @@ hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t
       return KS == 1 ? launch_shape<64, 2, 1>(p, s)
                      : KS == 2 ? launch_shape<64, 2, 2>(p, s) : launch_shape<64, 2, 4>(p, s);
     case 128:
-      return KS == 1 ? launch_shape<128, 2, 1>(p, s)
-                     : KS == 2 ? launch_shape<128, 2, 2>(p, s) : launch_shape<128, 2, 4>(p, s);
+      return KS == 1 ? launch_shape<128, 1, 1>(p, s)
+                     : KS == 2 ? launch_shape<128, 1, 2>(p, s) : launch_shape<128, 1, 4>(p, s);
     case 256:
       return KS == 1 ? launch_shape<256, 1, 1>(p, s) : launch_shape<256, 1, 2>(p, s);
   }
