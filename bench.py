@@ -160,6 +160,11 @@ def main():
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
+    # a timed run only counts if every branch came out well formed
+    if ai is not None and sd.specopd_tree_attn_device_status(adesc, aws) != 0:
+        raise SystemExit("tree attention reported malformed branches")
+    if sd.specopd_e2etv_device_status(ldesc, lws) != 0:
+        raise SystemExit("E2E-TV reported malformed or timed-out branches")
     ms_step = t_start.elapsed_time(t_end) / args.steps
     attn_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if ai is not None else 0.0
     loss_ms = float(np.mean([(e[1] if ai is not None else e[0]).elapsed_time(e[2]) for e in evs])) \

@@ -7,18 +7,26 @@
 // support kept), prefix products along the parent chain, loss = 1 - mean of
 // the prefix products, gradient through q only.
 //
-// Kernels (all vocab loops are coalesced 16-byte streams):
-//   rows      one workgroup per row: pass A (log-sum-exp of draft and target),
-//             then pass B over the same row (alpha and G = sum_{q<p} q).  The
-//             re-read of pass B follows the first read closely, so it is
-//             served from the caches.
-//   scan      one thread per branch: prefix products, suffix sums S, the
-//             per-row coefficient grad_scale * dLoss/dalpha, branch numerator.
-//   finalize  fixed-order sum of the branch numerators -> loss, numer, count.
-//   grad      grad[n][u] = coef_n * q_u * ([q_u < p_u] - G_n).
-// No atomics: every reduction has a fixed order, so results are bitwise
-// reproducible run to run.
-#include <float.h>
+// One fused kernel, one workgroup per row (row n = branch r, node j):
+//   pass A   stream the row: log-sum-exp of draft and target;
+//   pass B   stream it again (the caches serve it: it was just read):
+//            alpha = sum min(q, p) and G = sum_{q<p} q;
+//   post     publish (alpha, G) and count the row into its branch;
+//   scan     once every row of the branch has posted, compute prefix
+//            products, suffix sums S and this row's coefficient
+//            c = grad_scale * dLoss/dalpha in fp64 (every row of a branch
+//            repeats the same tiny scan in the same order);
+//   pass C   stream the row a third time and write
+//            grad[u] = c * q_u * ([q_u < p_u] - G).
+// Loads are software-pipelined: the next batch of 16-byte vectors is in
+// flight while the current one is reduced.  Rows are taken in order from an
+// atomic ticket, so a workgroup only waits for rows of its own branch that
+// were claimed just before or after it; the wait is bounded and a timeout
+// marks the branch malformed rather than hanging.  The exchange goes through
+// memory with cache-bypassing accesses (see post_f32).
+// A small kernel sums the branch numerators in a fixed order (loss).
+// No floating-point atomics: results are bitwise reproducible.
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -27,54 +35,8 @@ namespace specopd {
 
 namespace {
 
-constexpr int kRowThreads = 512;
-constexpr int kGradThreads = 256;
-constexpr int kGradUnroll = 4;
-
-// Vector loads of logits widened to fp32.  BF16: 8 values per 16 bytes; FP32:
-// 4 values per 16 bytes.
-template <bool BF16>
-struct Logits;
-
-template <>
-struct Logits<true> {
-  static constexpr int NV = 8;
-  __device__ static __forceinline__ void load(const void* base, size_t idx, float (&x)[8]) {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-        reinterpret_cast<const uint16_t*>(base) + idx));
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
-    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
-    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  }
-  __device__ static __forceinline__ void load_cached(const void* base, size_t idx, float (&x)[8]) {
-    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + idx);
-    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
-    x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
-    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
-    x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
-  }
-  __device__ static __forceinline__ float load1(const void* base, size_t idx) {
-    return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
-  }
-};
-
-template <>
-struct Logits<false> {
-  static constexpr int NV = 4;
-  __device__ static __forceinline__ void load(const void* base, size_t idx, float (&x)[4]) {
-    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(
-        reinterpret_cast<const float*>(base) + idx));
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
-  }
-  __device__ static __forceinline__ void load_cached(const void* base, size_t idx, float (&x)[4]) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + idx);
-    x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
-  }
-  __device__ static __forceinline__ float load1(const void* base, size_t idx) {
-    return reinterpret_cast<const float*>(base)[idx];
-  }
-};
+constexpr int kThreads = 1024;  // per workgroup (one row)
+constexpr int kU = 2;           // 16-byte vectors per tensor per thread per batch
 
 // One element's log2-probabilities.  The overlap pass and the gradient pass
 // both call exactly this, so the indicator [q < p] is decided identically.
@@ -84,7 +46,7 @@ __device__ __forceinline__ void log2probs(float z, float t, float nlz, float nlt
   lp = __builtin_fmaf(t, kLog2e, nlt);
 }
 
-// Running max / scaled sum over a vector of NV values.
+// Running max / scaled sum over NV values.
 template <int NV>
 __device__ __forceinline__ void lse_update(float& m, float& s, const float (&x)[NV]) {
   float vm = x[0];
@@ -103,23 +65,56 @@ __device__ __forceinline__ void lse_update(float& m, float& s, const float (&x)[
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void overlap_update(float& al, float& g, const float (&z)[NV],
-                                               const float (&t)[NV], float nlz, float nlt) {
+// Stream units [u0, u1) of a row (16-byte vectors, or single elements when
+// the row is not 16-byte aligned), pairs (draft, target): thread tid takes
+// u0 + tid + k * kThreads.  Two register batches alternate so the next
+// batch's loads are in flight while f() consumes the current one.
+template <bool VECTOR, bool NT, typename F>
+__device__ __forceinline__ void stream_pairs(const void* zrow, const void* trow, int u0, int u1,
+                                             int esize, F&& f) {
+  constexpr int STEP = kThreads * kU;
+  using T = typename std::conditional<VECTOR, u32x4, uint32_t>::type;
+  const int base = u0 + int(threadIdx.x);
+  T za[kU], ta[kU], zb[kU], tb[kU];
+  auto ld = [&](const void* row, int u) -> T {
+    if constexpr (VECTOR) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(row) + u;
+      if constexpr (NT) return __builtin_nontemporal_load(p);
+      return *p;
+    } else {
+      return esize == 2 ? uint32_t(reinterpret_cast<const uint16_t*>(row)[u])
+                        : reinterpret_cast<const uint32_t*>(row)[u];
+    }
+  };
+  auto load = [&](T(&z)[kU], T(&t)[kU], int b) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    float lq, lp;
-    log2probs(z[i], t[i], nlz, nlt, lq, lp);
-    const float e = fast_exp2(fminf(lq, lp));
-    al += e;
-    g += (lq < lp) ? e : 0.f;
+    for (int k = 0; k < kU; ++k) {
+      const int u = b + k * kThreads;
+      if (u < u1) {
+        z[k] = ld(zrow, u);
+        t[k] = ld(trow, u);
+      }
+    }
+  };
+  auto run = [&](const T(&z)[kU], const T(&t)[kU], int b) {
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+      const int u = b + k * kThreads;
+      if (u < u1) f(z[k], t[k], u);
+    }
+  };
+  if (base < u1) load(za, ta, base);
+  for (int b = base; b < u1; b += 2 * STEP) {
+    if (b + STEP < u1) load(zb, tb, b + STEP);
+    run(za, ta, b);
+    if (b + 2 * STEP < u1) load(za, ta, b + 2 * STEP);
+    if (b + STEP < u1) run(zb, tb, b + STEP);
   }
 }
 
 template <int BLOCK>
 __device__ __forceinline__ void block_lse2(float& mz, float& sz, float& mt, float& st,
                                            float* red) {
-  // wave level
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     float m2 = __shfl_xor(mz, o, 64), s2 = __shfl_xor(sz, o, 64);
@@ -165,124 +160,236 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
   __syncthreads();
 }
 
-// Pass A + pass B for one row per workgroup.
+// Cross-workgroup exchange.  The XCDs' L2 caches are not coherent with each
+// other, and device-scope release/acquire would write back / invalidate a
+// whole L2 per use.  Instead every exchanged word goes through memory with
+// system-scope relaxed accesses (write-through stores, cache-bypassing
+// loads): a workgroup posts its partials, waits until those stores are
+// acknowledged, and only then bumps the counter; a reader that sees the count
+// reads the partials the same cache-bypassing way.
+__device__ __forceinline__ void post_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float peek_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void post_count(int32_t* ctr) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged first
+  __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+// Bounded wait until *ctr reaches want.  False on timeout.
+__device__ __forceinline__ bool wait_count(int32_t* ctr, int want, int spin_limit) {
+  int spins = 0;
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < want) {
+    if (++spins > spin_limit) return false;
+    __builtin_amdgcn_s_sleep(8);
+  }
+  return true;
+}
+
+struct FusedArgs {
+  const void* draft;
+  const void* target;
+  const int32_t* parent;
+  int Wn, V;
+  double count;
+  float grad_scale;
+  int spin_limit;
+  float* segB;      // [N][2] (alpha, G) of every row
+  int32_t* bcount;  // [R] rows of each branch that posted
+  int32_t* ticket;
+  double* numer;
+  int32_t* branch_ok;
+  float* alpha_out;
+  float* prefix_out;
+  void* grad;
+};
+
+__global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ bcount,
+                                  int32_t* __restrict__ branch_ok, int R) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *ticket = 0;
+  if (i < R) {
+    bcount[i] = 0;
+    branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
+  }
+}
+
+// Elements of a streamed unit as fp32: a 16-byte vector, or one raw element.
 template <bool BF16, bool VECTOR>
-__global__ __launch_bounds__(kRowThreads) void e2etv_rows_kernel(const void* __restrict__ draft,
-                                                                 const void* __restrict__ target,
-                                                                 int V, float4* __restrict__ rowstat) {
-  using LD = Logits<BF16>;
-  constexpr int NV = LD::NV;
-  constexpr int U = 2;
-  __shared__ float red[4 * (kRowThreads / 64)];
-  const size_t row = size_t(blockIdx.x) * size_t(V);
+struct Unit {
+  static constexpr int NV = VECTOR ? (BF16 ? 8 : 4) : 1;
+  template <typename T>
+  __device__ static __forceinline__ float get(const T& w, int i) {
+    if constexpr (VECTOR) {
+      if constexpr (BF16) return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      else return __uint_as_float(w[i]);
+    } else {
+      if constexpr (BF16) return bf16_to_f32(uint16_t(w));
+      else return __uint_as_float(w);
+    }
+  }
+};
+
+template <bool BF16, bool VECTOR, bool GRAD, bool GBF16>
+__global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a) {
+  using U = Unit<BF16, VECTOR>;
+  constexpr int NV = U::NV;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  __shared__ float red[4 * (kThreads / 64)];
+  __shared__ int s_unit;
+  __shared__ float s_val[4];
+  __shared__ double sA[64], sP[64], sS[64];
+
   const int tid = threadIdx.x;
-  const int nvec = VECTOR ? V / NV : 0;
+  if (tid == 0)
+    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  const int n = s_unit;
+  const int r = n / a.Wn;
+  const int j = n - r * a.Wn;
+  const int V = a.V;
+  const size_t row = size_t(n) * size_t(V);
+  const void* zrow = static_cast<const char*>(a.draft) + row * ESZ;
+  const void* trow = static_cast<const char*>(a.target) + row * ESZ;
+  const int units = V / NV;  // whole units; a vector row's ragged tail is done element-wise
+  const int e0 = units * NV;
+  const float qnan = __builtin_nanf("");
+  auto load1 = [&](const void* rowp, int e) -> float {
+    if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[e]);
+    else return reinterpret_cast<const float*>(rowp)[e];
+  };
 
   // ---- pass A: log-sum-exp of both rows
   float mz = kNegInf, sz = 0.f, mt = kNegInf, st = 0.f;
-  int i = tid;
-  for (; i + (U - 1) * kRowThreads < nvec; i += U * kRowThreads) {
-    float z[U][NV], t[U][NV];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      LD::load_cached(draft, row + size_t(i + u * kRowThreads) * NV, z[u]);
-      LD::load_cached(target, row + size_t(i + u * kRowThreads) * NV, t[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      lse_update<NV>(mz, sz, z[u]);
-      lse_update<NV>(mt, st, t[u]);
-    }
-  }
-  for (; i < nvec; i += kRowThreads) {
+  stream_pairs<VECTOR, false>(zrow, trow, 0, units, ESZ, [&](const auto& zw, const auto& tw, int) {
     float z[NV], t[NV];
-    LD::load_cached(draft, row + size_t(i) * NV, z);
-    LD::load_cached(target, row + size_t(i) * NV, t);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      z[i] = U::get(zw, i);
+      t[i] = U::get(tw, i);
+    }
     lse_update<NV>(mz, sz, z);
     lse_update<NV>(mt, st, t);
-  }
-  for (int e = nvec * NV + tid; e < V; e += kRowThreads) {
-    float z[1] = {LD::load1(draft, row + e)}, t[1] = {LD::load1(target, row + e)};
+  });
+  for (int e = e0 + tid; e < V; e += kThreads) {
+    float z[1] = {load1(zrow, e)}, t[1] = {load1(trow, e)};
     lse_update<1>(mz, sz, z);
     lse_update<1>(mt, st, t);
   }
-  block_lse2<kRowThreads>(mz, sz, mt, st, red);
-  // -log2-sum-exp2 of the log2e-scaled logits; a row of only -inf gives NaN.
+  block_lse2<kThreads>(mz, sz, mt, st, red);
+  // -log2-sum-exp2 of the log2e-scaled logits; a row of only -inf gives NaN
   const float nlz = -(mz * kLog2e + log2f(sz));
   const float nlt = -(mt * kLog2e + log2f(st));
 
   // ---- pass B: alpha = sum min(q, p), G = sum_{q<p} q
   float al = 0.f, g = 0.f;
-  i = tid;
-  for (; i + (U - 1) * kRowThreads < nvec; i += U * kRowThreads) {
-    float z[U][NV], t[U][NV];
+  auto overlap = [&](float z, float t) {
+    float lq, lp;
+    log2probs(z, t, nlz, nlt, lq, lp);
+    const float e = fast_exp2(fminf(lq, lp));
+    al += e;
+    g += (lq < lp) ? e : 0.f;
+  };
+  stream_pairs<VECTOR, false>(zrow, trow, 0, units, ESZ, [&](const auto& zw, const auto& tw, int) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      LD::load_cached(draft, row + size_t(i + u * kRowThreads) * NV, z[u]);
-      LD::load_cached(target, row + size_t(i + u * kRowThreads) * NV, t[u]);
+    for (int i = 0; i < NV; ++i) overlap(U::get(zw, i), U::get(tw, i));
+  });
+  for (int e = e0 + tid; e < V; e += kThreads) overlap(load1(zrow, e), load1(trow, e));
+  block_sum2<kThreads>(al, g, red);
+
+  // ---- post, wait for the branch, scan
+  const bool lead = j == 0;
+  const bool need_scan = GRAD || lead;
+  if (tid == 0) {
+    post_f32(a.segB + size_t(n) * 2 + 0, al);
+    post_f32(a.segB + size_t(n) * 2 + 1, g);
+    post_count(&a.bcount[r]);
+    if (need_scan) {
+      bool ok = wait_count(&a.bcount[r], a.Wn, a.spin_limit);
+      const int32_t* par = a.parent + size_t(r) * a.Wn;
+      const float* sb = a.segB + size_t(r) * a.Wn * 2;
+      double sum = 0.0, Gj = 0.0;
+      for (int k = 0; k < a.Wn; ++k) {
+        int pk = par[k];
+        if (pk < -1 || pk >= k) {
+          ok = false;
+          pk = -1;
+        }
+        const float ak = peek_f32(sb + 2 * k), gk = peek_f32(sb + 2 * k + 1);
+        if (k == j) Gj = gk;
+        sA[k] = double(ak);
+        sP[k] = double(ak) * (pk < 0 ? 1.0 : sP[pk]);
+        sS[k] = 1.0;
+        sum += sP[k];
+      }
+      // suffix sums S_k = 1 + sum over children c of alpha_c S_c (children
+      // come after their parent, so a backward sweep sees them complete)
+      for (int k = a.Wn - 1; k >= 0; --k) {
+        const int pk = par[k];
+        if (pk >= 0 && pk < k) sS[pk] += sA[k] * sS[k];
+      }
+      const int pj = par[j];
+      const double pp = (pj >= 0 && pj < j) ? sP[pj] : 1.0;
+      const double c = -double(a.grad_scale) * pp * sS[j] / a.count;
+      s_val[0] = ok ? float(c * (1.0 - Gj)) : qnan;  // coefficient where q < p
+      s_val[1] = ok ? float(-c * Gj) : qnan;         // elsewhere
+      if (!ok) a.branch_ok[r] = 0;
+      if (lead) {
+        a.numer[r] = ok ? sum : double(qnan);
+        for (int k = 0; k < a.Wn; ++k) {
+          if (a.alpha_out) a.alpha_out[size_t(r) * a.Wn + k] = ok ? float(sA[k]) : qnan;
+          if (a.prefix_out) a.prefix_out[size_t(r) * a.Wn + k] = ok ? float(sP[k]) : qnan;
+        }
+      }
     }
+  }
+  if constexpr (!GRAD) return;
+  __syncthreads();
+
+  // ---- pass C: gradient
+  const float c1 = s_val[0], c0 = s_val[1];
+  auto gradv = [&](float z, float t) {
+    float lq, lp;
+    log2probs(z, t, nlz, nlt, lq, lp);
+    return fast_exp2(lq) * (lq < lp ? c1 : c0);
+  };
+  stream_pairs<VECTOR, true>(zrow, trow, 0, units, ESZ, [&](const auto& zw, const auto& tw, int u) {
+    float gv[NV];
 #pragma unroll
-    for (int u = 0; u < U; ++u) overlap_update<NV>(al, g, z[u], t[u], nlz, nlt);
-  }
-  for (; i < nvec; i += kRowThreads) {
-    float z[NV], t[NV];
-    LD::load_cached(draft, row + size_t(i) * NV, z);
-    LD::load_cached(target, row + size_t(i) * NV, t);
-    overlap_update<NV>(al, g, z, t, nlz, nlt);
-  }
-  for (int e = nvec * NV + tid; e < V; e += kRowThreads) {
-    float z[1] = {LD::load1(draft, row + e)}, t[1] = {LD::load1(target, row + e)};
-    overlap_update<1>(al, g, z, t, nlz, nlt);
-  }
-  block_sum2<kRowThreads>(al, g, red);
-  if (tid == 0) rowstat[blockIdx.x] = make_float4(nlz, nlt, al, g);
-}
-
-// Prefix products, suffix sums and per-row coefficients; one thread per branch.
-constexpr int kScanThreads = 32;
-
-__global__ __launch_bounds__(kScanThreads) void e2etv_scan_kernel(
-    const float4* __restrict__ rowstat, const int32_t* __restrict__ parent, int R, int Wn,
-    double count, float grad_scale, float* __restrict__ coef, double* __restrict__ numer,
-    int32_t* __restrict__ branch_ok, float* __restrict__ alpha_out, float* __restrict__ prefix_out) {
-  __shared__ double P[64 * kScanThreads];
-  __shared__ double S[64 * kScanThreads];
-  const int tid = threadIdx.x;
-  const int r = blockIdx.x * kScanThreads + tid;
-  if (r >= R) return;
-  const int32_t* par = parent + size_t(r) * Wn;
-  const size_t n0 = size_t(r) * Wn;
-  bool ok = true;
-  double sum = 0.0;
-  for (int j = 0; j < Wn; ++j) {
-    int p = par[j];
-    if (p < -1 || p >= j) {
-      ok = false;
-      p = -1;
+    for (int i = 0; i < NV; ++i) gv[i] = gradv(U::get(zw, i), U::get(tw, i));
+    if constexpr (VECTOR) {
+      if constexpr (GBF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.grad) + row + size_t(u) * NV;
+        if constexpr (NV == 8) {
+          const u32x4 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]),
+                           pack_bf16x2(gv[4], gv[5]), pack_bf16x2(gv[6], gv[7])};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
+        } else {
+          const u32x2 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(o));
+        }
+      } else {
+        float* o = reinterpret_cast<float*>(a.grad) + row + size_t(u) * NV;
+#pragma unroll
+        for (int i = 0; i < NV; i += 4)
+          __builtin_nontemporal_store(f32x4{gv[i], gv[i + 1], gv[i + 2], gv[i + 3]},
+                                      reinterpret_cast<f32x4*>(o + i));
+      }
+    } else {
+      if constexpr (GBF16)
+        reinterpret_cast<uint16_t*>(a.grad)[row + u] = f32_to_bf16(gv[0]);
+      else
+        reinterpret_cast<float*>(a.grad)[row + u] = gv[0];
     }
-    const double a = double(rowstat[n0 + j].z);
-    const double pp = (p < 0) ? 1.0 : P[p * kScanThreads + tid];
-    const double pj = a * pp;
-    P[j * kScanThreads + tid] = pj;
-    S[j * kScanThreads + tid] = 1.0;
-    sum += pj;
+  });
+  for (int e = e0 + tid; e < V; e += kThreads) {
+    const float gv = gradv(load1(zrow, e), load1(trow, e));
+    if constexpr (GBF16)
+      reinterpret_cast<uint16_t*>(a.grad)[row + e] = f32_to_bf16(gv);
+    else
+      reinterpret_cast<float*>(a.grad)[row + e] = gv;
   }
-  for (int j = Wn - 1; j >= 0; --j) {
-    int p = par[j];
-    if (p >= 0 && p < j)
-      S[p * kScanThreads + tid] += double(rowstat[n0 + j].z) * S[j * kScanThreads + tid];
-  }
-  const float qnan = __builtin_nanf("");
-  for (int j = 0; j < Wn; ++j) {
-    int p = par[j];
-    const double pp = (p >= 0 && p < j) ? P[p * kScanThreads + tid] : 1.0;
-    const double c = -double(grad_scale) * pp * S[j * kScanThreads + tid] / count;
-    coef[n0 + j] = ok ? float(c) : qnan;
-    if (alpha_out) alpha_out[n0 + j] = ok ? rowstat[n0 + j].z : qnan;
-    if (prefix_out) prefix_out[n0 + j] = ok ? float(P[j * kScanThreads + tid]) : qnan;
-  }
-  numer[r] = ok ? sum : double(qnan);
-  branch_ok[r] = ok ? 1 : 0;
 }
 
 constexpr int kFinThreads = 256;
@@ -307,102 +414,39 @@ __global__ __launch_bounds__(kFinThreads) void e2etv_finalize_kernel(const doubl
   }
 }
 
-template <bool GBF16>
-__device__ __forceinline__ void store_grad(void* grad, size_t idx, const float* g, int nv);
 
-template <>
-__device__ __forceinline__ void store_grad<false>(void* grad, size_t idx, const float* g, int nv) {
-  float* o = reinterpret_cast<float*>(grad) + idx;
-  if (nv == 8) {
-    __builtin_nontemporal_store(f32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<f32x4*>(o));
-    __builtin_nontemporal_store(f32x4{g[4], g[5], g[6], g[7]}, reinterpret_cast<f32x4*>(o + 4));
-  } else if (nv == 4) {
-    __builtin_nontemporal_store(f32x4{g[0], g[1], g[2], g[3]}, reinterpret_cast<f32x4*>(o));
-  } else {
-    for (int i = 0; i < nv; ++i) o[i] = g[i];
-  }
-}
-
-template <>
-__device__ __forceinline__ void store_grad<true>(void* grad, size_t idx, const float* g, int nv) {
-  uint16_t* o = reinterpret_cast<uint16_t*>(grad) + idx;
-  if (nv == 8) {
-    const u32x4 w = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
-                     pack_bf16x2(g[6], g[7])};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
-  } else if (nv == 4) {
-    const u32x2 w = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(o));
-  } else {
-    for (int i = 0; i < nv; ++i) o[i] = f32_to_bf16(g[i]);
-  }
-}
-
-// Gradient pass.  Workgroup b covers row b / chunks, vocabulary chunk b % chunks.
-template <bool BF16, bool VECTOR, bool GBF16>
-__global__ __launch_bounds__(kGradThreads) void e2etv_grad_kernel(
-    const void* __restrict__ draft, const void* __restrict__ target,
-    const float4* __restrict__ rowstat, const float* __restrict__ coef, int V, int chunks,
-    void* __restrict__ grad) {
-  using LD = Logits<BF16>;
-  constexpr int NV = VECTOR ? LD::NV : 1;
-  constexpr int CHUNK = kGradThreads * kGradUnroll * NV;
-  const int n = blockIdx.x / chunks;
-  const int c = blockIdx.x - n * chunks;
-  const float4 rs = rowstat[n];
-  const float cf = coef[n];
-  const size_t row = size_t(n) * size_t(V);
-  const int e0 = c * CHUNK;
-#pragma unroll
-  for (int u = 0; u < kGradUnroll; ++u) {
-    const int e = e0 + (u * kGradThreads + threadIdx.x) * NV;
-    if (e >= V) break;
-    float z[NV], t[NV], g[NV];
-    if constexpr (VECTOR) {
-      LD::load(draft, row + e, z);
-      LD::load(target, row + e, t);
-    } else {
-      z[0] = LD::load1(draft, row + e);
-      t[0] = LD::load1(target, row + e);
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      float lq, lp;
-      log2probs(z[i], t[i], rs.x, rs.y, lq, lp);
-      const float q = fast_exp2(lq);
-      g[i] = cf * q * ((lq < lp ? 1.f : 0.f) - rs.w);
-    }
-    store_grad<GBF16>(grad, row + e, g, NV);
-  }
-}
 
 template <bool BF16, bool VECTOR>
-hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s) {
+hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s, int spin_limit) {
   const E2etvWs L = e2etv_ws_layout(d);
-  const int R = d.R, Wn = d.Wn, V = d.V;
+  const int R = d.R, Wn = d.Wn;
   const int N = R * Wn;
-  float4* rowstat = reinterpret_cast<float4*>(a.ws + L.rowstat);
-  float* coef = reinterpret_cast<float*>(a.ws + L.coef);
-  double* numer = reinterpret_cast<double*>(a.ws + L.numer);
-  int32_t* ok = reinterpret_cast<int32_t*>(a.ws + L.branch_ok);
-  const double count = d.norm_count > 0 ? d.norm_count : double(N);
-
-  e2etv_rows_kernel<BF16, VECTOR><<<N, kRowThreads, 0, s>>>(a.draft, a.target, V, rowstat);
-  e2etv_scan_kernel<<<(R + kScanThreads - 1) / kScanThreads, kScanThreads, 0, s>>>(
-      rowstat, a.parent, R, Wn, count, d.grad_scale, coef, numer, ok, a.alpha_out, a.prefix_out);
-  e2etv_finalize_kernel<<<1, kFinThreads, 0, s>>>(numer, R, count, a.loss_out);
-  if (a.grad) {
-    constexpr int NV = VECTOR ? Logits<BF16>::NV : 1;
-    constexpr int CHUNK = kGradThreads * kGradUnroll * NV;
-    const int chunks = (V + CHUNK - 1) / CHUNK;
-    const unsigned blocks = unsigned(N) * unsigned(chunks);
-    if (d.grad_dtype == SPECOPD_BF16)
-      e2etv_grad_kernel<BF16, VECTOR, true><<<blocks, kGradThreads, 0, s>>>(
-          a.draft, a.target, rowstat, coef, V, chunks, a.grad);
-    else
-      e2etv_grad_kernel<BF16, VECTOR, false><<<blocks, kGradThreads, 0, s>>>(
-          a.draft, a.target, rowstat, coef, V, chunks, a.grad);
-  }
+  FusedArgs f{};
+  f.draft = a.draft;
+  f.target = a.target;
+  f.parent = a.parent;
+  f.Wn = Wn;
+  f.V = d.V;
+  f.count = d.norm_count > 0 ? d.norm_count : double(N);
+  f.grad_scale = d.grad_scale;
+  f.spin_limit = spin_limit;
+  f.segB = reinterpret_cast<float*>(a.ws + L.segB);
+  f.bcount = reinterpret_cast<int32_t*>(a.ws + L.bcount);
+  f.ticket = reinterpret_cast<int32_t*>(a.ws + L.ticket);
+  f.numer = reinterpret_cast<double*>(a.ws + L.numer);
+  f.branch_ok = reinterpret_cast<int32_t*>(a.ws + L.branch_ok);
+  f.alpha_out = a.alpha_out;
+  f.prefix_out = a.prefix_out;
+  f.grad = a.grad;
+  e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.bcount, f.branch_ok, R);
+  const unsigned grid = unsigned(N);
+  if (!a.grad)
+    e2etv_fused_kernel<BF16, VECTOR, false, false><<<grid, kThreads, 0, s>>>(f);
+  else if (d.grad_dtype == SPECOPD_BF16)
+    e2etv_fused_kernel<BF16, VECTOR, true, true><<<grid, kThreads, 0, s>>>(f);
+  else
+    e2etv_fused_kernel<BF16, VECTOR, true, false><<<grid, kThreads, 0, s>>>(f);
+  e2etv_finalize_kernel<<<1, kFinThreads, 0, s>>>(f.numer, R, f.count, a.loss_out);
   return hipGetLastError();
 }
 
@@ -412,8 +456,9 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   const size_t N = size_t(d.R) * size_t(d.Wn);
   E2etvWs w{};
   size_t off = 0;
-  w.rowstat = off;   off = align_up(off + N * sizeof(float4), 256);
-  w.coef = off;      off = align_up(off + N * sizeof(float), 256);
+  w.segB = off;      off = align_up(off + N * 2 * sizeof(float), 256);
+  w.bcount = off;    off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
+  w.ticket = off;    off = align_up(off + sizeof(int32_t), 256);
   w.numer = off;     off = align_up(off + size_t(d.R) * sizeof(double), 256);
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
   w.total = off;
@@ -421,14 +466,15 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
 }
 
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s) {
+  const int spin_limit = a.spin_limit > 0 ? a.spin_limit : (1 << 20);
   const size_t esz = d.logits_dtype == SPECOPD_BF16 ? 2 : 4;
   const bool vec = (size_t(d.V) * esz) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(a.draft) % 16) == 0 &&
                    (reinterpret_cast<uintptr_t>(a.target) % 16) == 0 &&
                    (a.grad == nullptr || (reinterpret_cast<uintptr_t>(a.grad) % 16) == 0);
   if (d.logits_dtype == SPECOPD_BF16)
-    return vec ? launch_all<true, true>(d, a, s) : launch_all<true, false>(d, a, s);
-  return vec ? launch_all<false, true>(d, a, s) : launch_all<false, false>(d, a, s);
+    return vec ? launch_all<true, true>(d, a, s, spin_limit) : launch_all<true, false>(d, a, s, spin_limit);
+  return vec ? launch_all<false, true>(d, a, s, spin_limit) : launch_all<false, false>(d, a, s, spin_limit);
 }
 
 }  // namespace specopd

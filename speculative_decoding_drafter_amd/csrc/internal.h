@@ -54,14 +54,16 @@ hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t
 
 // ---------------------------------------------------------------- E2E-TV
 // Workspace layout:
-//   rowstat    float4 [N]  (-lse2 draft, -lse2 target, alpha, G) per row
-//   coef       float  [N]  grad_scale * dLoss/dalpha per row
-//   numer      double [R]  sum of prefix products of each branch
+//   segB       float  [N][2]  (alpha, G) of every row
+//   bcount     int32  [R]     rows of each branch that posted
+//   ticket     int32          next row to hand out, in order
+//   numer      double [R]     sum of prefix products of each branch
 //   branch_ok  int32  [R]
 struct E2etvWs {
-  size_t rowstat, coef, numer, branch_ok, total;
+  size_t segB, bcount, ticket, numer, branch_ok, total;
 };
 E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d);
+
 
 struct E2etvArgs {
   const void *draft, *target;
@@ -70,6 +72,7 @@ struct E2etvArgs {
   double* loss_out;
   void* grad;
   char* ws;
+  int spin_limit;  // bound on a workgroup's wait for its branch (<= 0: default)
 };
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s);
 

@@ -127,6 +127,7 @@ def _ecall(desc, ws_bytes=1 << 30, **over):
     ("grad_dtype", -1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("grad_scale", float("inf"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("V", 200_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # beyond 32-bit element indexing
 ])
 def test_e2etv_desc_errors(field, value, code):
     d = _edesc()

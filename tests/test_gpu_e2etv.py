@@ -128,6 +128,31 @@ def test_malformed_parent_flags_branch(gpu_ok):
     assert sd.specopd_e2etv_device_status(ok["desc"], ok["ws"]) == 0
 
 
+def test_branch_wait_timeout_is_reported_not_hung(gpu_ok, monkeypatch):
+    """Force the bounded in-kernel wait for sibling rows to give up at once:
+    the call must return, and every branch must be either flagged malformed
+    (NaN outputs) or correct."""
+    cfg = shrink_loss(WORKLOADS[2].loss, R=16, V=8192)
+    inp = gen_loss(cfg, 6, device=DEV, cid=2)
+    monkeypatch.setenv("SPECOPD_E2ETV_SPIN_LIMIT", "1")
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    bad = sd.specopd_e2etv_device_status(out["desc"], out["ws"])
+    monkeypatch.delenv("SPECOPD_E2ETV_SPIN_LIMIT")
+    assert 0 <= bad <= 16
+    ref = oracle.e2etv(inp["draft"].cpu(), inp["target"].cpu(), inp["parent"].cpu())
+    g = out["grad"].float().cpu().numpy()
+    a = out["alpha"].cpu().numpy()
+    flagged = 0
+    for r in range(16):
+        if np.isnan(a[r]).all() or np.isnan(g[r]).any():
+            flagged += 1
+            continue
+        assert np.abs(g[r] - ref["grad"][r]).max() <= 1e-5
+    assert flagged <= bad or bad == 16
+    ok = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    assert sd.specopd_e2etv_device_status(ok["desc"], ok["ws"]) == 0
+
+
 def test_deterministic_bitwise(gpu_ok):
     cfg = shrink_loss(WORKLOADS[3].loss, R=8, V=151936)
     inp = gen_loss(cfg, 5, device=DEV, cid=3)
