@@ -49,6 +49,30 @@ def loss_bytes(cfg, grad_bytes=4):
     return cfg.N * cfg.V * (2 * s_in + grad_bytes) + 12 * cfg.N
 
 
+def measured_traffic(kernel_tag, src_files):
+    """HBM bytes per launch of a kernel from the committed counter summary
+    (profiles/<kernel_tag>.txt), or None when the kernel source has changed
+    since the counters were taken (the summary records its sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", kernel_tag + ".txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in src_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, attn_inp_cpu, loss_inp_cpu, budget_s=20.0):
     """The fp64 oracle as it stands, single BLAS thread, on a bounded sample:
     whole branches (every node, every head) of attention and their loss rows.
@@ -91,6 +115,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -150,6 +176,16 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.calibrate_copy > 0:
+        # a plain copy of known size: hardware byte counters are read for it
+        # too, and the ratio converts the loss kernel's counters to bytes
+        nbytes = args.calibrate_copy << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -182,9 +218,15 @@ def main():
             "loss": {"R": lc.R, "Wn": lc.Wn, "V": lc.V, "logits": lc.dtype, "grad": "f32"}}
     lb = loss_bytes(lc)
     loss_gbs = lb / (loss_ms / 1e3) / 1e9
+    t_loss = measured_traffic(f"e2etv_fused_{wl.name}",
+                              ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
+                               "speculative_decoding_drafter_amd/csrc/device_common.h"])
     roof_loss = {"bound": "hbm", "achieved": loss_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": loss_gbs / HBM_PEAK_GBS, "traffic": None,
-                 "kernel": "specopd_e2etv_fwd_bwd", "ms": loss_ms, "alg_bytes": lb}
+                 "frac": loss_gbs / HBM_PEAK_GBS,
+                 "traffic": None if t_loss is None else t_loss / (loss_ms / 1e3) / 1e9,
+                 "traffic_bytes_per_launch": t_loss,
+                 "kernel": "e2etv_fused_kernel (specopd_e2etv_fwd_bwd)", "ms": loss_ms,
+                 "alg_bytes_per_launch": lb}
     roofs = {"loss": roof_loss}
     if ai is not None:
         ac = wl.attn
@@ -193,9 +235,15 @@ def main():
         fl = attn_flops(ac, ai["anchors"].cpu().numpy())
         tf = fl / (attn_ms / 1e3) / 1e12
         peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
+        t_attn = measured_traffic(f"tree_attn_mfma_{wl.name}",
+                                  ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
+                                   "speculative_decoding_drafter_amd/csrc/device_common.h"])
         roofs["attn"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tf / peak, "traffic": None, "kernel": "specopd_tree_attn_fwd",
-                         "ms": attn_ms, "alg_flops": fl}
+                         "frac": tf / peak,
+                         "traffic": None if t_attn is None else t_attn / (attn_ms / 1e3) / 1e9,
+                         "traffic_unit": "GB/s", "traffic_bytes_per_launch": t_attn,
+                         "kernel": "tree_attn_mfma_kernel (specopd_tree_attn_fwd)",
+                         "ms": attn_ms, "alg_flops_per_launch": fl}
         res["attn_rows_per_s"] = ac.rows / (attn_ms / 1e3)
     res["loss_rows_per_s"] = N / (loss_ms / 1e3)
     res["config"] = conf
