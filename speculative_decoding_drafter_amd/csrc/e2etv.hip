@@ -36,6 +36,8 @@ namespace specopd {
 namespace {
 
 constexpr int kThreads = 1024;  // per workgroup (one row)
+constexpr int kCtrStride = 64;  // branch counters 256 B apart, so polls of different
+                                // branches do not all land on one memory channel
 constexpr int kU = 2;           // 16-byte vectors per tensor per thread per batch
 
 // One element's log2-probabilities.  The overlap pass and the gradient pass
@@ -182,7 +184,10 @@ __device__ __forceinline__ bool wait_count(int32_t* ctr, int want, int spin_limi
   int spins = 0;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < want) {
     if (++spins > spin_limit) return false;
-    __builtin_amdgcn_s_sleep(8);
+    if (spins < 8)  // back off after the first polls
+      __builtin_amdgcn_s_sleep(4);
+    else
+      __builtin_amdgcn_s_sleep(32);
   }
   return true;
 }
@@ -210,7 +215,7 @@ __global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restr
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) *ticket = 0;
   if (i < R) {
-    bcount[i] = 0;
+    bcount[size_t(i) * kCtrStride] = 0;
     branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
   }
 }
@@ -304,9 +309,9 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   if (tid == 0) {
     post_f32(a.segB + size_t(n) * 2 + 0, al);
     post_f32(a.segB + size_t(n) * 2 + 1, g);
-    post_count(&a.bcount[r]);
+    post_count(&a.bcount[size_t(r) * kCtrStride]);
     if (need_scan) {
-      bool ok = wait_count(&a.bcount[r], a.Wn, a.spin_limit);
+      bool ok = wait_count(&a.bcount[size_t(r) * kCtrStride], a.Wn, a.spin_limit);
       const int32_t* par = a.parent + size_t(r) * a.Wn;
       const float* sb = a.segB + size_t(r) * a.Wn * 2;
       double sum = 0.0, Gj = 0.0;
@@ -457,7 +462,7 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   E2etvWs w{};
   size_t off = 0;
   w.segB = off;      off = align_up(off + N * 2 * sizeof(float), 256);
-  w.bcount = off;    off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
+  w.bcount = off;    off = align_up(off + size_t(d.R) * kCtrStride * sizeof(int32_t), 256);
   w.ticket = off;    off = align_up(off + sizeof(int32_t), 256);
   w.numer = off;     off = align_up(off + size_t(d.R) * sizeof(double), 256);
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
