@@ -32,11 +32,17 @@ COMMON = [
 
 SOURCES = ["specopd_api.cpp", "e2etv.hip", "tree_attn.hip", "tree_attn_mfma.hip"]
 
+# Matrix-core accumulators live in ordinary VGPRs (the AGPR half of the file
+# serves as extra room): with one wave per SIMD the attention kernel's
+# softmax works on the same registers the matrix core writes, and the
+# default form would shuttle them between the two halves every tile.
+EXTRA = {"tree_attn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -18,8 +18,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   branch_ok  int32  [T*B]      1 = well formed, 0 = malformed (outputs NaN)
 //   order      int32  [T*B]      branches of each trunk by anchor, longest first
 //   rot        rotated branch queries and keys
+//   pstart     int32  [T][npacks+1]  first key tile of each pack (prefix sums)
+//   ctr        int32  [T][Hkv][npacks]  segments of a split pack that finished
+//   part       partial results, two slots per workgroup of the matrix-core grid
 struct TreeAttnWs {
-  size_t anc, branch_ok, order, rot, total;
+  size_t anc, branch_ok, order, rot, pstart, ctr, part, total;
 };
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d);
 
@@ -33,6 +36,16 @@ struct TreeAttnArgs {
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
 
 // Matrix-core path (tree_attn_mfma.hip).  bf16 tensors are passed as uint16_t.
+// Waves per workgroup: 8 (two per SIMD) where a wave's accumulators and
+// query operand fit in 256 registers, 4 (one per SIMD, 512 registers) for
+// head size 256.  A wave owns one block of 32 rows (the kernel is written for
+// several blocks per wave, which more registers would allow).
+constexpr int mfma_waves(int D) { return D == 256 ? 4 : 8; }
+constexpr int mfma_row_blocks(int) { return 1; }
+constexpr int mfma_rows_per_wg(int D) { return mfma_waves(D) * 32 * mfma_row_blocks(D); }
+constexpr int kMfmaGrid = 256;  // workgroups of the matrix-core launch (one per CU)
+size_t mfma_slot_bytes(int D);
+
 struct MfmaParams {
   const uint16_t *trunk_k, *trunk_v;  // [T][L][Hkv][D]
   const uint16_t* qr;                 // rotated, scaled queries [T][B][Wn][Hq][D]
@@ -42,15 +55,17 @@ struct MfmaParams {
   const uint64_t* anc;                // ancestor bitmasks [T][B][Wn]
   const int32_t* branch_ok;           // [T][B]
   const int32_t* order;               // [T][B] branches by anchor, longest first
+  const int32_t* pstart;              // [T][npacks+1]
+  int32_t* ctr;                       // [T][Hkv][npacks], zero on entry
+  char* part;                         // 2 * nwg slots of slot_bytes
+  size_t slot_bytes;
   uint16_t* out;                      // [T][B][Wn][Hq][D]
-  int B, L, Wn, Hq, Hkv, G;
+  int T, B, L, Wn, Hq, Hkv, G;
   int bpp;     // branches per pack
-  int npacks;  // packs per (trunk, kv head)
-  int nunits;  // T * Hkv * npacks
-  int per;     // units per XCD (grid = 8 * per)
+  int npacks;  // packs per trunk
+  int nwg;     // workgroups (multiple of 8, at most kMfmaGrid)
 };
-int mfma_rows_per_wg(int D, int KS);
-hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t s);
+hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------- E2E-TV
 // Workspace layout:

@@ -48,23 +48,6 @@ __global__ void tree_plan_kernel(const int32_t* __restrict__ anchors,
   branch_ok[tb] = ok ? 1 : 0;
 }
 
-// One workgroup per trunk: branch order by anchor, longest first (malformed
-// branches last), ties by index.  Rank sort, O(B^2) comparisons.
-__global__ void tree_sort_kernel(const int32_t* __restrict__ anchors,
-                                 const int32_t* __restrict__ branch_ok, int B,
-                                 int32_t* __restrict__ order) {
-  const size_t tB = size_t(blockIdx.x) * B;
-  for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const int kb = branch_ok[tB + b] ? anchors[tB + b] : -1;
-    int rank = 0;
-    for (int o = 0; o < B; ++o) {
-      const int ko = branch_ok[tB + o] ? anchors[tB + o] : -1;
-      rank += (ko > kb) || (ko == kb && o < b);
-    }
-    order[tB + rank] = b;
-  }
-}
-
 // ---------------------------------------------------------------- rotary
 
 // Rotates every branch query and key at its node's semantic position.  One
@@ -95,6 +78,152 @@ __global__ void rope_branch_kernel(const T* __restrict__ x, const int32_t* __res
       store_f32(dst + i, (x1 * c - x2 * s) * qmul);
       store_f32(dst + i + half, (x2 * c + x1 * s) * qmul);
     }
+  }
+}
+
+// ---------------------------------------------------------------- preparation (bf16 path)
+
+struct PrepParams {
+  const int32_t *anchors, *parent, *pos;
+  const uint16_t *q, *k;
+  uint64_t* anc;
+  int32_t *branch_ok, *order, *pstart, *ctr;
+  uint16_t *qr, *kr;
+  int T, B, L, Wn, Hq, Hkv, D, bpp, npacks;
+  double log2_base;
+  float qmul;
+};
+
+constexpr int kSortLds = 2048;  // branches per trunk whose sort keys are staged in LDS
+
+__device__ void plan_branch(const PrepParams& p, size_t tb) {
+  const int a = p.anchors[tb];
+  bool ok = (a >= 0) && (a < p.L);
+  const int32_t* par = p.parent + tb * p.Wn;
+  const int32_t* ps = p.pos + tb * p.Wn;
+  uint64_t* an = p.anc + tb * p.Wn;
+  for (int j = 0; j < p.Wn; ++j) {
+    const int pj = par[j];
+    uint64_t m = uint64_t(1) << j;
+    if (pj >= 0 && pj < j) {
+      m |= an[pj];  // written by this thread above
+    } else if (pj != -1) {
+      ok = false;
+    }
+    an[j] = m;
+    const int depth = __popcll(m) - 1;
+    if (ps[j] != a + 1 + depth) ok = false;
+  }
+  p.branch_ok[tb] = ok ? 1 : 0;
+}
+
+// Key tiles of pack pk of trunk t: trunk tiles up to its longest anchor, then
+// tail tiles holding the pack's branch nodes.
+__device__ int pack_tiles(const PrepParams& p, int t, int pk) {
+  const size_t tB = size_t(t) * p.B;
+  const int b0 = pk * p.bpp;
+  const int nbr = min(p.bpp, p.B - b0);
+  const int bl = p.order[tB + b0];
+  const int a = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
+  return (a + 32) / 32 + (nbr * p.Wn + 31) / 32;
+}
+
+// One launch prepares everything the matrix-core kernel reads:
+//   workgroups [0, T): one trunk each -- validate its branches and record
+//     ancestor masks, order the branches by anchor (longest first, malformed
+//     last, ties by index; rank sort), tabulate the packs' key tiles as prefix
+//     sums, and clear the trunk's split-pack counters;
+//   the other workgroups: rotary embedding of branch queries (times qmul) and
+//     keys, one thread per (node, four consecutive pairs), angles in fp64.
+__global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
+  const int tid = threadIdx.x;
+  if (int(blockIdx.x) < p.T) {
+    const int t = blockIdx.x;
+    const size_t tB = size_t(t) * p.B;
+    __shared__ int keys[kSortLds];
+    for (int b = tid; b < p.B; b += 256) plan_branch(p, tB + b);
+    __syncthreads();
+    const bool in_lds = p.B <= kSortLds;
+    if (in_lds)
+      for (int b = tid; b < p.B; b += 256) keys[b] = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
+    __syncthreads();
+    for (int b = tid; b < p.B; b += 256) {
+      const int kb = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
+      int rank = 0;
+      for (int o = 0; o < p.B; ++o) {
+        const int ko = in_lds ? keys[o] : (p.branch_ok[tB + o] ? p.anchors[tB + o] : -1);
+        rank += (ko > kb) || (ko == kb && o < b);
+      }
+      p.order[tB + rank] = b;
+    }
+    __syncthreads();
+    // exclusive prefix sums of the packs' tiles: per-thread runs, then a scan
+    // of the 256 run totals
+    __shared__ int run[256];
+    const int np = p.npacks;
+    const int per = (np + 255) / 256;
+    const int lo = min(tid * per, np), hi = min(lo + per, np);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += pack_tiles(p, t, i);
+    run[tid] = sum;
+    __syncthreads();
+    int32_t* ps = p.pstart + size_t(t) * (np + 1);
+    if (tid == 0) {
+      int acc = 0;
+      for (int i = 0; i < 256; ++i) {
+        const int x = run[i];
+        run[i] = acc;
+        acc += x;
+      }
+      ps[np] = acc;
+    }
+    __syncthreads();
+    int acc = run[tid];
+    for (int i = lo; i < hi; ++i) {
+      ps[i] = acc;
+      acc += pack_tiles(p, t, i);
+    }
+    int32_t* c = p.ctr + size_t(t) * p.Hkv * np;
+    for (int i = tid; i < p.Hkv * np; i += 256) c[i] = 0;
+    return;
+  }
+  const int quads = p.D / 8;  // four pairs (i, i + D/2) per thread
+  const int half = p.D / 2;
+  const size_t total = size_t(p.T) * p.B * p.Wn * quads;
+  const size_t stride = size_t(gridDim.x - p.T) * 256;
+  for (size_t idx = size_t(blockIdx.x - p.T) * 256 + tid; idx < total; idx += stride) {
+    const size_t node = idx / quads;
+    const int i0 = int(idx - node * quads) * 4;
+    const double ps = double(p.pos[node]);
+    float c[4], sn[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double theta = exp2(-(2.0 * (i0 + e) / p.D) * p.log2_base);
+      double sd, cd;
+      sincos(ps * theta, &sd, &cd);
+      c[e] = float(cd);
+      sn[e] = float(sd);
+    }
+    auto rotate = [&](const uint16_t* src, uint16_t* dst, int H, float mul) {
+      for (int hd = 0; hd < H; ++hd) {
+        const size_t off = (node * H + hd) * p.D + i0;
+        const u32x2 a = *reinterpret_cast<const u32x2*>(src + off);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(src + off + half);
+        const float x1[4] = {bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1])};
+        const float x2[4] = {bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
+        float y1[4], y2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y1[e] = (x1[e] * c[e] - x2[e] * sn[e]) * mul;
+          y2[e] = (x2[e] * c[e] + x1[e] * sn[e]) * mul;
+        }
+        *reinterpret_cast<u32x2*>(dst + off) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
+        *reinterpret_cast<u32x2*>(dst + off + half) =
+            u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+      }
+    };
+    rotate(p.q, p.qr, p.Hq, p.qmul);
+    rotate(p.k, p.kr, p.Hkv, 1.0f);
   }
 }
 
@@ -187,16 +316,36 @@ __global__ __launch_bounds__(256) void tree_attn_generic_kernel(
 
 // ---------------------------------------------------------------- launch
 
+// Matrix-core plan: branches per pack and packs per trunk; false when the
+// inputs are fp32 or a single branch's rows exceed one workgroup.
+static bool mfma_plan(const specopd_tree_attn_desc& d, int* bpp, int* npacks) {
+  if (d.dtype != SPECOPD_BF16) return false;
+  const int rows_per_branch = d.Wn * (d.Hq / d.Hkv);
+  const int b = mfma_rows_per_wg(d.D) / rows_per_branch;
+  if (b < 1) return false;
+  // per-trunk element offsets are formed in 32 bits
+  const double lim = 2147483647.0;
+  if (double(d.L) * d.Hkv * d.D > lim || double(d.B) * d.Wn * d.Hq * d.D > lim) return false;
+  *bpp = b;
+  *npacks = (d.B + b - 1) / b;
+  return true;
+}
+
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   const size_t TB = size_t(d.T) * d.B, nodes = TB * d.Wn;
+  int bpp = 0, np = 0;
+  const bool mf = mfma_plan(d, &bpp, &np);
   TreeAttnWs w{};
   size_t off = 0;
   w.anc = off;        off = align_up(off + nodes * sizeof(uint64_t), 256);
   w.branch_ok = off;  off = align_up(off + TB * sizeof(int32_t), 256);
   w.order = off;      off = align_up(off + TB * sizeof(int32_t), 256);
-  // rotated branch queries then keys: fp32 for the fp32 path, bf16 for the
-  // matrix-core path (sized for fp32)
-  w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * sizeof(float), 256);
+  // rotated branch queries then keys: bf16 for the matrix-core path, fp32 otherwise
+  const size_t esz = mf ? sizeof(uint16_t) : sizeof(float);
+  w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * esz, 256);
+  w.pstart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
+  w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
+  w.part = off;       off = align_up(off + (mf ? 2 * size_t(kMfmaGrid) * mfma_slot_bytes(d.D) : 0), 256);
   w.total = off;
   return w;
 }
@@ -235,26 +384,6 @@ static hipError_t launch_rope_fp32(const specopd_tree_attn_desc& d, const TreeAt
   return hipGetLastError();
 }
 
-// Matrix-core layout choice: rows per workgroup shrink (more waves split the
-// keys instead) until there are enough workgroups to cover the chip.
-static bool pick_mfma(const specopd_tree_attn_desc& d, int* KS_out, int* bpp_out) {
-  const int rows_per_branch = d.Wn * (d.Hq / d.Hkv);
-  const int ks_max = d.D == 256 ? 2 : 4;
-  int best = -1, best_bpp = 0;
-  for (int KS = 1; KS <= ks_max; KS *= 2) {
-    const int bpp = mfma_rows_per_wg(d.D, KS) / rows_per_branch;
-    if (bpp < 1) break;
-    const long units = long(d.T) * d.Hkv * ((d.B + bpp - 1) / bpp);
-    best = KS;
-    best_bpp = bpp;
-    if (units >= 512) break;
-  }
-  if (best < 0) return false;
-  *KS_out = best;
-  *bpp_out = best_bpp;
-  return true;
-}
-
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s) {
   const TreeAttnWs L = tree_attn_ws_layout(d);
   uint64_t* anc = reinterpret_cast<uint64_t*>(a.ws + L.anc);
@@ -262,19 +391,26 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
   int32_t* order = reinterpret_cast<int32_t*>(a.ws + L.order);
   const int TB = d.T * d.B;
   const int nodes = TB * d.Wn;
-  tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);
   hipError_t e;
-  int KS = 0, bpp = 0;
-  if (d.dtype == SPECOPD_BF16 && pick_mfma(d, &KS, &bpp)) {
-    tree_sort_kernel<<<d.T, 256, 0, s>>>(a.anchors, ok, d.B, order);
+  int bpp = 0, np = 0;
+  if (mfma_plan(d, &bpp, &np)) {
     uint16_t* qr = reinterpret_cast<uint16_t*>(a.ws + L.rot);
     uint16_t* kr = qr + size_t(nodes) * d.Hq * d.D;
-    const double lb = log2(double(a.rope_base));
-    auto grid = [](size_t n) { return unsigned(std::min<size_t>((n + 255) / 256, 65536)); };
-    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
-        static_cast<const uint16_t*>(a.q), a.pos, nodes, d.Hq, d.D, lb, a.scale * kLog2e, qr);
-    rope_branch_kernel<uint16_t, uint16_t><<<grid(size_t(nodes) * d.D / 2), 256, 0, s>>>(
-        static_cast<const uint16_t*>(a.k), a.pos, nodes, d.Hkv, d.D, lb, 1.0f, kr);
+    PrepParams pp{};
+    pp.anchors = a.anchors; pp.parent = a.parent; pp.pos = a.pos;
+    pp.q = static_cast<const uint16_t*>(a.q);
+    pp.k = static_cast<const uint16_t*>(a.k);
+    pp.anc = anc; pp.branch_ok = ok; pp.order = order;
+    pp.pstart = reinterpret_cast<int32_t*>(a.ws + L.pstart);
+    pp.ctr = reinterpret_cast<int32_t*>(a.ws + L.ctr);
+    pp.qr = qr; pp.kr = kr;
+    pp.T = d.T; pp.B = d.B; pp.L = d.L; pp.Wn = d.Wn; pp.Hq = d.Hq; pp.Hkv = d.Hkv; pp.D = d.D;
+    pp.bpp = bpp; pp.npacks = np;
+    pp.log2_base = log2(double(a.rope_base));
+    pp.qmul = a.scale * kLog2e;
+    const size_t rope_threads = size_t(nodes) * (d.D / 8);
+    const unsigned rope_blocks = unsigned(std::min<size_t>((rope_threads + 255) / 256, 8192));
+    tree_prep_kernel<<<unsigned(d.T) + rope_blocks, 256, 0, s>>>(pp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MfmaParams p{};
     p.trunk_k = static_cast<const uint16_t*>(a.trunk_k);
@@ -286,14 +422,18 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.anc = anc;
     p.branch_ok = ok;
     p.order = order;
+    p.pstart = pp.pstart;
+    p.ctr = pp.ctr;
+    p.part = a.ws + L.part;
+    p.slot_bytes = mfma_slot_bytes(d.D);
     p.out = static_cast<uint16_t*>(a.out);
-    p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
+    p.T = d.T; p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
     p.bpp = bpp;
-    p.npacks = (d.B + bpp - 1) / bpp;
-    p.nunits = d.T * d.Hkv * p.npacks;
-    p.per = (p.nunits + 7) / 8;
-    return launch_tree_attn_mfma(d.D, KS, p, s);
+    p.npacks = np;
+    p.nwg = kMfmaGrid;
+    return launch_tree_attn_mfma(d.D, p, s);
   }
+  tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);
   float* qr = reinterpret_cast<float*>(a.ws + L.rot);
   float* kr = qr + size_t(nodes) * d.Hq * d.D;
   if (d.dtype == SPECOPD_BF16) {

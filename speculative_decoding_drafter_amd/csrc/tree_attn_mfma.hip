@@ -3,41 +3,51 @@
 //
 // What is computed (jaehun.me review of SpecOPD, §3.2(a), Eq. 5): every node
 // j of branch b attends to trunk keys 0..a_b of the shared prefilled cache
-// and to the nodes on its own parent chain; rotary embedding at the node's
-// semantic position has already been applied to its query/key by
-// rope_branch_kernel (queries also carry scale * log2(e), so scores come out
-// of the matrix cores in log2 units).
+// and to the nodes on its own parent chain.  Rotary embedding at the node's
+// semantic position has already been applied to its query and key by the
+// preparation kernel; queries also carry scale * log2(e), so scores come out
+// of the matrix cores in log2 units.
 //
-// Work unit = (trunk t, kv head g, pack of branches).  Branches of a trunk are
-// sorted by anchor (longest first) and consecutive ones are packed so that
-// the pack's rows (node x query head of the kv group) fill the workgroup.  All
-// rows of a pack share trunk keys 0..max anchor, so one K/V tile feeds every
-// row; rows whose anchor is shorter mask the tail of the last tiles.  The
-// branches' own nodes form extra "tail" tiles masked by the ancestor bitmask
-// and by branch identity.
+// Packs.  Branches of a trunk are sorted by anchor (longest first) and
+// consecutive ones are packed so that the pack's rows (node x query head of
+// one kv group) fill a workgroup.  All rows of a pack share trunk keys
+// 0..max anchor, so one K/V tile feeds every row; rows whose anchor is shorter
+// mask the tail of the last tiles.  The branches' own nodes form extra "tail"
+// tiles masked by the ancestor bitmask and by branch identity.  A pack's key
+// tiles (trunk tiles, then tail tiles) are its units of work.
 //
-// Wave layout (8 waves, two per SIMD so one wave's softmax overlaps the
-// other's matrix work): KS key slices x (8/KS) row groups.  A row group is NB
-// blocks of 32 rows (one wave).  Waves of the same slice share one
-// double-buffered K/V tile in LDS; waves of different slices take interleaved
-// tiles and are merged at the end through LDS in a fixed order
-// (deterministic).
+// Work split (stream-K).  The units of all (trunk, kv head, pack) triples are
+// laid end to end and a fixed grid cuts the line into equal ranges, one per
+// workgroup, so every compute unit gets the same number of key tiles whatever
+// the anchors are.  A pack cut between workgroups leaves partial results
+// (unnormalised output in bf16, running max and sum in fp32) in the
+// workspace; the workgroup that finishes last merges them in segment order,
+// so the result does not depend on timing.  Consecutive ranges go to the
+// same XCD, so workgroups that read the same trunk rows share an L2.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, lane l = r + 32h):
-//   S^T[key][row] = K[key][:] . Q[row][:]      A = K tile (LDS, 16 B reads),
-//                                              B = Q^T (registers)
+//   S^T[key][row] = K[key][:] . Q[row][:]      A = K tile (LDS, 16-byte
+//                                              reads), B = Q^T (registers)
 //   lane (r, h) holds row r's scores for keys 8(i/4) + 4h + i%4, i = 0..15,
 //   which is exactly the B operand P^T of the second product for k-steps of
-//   16 keys (elements 8s..8s+7 -> keys 16s + 8(e/4) + 4h + e%4), so P never
-//   leaves registers;
+//   16 keys, so P never leaves registers;
 //   O^T[dim][row] += V^T[dim][key] . P^T[key][row]
 //                                              A = V^T read from the row-major
-//                                              V tile with ds_read_b64_tr_b16
-//                                              (each 16-lane group turns four
-//                                              4-element rows into columns).
-// Softmax is online in log2 units with a lazily moved reference maximum: the
-// accumulators are rescaled only when a row's maximum grows by more than
-// 2^8, so the common tile costs no rescale.
+//                                              V tile with ds_read_b64_tr_b16.
+// LDS rows are padded (K by 16 bytes, V by 32) so that both read patterns hit
+// distinct banks of the 64-bank LDS.
+//
+// Pipeline per wave: while the exponentials of tile i are formed on the
+// vector ALU, the matrix core already computes the scores of tile i + 1; the
+// products with V of tile i follow.  Tiles go from global memory straight
+// into LDS (global_load_lds: each lane of a wave-wide load writes 16 bytes at
+// base + 16 * lane), three tiles ahead through four LDS buffers, one barrier
+// per tile.  Lanes whose 16 bytes land on a row's pad chunk load a harmless
+// in-bounds chunk that is never read.
+//
+// Softmax is online in log2 units against a per-row reference maximum m that
+// moves only when a score exceeds it by more than 2^8, so the common tile
+// costs no rescale of the accumulators.
 #include "device_common.h"
 #include "internal.h"
 
@@ -52,34 +62,25 @@ namespace {
 
 constexpr int KT = 32;            // keys per tile
 constexpr float kRescale = 8.0f;  // log2 headroom before the reference max moves
-constexpr float kFarNeg = -1.0e30f;
+constexpr float kUnset = -3.0e38f;
 
-// Waves per workgroup: 8 (two per SIMD) where a wave fits in 256 registers;
-// 4 for D = 256, whose accumulators and query operand need more.
 template <int D>
-constexpr int waves_for() { return D == 256 ? 4 : 8; }
-
-template <int D, int NB, int KS>
-struct Shape {
-  static constexpr int NW = waves_for<D>();
-  static constexpr int RG = NW / KS;         // row groups per workgroup
-  static constexpr int ROWS_G = 32 * NB;     // rows per row group (one wave)
-  static constexpr int RW = RG * ROWS_G;     // rows per workgroup
-  static constexpr int LDK = D + 8;          // LDS row stride (elements); +16 B spreads banks
-  static constexpr int TILE = KT * LDK;      // elements of one K (or V) tile
-  static constexpr int SLICE = 2 * 2 * TILE; // double-buffered K and V
-  static constexpr int TILES_BYTES = KS * SLICE * 2;
-  static constexpr int OREGS = NB * D / 2;   // fp32 accumulator registers per lane
-  static constexpr int COMB_WORDS = (KS > 1) ? (KS - 1) * RG * (OREGS + 2 * NB) * 64 : 0;
-  static constexpr int LDS_BYTES = TILES_BYTES > COMB_WORDS * 4 ? TILES_BYTES : COMB_WORDS * 4;
-  static constexpr int CHUNKS = 2 * KT * D / 8;  // 16-byte pieces of a K+V tile
-  // threads filling one slice's tile (capped so every loader has a K and a V piece)
-  static constexpr int LOADERS = 64 * RG < CHUNKS / 2 ? 64 * RG : CHUNKS / 2;
-  static constexpr int CPT = CHUNKS / LOADERS;   // pieces per loader (first half K)
-  static_assert(CHUNKS % LOADERS == 0 && CPT % 2 == 0, "tile must split evenly over loaders");
+struct Geo {
+  static constexpr int NW = mfma_waves(D);       // waves per workgroup
+  static constexpr int NB = mfma_row_blocks(D);  // 32-row blocks per wave
+  static constexpr int OREG = D / 32;            // 16-register accumulator blocks per row block
+  static constexpr int CH = D / 8;               // 16-byte chunks of a key row
+  static constexpr int KROW = 2 * D + 16;        // LDS bytes per K row (one pad chunk)
+  static constexpr int VROW = 2 * D + 32;        // LDS bytes per V row (two pad chunks)
+  static constexpr int SK = KROW / 16, SV = VROW / 16;
+  static constexpr int KBYTES = KT * KROW;
+  static constexpr int NJ = (KBYTES + KT * VROW + 1023) / 1024;  // 1 KB writes a tile needs
+  static constexpr int JPW = (NJ + NW - 1) / NW; // wave writes per tile (every wave the same)
+  static constexpr int BUFB = JPW * NW * 1024;   // bytes of one staged K+V tile, with slack
+  static constexpr int NBUF = 4;
 };
 
-__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+__device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(p));
 }
@@ -94,324 +95,526 @@ __device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int Wn, 
   return uint32_t(w);
 }
 
-template <int D, int NB, int KS>
-__global__ __launch_bounds__(waves_for<D>() * 64, 1) void tree_attn_mfma_kernel(const MfmaParams p) {
-  using S = Shape<D, NB, KS>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[S::LDS_BYTES / 2];
+// Workgroup holding line position x when the line of W units is cut into
+// nwg ranges [floor(w W / nwg), floor((w+1) W / nwg)).
+__device__ __forceinline__ int range_owner(long long x, long long W, int nwg) {
+  return int(((x + 1) * nwg - 1) / W);
+}
+__device__ __forceinline__ long long range_begin(int w, long long W, int nwg) {
+  return (long long)w * W / nwg;
+}
+
+// Wait until at most n of this wave's vector-memory operations are in flight
+// (n is wave-uniform and small).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+  }
+}
+// Workgroup barrier for LDS traffic: this wave's LDS reads and writes are
+// done, global-to-LDS loads are waited for separately (wait_vm), so loads of
+// later tiles stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void post_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint32_t peek_u32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float peek_f32(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void post_f32(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Raw scores (log2 units) of a staged K tile against this wave's queries.
+template <int D>
+__device__ __forceinline__ void tile_scores(const char* kl,
+                                            const bf16x8 (&qop)[Geo<D>::NB][D / 16],
+                                            f32x16 (&S)[Geo<D>::NB]) {
+  constexpr int NB = Geo<D>::NB;
+#pragma unroll
+  for (int s2 = 0; s2 < D / 16; ++s2) {
+    const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kl + 32 * s2);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      S[nb] = s2 == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s2], f32x16{}, 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s2], S[nb], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T for a staged V tile (vl: this lane's first transposed read).
+// vl is restrict-qualified so that the transposed reads carry alias
+// information; without any, the compiler makes them wait for every
+// global-to-LDS load in flight.
+template <int D>
+__device__ __forceinline__ void tile_pv(const char* __restrict__ vl,
+                                        const bf16x8 (&P)[Geo<D>::NB][2],
+                                        f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
+  using Gm = Geo<D>;
+#pragma unroll
+  for (int db = 0; db < Gm::OREG; ++db) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const s16x4 va = lds_read_tr(vl + 16 * s2 * Gm::VROW + 64 * db);
+      const s16x4 vc = lds_read_tr(vl + (16 * s2 + 8) * Gm::VROW + 64 * db);
+      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int nb = 0; nb < Gm::NB; ++nb)
+        oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[nb][s2], oacc[nb][db], 0, 0, 0);
+    }
+  }
+}
+
+// Probabilities of one tile (bf16, as the V product uses them) and their sum.
+template <int D>
+__device__ __forceinline__ void tile_probs(const f32x16 (&S)[Geo<D>::NB], const float (&mref)[Geo<D>::NB],
+                                           float (&lsum)[Geo<D>::NB], bf16x8 (&P)[Geo<D>::NB][2]) {
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int nb = 0; nb < Geo<D>::NB; ++nb) {
+    float acc = lsum[nb];
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(S[nb][i] - mref[nb])),
+                         static_cast<__bf16>(fast_exp2(S[nb][i + 1] - mref[nb]))};
+      P[nb][i >> 3][i & 7] = e2[0];
+      P[nb][i >> 3][(i & 7) + 1] = e2[1];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc, false);  // sums the bf16 weights used below
+    }
+    lsum[nb] = acc;
+  }
+}
+
+// Loads key tile v (trunk tile, or tail tile of branch nodes) of the current
+// pack into LDS buffer b: this wave's share of the wave-wide 1 KB writes.
+// A plain function rather than a lambda: a lambda's closure here stays in
+// private memory.
+template <int D>
+__device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk, int kvrow, int Wn,
+                                         int wave, const uint16_t* tk, const uint16_t* tv,
+                                         const uint16_t* bk, const uint16_t* bv,
+                                         const int32_t* pord, char* lb,
+                                         const int (&dcode)[Geo<D>::JPW]) {
+  using Gm = Geo<D>;
+  const bool trunk = v < ntrunk;
+#pragma unroll
+  for (int q = 0; q < Gm::JPW; ++q) {
+    const int code = dcode[q];
+    const int key = code & 31, c = (code >> 5) & 127;
+    const bool isv = (code >> 12) & 1;
+    const uint16_t* src;
+    if (trunk) {
+      const int off = min(v * KT + key, Lk - 1) * kvrow + c * 8;
+      src = (isv ? tv : tk) + off;
+    } else {
+      int tau = (v - ntrunk) * KT + key;
+      if (tau >= nt_total) tau = 0;
+      const int sl = tau / Wn;
+      const int node = tau - sl * Wn;
+      // branch of a tail slot from global memory: an LDS read here would make
+      // the compiler wait for every load in flight before later LDS reads
+      const int off = (pord[sl] * Wn + node) * kvrow + c * 8;
+      src = (isv ? bv : bk) + off;
+    }
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(
+                                              lb + (wave + Gm::NW * q) * 1024), 16, 0, 0);
+  }
+}
+
+// One steady-state tile: start the load of a later tile into dbuf, score the
+// next tile (K in kbuf) and accumulate this one (V in vbuf); the three
+// buffers are distinct.
+template <int D>
+__device__ __forceinline__ void tile_step(char* dbuf, const char* kbuf,
+                                          const char* vbuf, bool load, int vload,
+                                          int ntrunk, int nt_total, int Lk, int kvrow, int Wn, int wave,
+                                          const uint16_t* tk, const uint16_t* tv, const uint16_t* bk,
+                                          const uint16_t* bv, const int32_t* pord,
+                                          const int (&dcode)[Geo<D>::JPW],
+                                          const bf16x8 (&qop)[Geo<D>::NB][D / 16],
+                                          const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
+                                          const float (&mref)[Geo<D>::NB], float (&lsum)[Geo<D>::NB],
+                                          f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
+  if (load)
+    dma_tile<D>(vload, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, pord, dbuf, dcode);
+  tile_scores<D>(kbuf, qop, Snext);
+  bf16x8 P[Geo<D>::NB][2];
+  tile_probs<D>(Scur, mref, lsum, P);
+  tile_pv<D>(vbuf, P, oacc);
+}
+
+template <int D>
+__global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(const MfmaParams p) {
+  using Gm = Geo<D>;
+  constexpr int NB = Gm::NB, OREG = Gm::OREG;
+  // The kernel's only LDS object (tile buffers, then one flag word): with a
+  // second __shared__ variable the compiler tags LDS accesses with alias
+  // scopes and then waits for every global-to-LDS load before any LDS read.
+  __shared__ __attribute__((aligned(1024))) char smem[Gm::NBUF * Gm::BUFB + 16];
+  int* const s_last = reinterpret_cast<int*>(smem + Gm::NBUF * Gm::BUFB);
+  static_assert(Gm::JPW <= 9, "wait_vm covers at most 9 loads per tile");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int slice = wave % KS, rgrp = wave / KS;
   const int h = lane >> 5, r32 = lane & 31;
-
-  // XCD-aware unit order: workgroups are dealt to the 8 XCDs round robin, so
-  // consecutive units (same trunk and kv head, hence same K/V) land on one XCD.
-  const int bid = blockIdx.x;
-  const int u = (bid & 7) * p.per + (bid >> 3);
-  if (u >= p.nunits) return;
-  const int pk = u % p.npacks;
-  const int tg = u / p.npacks;
-  const int g = tg % p.Hkv, t = tg / p.Hkv;
-  const int rows_per_branch = p.Wn * p.G;
-  const size_t tB = size_t(t) * p.B;
-  const int32_t* ord = p.order + tB;
-  const int b0 = pk * p.bpp;
-  const int nbr = min(p.bpp, p.B - b0);
-
-  int amax = -1, amin = 0x7fffffff;
-  for (int i = 0; i < nbr; ++i) {
-    const int b = ord[b0 + i];
-    const int a = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
-    amax = max(amax, a);
-    amin = min(amin, a);
-  }
-
-  // ---- this lane's rows: metadata and the Q^T operand
-  int ra[NB], rslot[NB];
-  uint64_t rmask[NB];
-  bf16x8 qop[NB][D / 16];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int rho = rgrp * S::ROWS_G + nb * 32 + r32;
-    const int slot = rho / rows_per_branch;
-    const int within = rho - slot * rows_per_branch;
-    const int j = within / p.G;
-    const int hh = within - j * p.G;
-    const bool exists = slot < nbr;
-    const int b = exists ? ord[b0 + slot] : 0;
-    const bool ok = exists && p.branch_ok[tB + b];
-    ra[nb] = ok ? p.anchors[tB + b] : -1;
-    rslot[nb] = slot;
-    rmask[nb] = ok ? p.anc[(tB + b) * p.Wn + j] : 0ull;
-    const uint16_t* qrow = p.qr + ((((tB + b) * p.Wn + j) * p.Hq) + size_t(g) * p.G + hh) * D;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qop[nb][s] = ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * h) : bf16x8{};
-  }
-
-  const int ntrunk = (amax + 1 + KT - 1) / KT;
-  const int nt_total = nbr * p.Wn;
-  const int ntail = (nt_total + KT - 1) / KT;
-  const int nvt = ntrunk + ntail;
-  const int iters = (nvt + KS - 1) / KS;
-
-  // ---- tile staging (global -> registers -> LDS), two tiles ahead.  Piece c
-  // of a loader: the first CPT/2 are K, the rest V (compile-time split).
-  uint16_t* sbase = smem + slice * S::SLICE;
-  const int li = rgrp * 64 + lane;
-  constexpr int HALF = S::CPT / 2;
-  u32x4 stage[S::CPT];
-  auto load_tile = [&](int vt) {
-    const bool trunk = vt < ntrunk;
-    if (li >= S::LOADERS) return;
-#pragma unroll
-    for (int c = 0; c < S::CPT; ++c) {
-      const int rem = li + (c % HALF) * S::LOADERS;
-      const int key = rem / (D / 8);
-      const int part = rem - key * (D / 8);
-      size_t row;
-      if (trunk) {
-        row = (size_t(t) * p.L + min(vt * KT + key, p.L - 1)) * p.Hkv + g;
-      } else {
-        int tau = (vt - ntrunk) * KT + key;
-        if (tau >= nt_total) tau = 0;
-        const int sl = tau / p.Wn;
-        const int node = tau - sl * p.Wn;
-        row = ((tB + size_t(ord[b0 + sl])) * p.Wn + node) * p.Hkv + g;
-      }
-      const uint16_t* base = c < HALF ? (trunk ? p.trunk_k : p.kr) : (trunk ? p.trunk_v : p.v);
-      stage[c] = *reinterpret_cast<const u32x4*>(base + row * D + part * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    if (li >= S::LOADERS) return;
-#pragma unroll
-    for (int c = 0; c < S::CPT; ++c) {
-      const int rem = li + (c % HALF) * S::LOADERS;
-      const int key = rem / (D / 8);
-      const int part = rem - key * (D / 8);
-      *reinterpret_cast<u32x4*>(sbase + (buf * 2 + c / HALF) * S::TILE + key * S::LDK + part * 8) =
-          stage[c];
-    }
-  };
-
-  // ---- accumulators
-  f32x16 oacc[NB][D / 32];
-  float mref[NB], lsum[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    mref[nb] = kFarNeg;
-    lsum[nb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[nb][db] = f32x16{};
-  }
-
-  if (slice < nvt) {
-    load_tile(slice);
-    store_tile(0);
-  }
-  if (KS + slice < nvt) load_tile(KS + slice);
-  __syncthreads();
-
   const int gi = lane >> 4, rq = lane & 15;
+  const int nwg = gridDim.x;
+
+  // XCD-aware range order: workgroups are dealt to the 8 XCDs round robin, so
+  // workgroup u below takes a range next to those of the other workgroups on
+  // its XCD.
+  const int u = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int np = p.npacks;
+  const int psz = np + 1;
+
+  long long W = 0;
+  for (int t = 0; t < p.T; ++t) W += (long long)p.Hkv * p.pstart[size_t(t) * psz + np];
+  const long long s0 = range_begin(u, W, nwg), s1 = range_begin(u + 1, W, nwg);
+  if (s0 >= s1) return;
+
+  const int rows_per_branch = p.Wn * p.G;
+  // scalars the helper lambdas use, copied so that no lambda takes the
+  // address of the kernel argument block (that would move it to scratch)
+  const int Lk = p.L, Wn = p.Wn;
+  char* const part = p.part;
+  const size_t slot_bytes = p.slot_bytes;
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-  for (int it = 0; it < iters; ++it) {
-    const int vt = it * KS + slice;
-    const int buf = it & 1;
-    if (vt < nvt) {
-      const uint16_t* Kt = sbase + (buf * 2) * S::TILE;
-      const uint16_t* Vt = Kt + S::TILE;
-      f32x16 sacc[NB];
+
+  // This lane's 16-byte slot in each of its wave's tile loads: key row,
+  // chunk, K or V.  Pad chunks and the slack after the V rows load chunk 0 of
+  // a valid row.
+  int dcode[Gm::JPW];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
+  for (int q = 0; q < Gm::JPW; ++q) {
+    const int pos = (wave + Gm::NW * q) * 64 + lane;
+    int key = 0, c = 0, isv = 0;
+    if (pos < KT * Gm::SK) {
+      key = pos / Gm::SK;
+      c = pos - key * Gm::SK;
+    } else if (pos < KT * (Gm::SK + Gm::SV)) {
+      const int pv = pos - KT * Gm::SK;
+      key = pv / Gm::SV;
+      c = pv - key * Gm::SV;
+      isv = 1;
+    }
+    if (c >= Gm::CH) c = 0;
+    dcode[q] = key | (c << 5) | (isv << 12);
+  }
+
+  long long s = s0, base = 0;
+  int t = 0;
+  while (s < s1) {
+    const int* ps = p.pstart + size_t(t) * psz;
+    const int Wt = ps[np];
+    const long long rel = s - base;
+    if (rel >= (long long)p.Hkv * Wt) {
+      base += (long long)p.Hkv * Wt;
+      ++t;
+      continue;
+    }
+    const int g = int(rel / Wt);
+    const int r = int(rel - (long long)g * Wt);
+    int lo = 0, hi = np;  // largest pack whose first unit is <= r
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (ps[mid] <= r) lo = mid; else hi = mid;
+    }
+    const int pk = lo;
+    const int v0 = r - ps[pk];
+    const int nvt = ps[pk + 1] - ps[pk];
+    const int n = int(min((long long)(nvt - v0), s1 - s));
+    const long long pack_start = base + (long long)g * Wt + ps[pk];
+    s += n;
+
+    // ---- pack geometry
+    const size_t tB = size_t(t) * p.B;
+    const int32_t* ord = p.order + tB;
+    const int b0 = pk * p.bpp;
+    const int nbr = min(p.bpp, p.B - b0);
+    const int bl = ord[b0];
+    const int amax = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
+    const int ntrunk = (amax + KT) / KT;
+    const int nt_total = nbr * p.Wn;
+
+    // per-segment bases (uniform); per-lane offsets below stay in 32 bits
+    const uint16_t* tk = p.trunk_k + (size_t(t) * p.L * p.Hkv + g) * D;
+    const uint16_t* tv = p.trunk_v + (size_t(t) * p.L * p.Hkv + g) * D;
+    const uint16_t* bk = p.kr + (tB * p.Wn * p.Hkv + g) * D;
+    const uint16_t* bv = p.v + (tB * p.Wn * p.Hkv + g) * D;
+    const int kvrow = p.Hkv * D;  // elements between consecutive keys
+
+    // ---- this lane's rows: metadata and the Q^T operand
+    int ra[NB], rslot[NB];
+    uint64_t rmask[NB];
+    bf16x8 qop[NB][D / 16];
+    int wmin = 0x7fffffff;
+    {
+      const uint16_t* qb = p.qr + (tB * p.Wn * p.Hq + size_t(g) * p.G) * D;
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(Kt + r32 * S::LDK + 16 * s + 8 * h);
+      for (int nb = 0; nb < NB; ++nb) {
+        const int rho = (wave * NB + nb) * 32 + r32;
+        const int slot = rho / rows_per_branch;
+        const int within = rho - slot * rows_per_branch;
+        const int j = within / p.G;
+        const int hh = within - j * p.G;
+        const bool exists = slot < nbr;
+        const int b = exists ? ord[b0 + slot] : 0;
+        const bool ok = exists && p.branch_ok[tB + b];
+        ra[nb] = ok ? p.anchors[tB + b] : amax;  // rows without output never force a mask
+        rslot[nb] = slot;
+        rmask[nb] = ok ? p.anc[(tB + b) * p.Wn + j] : 0ull;
+        wmin = min(wmin, ra[nb]);
+        const uint16_t* qrow = qb + ((b * p.Wn + j) * p.Hq + hh) * D;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s], sacc[nb], 0, 0, 0);
+        for (int s2 = 0; s2 < D / 16; ++s2)
+          qop[nb][s2] = ok ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s2 + 8 * h) : bf16x8{};
       }
-      // masks: trunk keys beyond a row's anchor (edge tiles only); tail keys
-      // of other branches or outside the row's ancestor chain
-      if (vt < ntrunk) {
-        const int k0 = vt * KT;
-        if (k0 + KT - 1 > amin) {
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wmin = min(wmin, __shfl_xor(wmin, o, 64));
+    const int wave_amin = __builtin_amdgcn_readfirstlane(wmin);
+
+    // ---- tile loads: global -> LDS buffer b
+#define DMA_TILE(v, b) dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode)
+    const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
+    const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
+
+    // ---- running state
+    f32x16 oacc[NB][OREG];
+    float mref[NB], lim[NB], lsum[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      mref[nb] = 0.f;
+      lim[nb] = kUnset;
+      lsum[nb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
+    }
+
+    // trunk keys beyond a row's anchor (edge tiles only); tail keys of other
+    // branches or outside the row's ancestor chain
+    auto mask = [&](int v, f32x16 (&S)[NB]) __attribute__((always_inline)) {
+      if (v < ntrunk) {
+        const int k0 = v * KT;
+        if (k0 + KT - 1 > wave_amin) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
-            const int lim = ra[nb] - k0 - 4 * h;  // element i visible iff 8(i/4)+(i%4) <= lim
+            const int lm = ra[nb] - k0 - 4 * h;  // element i visible iff 8(i/4)+(i%4) <= lm
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (8 * (i >> 2) + (i & 3) > lim) sacc[nb][i] = kNegInf;
+              if (8 * (i >> 2) + (i & 3) > lm) S[nb][i] = kNegInf;
           }
         }
       } else {
-        const int tau0 = (vt - ntrunk) * KT;
+        const int tau0 = (v - ntrunk) * KT;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t vis = tail_window(rmask[nb], rslot[nb], p.Wn, tau0) >> (4 * h);
+          const uint32_t vis = tail_window(rmask[nb], rslot[nb], Wn, tau0) >> (4 * h);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (!((vis >> (8 * (i >> 2) + (i & 3))) & 1u)) sacc[nb][i] = kNegInf;
+            if (!((vis >> (8 * (i >> 2) + (i & 3))) & 1u)) S[nb][i] = kNegInf;
         }
       }
-      // online softmax (log2 units), lazily rescaled
-      bool need[NB];
+    };
+    // move the reference maximum of rows that need it (rare)
+    auto settle = [&](f32x16 (&S)[NB]) __attribute__((always_inline)) {
       bool any = false;
-      float mt[NB];
+      float mx[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        float m = sacc[nb][0];
+        float m = S[nb][0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, sacc[nb][i]);
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        mt[nb] = m;
-        need[nb] = m > mref[nb] + kRescale;
-        any |= need[nb];
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
+        mx[nb] = m;
+        any |= m > lim[nb];
       }
       if (__any(any)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const float alpha = need[nb] ? fast_exp2(mref[nb] - mt[nb]) : 1.0f;
-          mref[nb] = need[nb] ? mt[nb] : mref[nb];
-          lsum[nb] *= alpha;
+          const float m = fmaxf(mx[nb], __shfl_xor(mx[nb], 32, 64));  // whole row
+          const bool nd = m > lim[nb];
+          const float f = (nd && lim[nb] != kUnset) ? fast_exp2(mref[nb] - m) : 1.0f;
+          lsum[nb] *= f;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) oacc[nb][db] *= alpha;
+          for (int db = 0; db < OREG; ++db) oacc[nb][db] *= f;
+          mref[nb] = nd ? m : mref[nb];
+          lim[nb] = nd ? m + kRescale : lim[nb];
         }
       }
-      bf16x8 pop[NB][2];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float ps = lsum[nb];
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(sacc[nb][i] - mref[nb])),
-                             static_cast<__bf16>(fast_exp2(sacc[nb][i + 1] - mref[nb]))};
-          pop[nb][i >> 3][i & 7] = e2[0];
-          pop[nb][i >> 3][(i & 7) + 1] = e2[1];
-          ps = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, ps, false);  // sums the bf16 weights used below
-        }
-        lsum[nb] = ps;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const uint16_t* vb = Vt + (16 * s2 + 4 * (gi >> 1) + (rq >> 2)) * S::LDK + 32 * db +
-                               16 * (gi & 1) + 4 * (rq & 3);
-          const s16x4 va = lds_read_tr(vb);
-          const s16x4 vc = lds_read_tr(vb + 8 * S::LDK);
-          const bf16x8 vop = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[nb][s2], oacc[nb][db], 0, 0, 0);
-        }
-      }
-    }
-    if (it + 1 < iters) {
-      if (vt + KS < nvt) store_tile(buf ^ 1);
-      if (vt + 2 * KS < nvt) load_tile(vt + 2 * KS);
-    }
-    __syncthreads();
-  }
+    };
+    // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight
+    DMA_TILE(v0, 0);
+    if (n > 1) DMA_TILE(v0 + 1, 1);
+    if (n > 2) DMA_TILE(v0 + 2, 2);
+    wait_vm(n > 2 ? Gm::JPW : 0);
+    lds_barrier();
 
-  // ---- merge key slices (fixed order), then normalise and write
-  if constexpr (KS > 1) {
-    float* comb = reinterpret_cast<float*>(smem);
-    constexpr int PER = S::OREGS + 2 * NB;  // O registers, then (m, l), per row block
-    if (slice > 0) {
-      float* dst = comb + size_t((rgrp * (KS - 1) + (slice - 1)) * PER) * 64;
-      int k = 0;
+    f32x16 Sa[NB], Sb[NB];
+    tile_scores<D>(smem + koff, qop, Sa);
+    mask(v0, Sa);
+    settle(Sa);
+
+    // one tile: scores of tile i+1 overlap the probabilities of tile i
+    for (int i = 0; i < n; ++i) {
+      const bool more = i + 1 < n;
+      // load tile i+3 into the buffer of tile i-1 (free since the last barrier);
+      // the scores of tile i+1 are unused after the last tile (they keep the
+      // block straight)
+      tile_step<D>(smem + ((i + 3) & 3) * Gm::BUFB, smem + ((i + 1) & 3) * Gm::BUFB + koff,
+                   smem + (i & 3) * Gm::BUFB + voff, i + 3 < n, v0 + i + 3, ntrunk, nt_total, Lk, kvrow,
+                   Wn, wave, tk, tv, bk, bv, ord + b0, dcode, qop, Sa, Sb, mref, lsum, oacc);
+      if (more) {
+        mask(v0 + i + 1, Sb);
+        settle(Sb);
+      }
+      wait_vm(i + 3 < n ? Gm::JPW : 0);  // tile i+2 has landed
+      lds_barrier();
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Sa[nb] = Sb[nb];
+    }
+
+#undef DMA_TILE
+
+    // ---- finish the pack (or this workgroup's segment of it)
+    const bool whole = (v0 == 0) && (n == nvt);
+    bool write = whole;
+    if (!whole) {
+      // segment bookkeeping
+      const long long pend = pack_start + nvt;
+      // workgroups whose (non-empty) ranges cut this pack; with fewer units
+      // than workgroups some ranges in between are empty
+      const int wfirst = range_owner(pack_start, W, nwg);
+      const int wlast = range_owner(pend - 1, W, nwg);
+      auto nonempty = [=](int w) __attribute__((always_inline)) {
+        return range_begin(w + 1, W, nwg) > range_begin(w, W, nwg);
+      };
+      int nseg = 0;
+      for (int w = wfirst; w <= wlast; ++w) nseg += nonempty(w);
+      const size_t ctr_i = (size_t(t) * p.Hkv + g) * np + pk;
+      auto slot_of = [=](int w) __attribute__((always_inline)) -> char* {
+        const int side = (w == wfirst && range_begin(w, W, nwg) < pack_start) ? 1 : 0;
+        return part + size_t(2 * w + side) * slot_bytes;
+      };
+      constexpr int OWORDS = NB * OREG * 8;  // bf16 pairs per lane
+      char* mine = slot_of(u);
+      uint32_t* po = reinterpret_cast<uint32_t*>(mine) + wave * OWORDS * 64 + lane;
+      float* pm = reinterpret_cast<float*>(mine + Gm::NW * OWORDS * 64 * 4) + wave * NB * 128 + lane;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < OREG; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) dst[(k++) * 64 + lane] = oacc[nb][db][i];
-        dst[(k++) * 64 + lane] = mref[nb];
-        dst[(k++) * 64 + lane] = lsum[nb];
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t w2 = pack_bf16x2(oacc[nb][db][2 * k], oacc[nb][db][2 * k + 1]);
+            post_u32(po + ((nb * OREG + db) * 8 + k) * 64, w2);
+          }
+        post_f32(pm + nb * 128, lim[nb] == kUnset ? kNegInf : mref[nb]);
+        post_f32(pm + nb * 128 + 64, lsum[nb]);
       }
-    }
-    __syncthreads();
-    if (slice == 0) {
-#pragma unroll 1
-      for (int o = 1; o < KS; ++o) {
-        const float* src = comb + size_t((rgrp * (KS - 1) + (o - 1)) * PER) * 64;
-        int k = 0;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged first
+      __syncthreads();
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(p.ctr + ctr_i, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_SYSTEM);
+        *s_last = old == nseg - 1;
+      }
+      __syncthreads();
+      write = *s_last != 0;
+      if (write) {
+        // merge every segment, this one included, from the stored values in
+        // segment order, so the result does not depend on who merges
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const int kb = k;
-          k += S::OREGS / NB;
-          const float m2 = src[(k++) * 64 + lane];
-          const float l2 = src[(k++) * 64 + lane];
-          const float mn = fmaxf(mref[nb], m2);
-          const float a0 = fast_exp2(mref[nb] - mn), a1 = fast_exp2(m2 - mn);
-          int kk = kb;
+          mref[nb] = kNegInf;
+          lsum[nb] = 0.f;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+          for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
+        }
+        for (int w = wfirst; w <= wlast; ++w) {
+          if (!nonempty(w)) continue;
+          const char* sl = slot_of(w);
+          const uint32_t* qo = reinterpret_cast<const uint32_t*>(sl) + wave * OWORDS * 64 + lane;
+          const float* qm = reinterpret_cast<const float*>(sl + Gm::NW * OWORDS * 64 * 4) +
+                            wave * NB * 128 + lane;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              oacc[nb][db][i] = oacc[nb][db][i] * a0 + src[(kk++) * 64 + lane] * a1;
-          lsum[nb] = lsum[nb] * a0 + l2 * a1;
-          mref[nb] = mn;
+          for (int nb = 0; nb < NB; ++nb) {
+            const float m2 = peek_f32(qm + nb * 128);
+            const float l2 = peek_f32(qm + nb * 128 + 64);
+            const float mn = fmaxf(mref[nb], m2);
+            const float a0 = mref[nb] == kNegInf ? 0.f : fast_exp2(mref[nb] - mn);
+            const float a1 = m2 == kNegInf ? 0.f : fast_exp2(m2 - mn);
+#pragma unroll
+            for (int db = 0; db < OREG; ++db)
+#pragma unroll
+              for (int k = 0; k < 8; ++k) {
+                const uint32_t w2 = peek_u32(qo + ((nb * OREG + db) * 8 + k) * 64);
+                oacc[nb][db][2 * k] = oacc[nb][db][2 * k] * a0 + bf16_lo(w2) * a1;
+                oacc[nb][db][2 * k + 1] = oacc[nb][db][2 * k + 1] * a0 + bf16_hi(w2) * a1;
+              }
+            lsum[nb] = lsum[nb] * a0 + l2 * a1;
+            mref[nb] = mn;
+          }
         }
       }
     }
-  }
-  if (slice != 0) return;
-
+    if (write) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float lt = lsum[nb] + __shfl_xor(lsum[nb], 32, 64);
-    const int rho = rgrp * S::ROWS_G + nb * 32 + r32;
-    const int slot = rho / rows_per_branch;
-    if (slot >= nbr) continue;
-    const int within = rho - slot * rows_per_branch;
-    const int j = within / p.G;
-    const int hh = within - j * p.G;
-    const size_t b = size_t(ord[b0 + slot]);
-    const bool ok = p.branch_ok[tB + b] != 0;
-    const float inv = ok ? 1.0f / lt : __builtin_nanf("");
-    uint16_t* orow = p.out + ((((tB + b) * p.Wn + j) * p.Hq) + size_t(g) * p.G + hh) * D;
+      for (int nb = 0; nb < NB; ++nb) {
+        const float lt = lsum[nb] + __shfl_xor(lsum[nb], 32, 64);
+        const int rho = (wave * NB + nb) * 32 + r32;
+        const int slot = rho / rows_per_branch;
+        if (slot >= nbr) continue;
+        const int within = rho - slot * rows_per_branch;
+        const int j = within / p.G;
+        const int hh = within - j * p.G;
+        const size_t b = size_t(ord[b0 + slot]);
+        const bool ok = p.branch_ok[tB + b] != 0;
+        const float inv = ok ? 1.0f / lt : __builtin_nanf("");
+        uint16_t* orow = p.out + (tB * p.Wn * p.Hq + size_t(g) * p.G) * D +
+                         ((int(b) * p.Wn + j) * p.Hq + hh) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < OREG; ++db)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int dim = 32 * db + 8 * q + 4 * h;
-        const f32x16& o = oacc[nb][db];
-        u32x2 w = {pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
-                   pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + dim) = w;
+          for (int q = 0; q < 4; ++q) {
+            const int dim = 32 * db + 8 * q + 4 * h;
+            const f32x16& o = oacc[nb][db];
+            u32x2 w = {pack_bf16x2(o[4 * q] * inv, o[4 * q + 1] * inv),
+                       pack_bf16x2(o[4 * q + 2] * inv, o[4 * q + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + dim) = w;
+          }
       }
+    }
   }
-}
-
-template <int D, int NB, int KS>
-hipError_t launch_shape(const MfmaParams& p, hipStream_t s) {
-  tree_attn_mfma_kernel<D, NB, KS><<<8 * p.per, waves_for<D>() * 64, 0, s>>>(p);
-  return hipGetLastError();
 }
 
 }  // namespace
 
-int mfma_rows_per_wg(int D, int KS) {
-  const int NB = D == 64 ? 2 : 1;
-  const int nw = D == 256 ? waves_for<256>() : waves_for<128>();
-  return (nw / KS) * 32 * NB;
+size_t mfma_slot_bytes(int D) {
+  const int nw = mfma_waves(D), nb = mfma_row_blocks(D);
+  return align_up(size_t(nw) * nb * (D / 32) * 8 * 64 * 4 + size_t(nw) * nb * 128 * 4, 256);
 }
 
-hipError_t launch_tree_attn_mfma(int D, int KS, const MfmaParams& p, hipStream_t s) {
+hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s) {
   switch (D) {
-    case 64:
-      return KS == 1 ? launch_shape<64, 2, 1>(p, s)
-                     : KS == 2 ? launch_shape<64, 2, 2>(p, s) : launch_shape<64, 2, 4>(p, s);
-    case 128:
-      return KS == 1 ? launch_shape<128, 1, 1>(p, s)
-                     : KS == 2 ? launch_shape<128, 1, 2>(p, s) : launch_shape<128, 1, 4>(p, s);
-    case 256:
-      return KS == 1 ? launch_shape<256, 1, 1>(p, s) : launch_shape<256, 1, 2>(p, s);
+    case 64: tree_attn_mfma_kernel<64><<<p.nwg, mfma_waves(64) * 64, 0, s>>>(p); break;
+    case 128: tree_attn_mfma_kernel<128><<<p.nwg, mfma_waves(128) * 64, 0, s>>>(p); break;
+    case 256: tree_attn_mfma_kernel<256><<<p.nwg, mfma_waves(256) * 64, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace specopd
