@@ -94,7 +94,9 @@ struct PrepParams {
   float qmul;
 };
 
-constexpr int kSortLds = 2048;  // branches per trunk whose sort keys are staged in LDS
+constexpr int kSortLds = 2048;  // branches per trunk planned and sorted in LDS
+constexpr int kPlanLds = 8192;  // nodes per trunk whose parents are staged in LDS
+constexpr int kRopeNodes = 4;   // nodes per rotary pass of a workgroup
 
 __device__ void plan_branch(const PrepParams& p, size_t tb) {
   const int a = p.anchors[tb];
@@ -117,113 +119,204 @@ __device__ void plan_branch(const PrepParams& p, size_t tb) {
   p.branch_ok[tb] = ok ? 1 : 0;
 }
 
-// Key tiles of pack pk of trunk t: trunk tiles up to its longest anchor, then
-// tail tiles holding the pack's branch nodes.
-__device__ int pack_tiles(const PrepParams& p, int t, int pk) {
-  const size_t tB = size_t(t) * p.B;
-  const int b0 = pk * p.bpp;
-  const int nbr = min(p.bpp, p.B - b0);
-  const int bl = p.order[tB + b0];
-  const int a = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
-  return (a + 32) / 32 + (nbr * p.Wn + 31) / 32;
-}
-
 // One launch prepares everything the matrix-core kernel reads:
 //   workgroups [0, T): one trunk each -- validate its branches and record
 //     ancestor masks, order the branches by anchor (longest first, malformed
 //     last, ties by index; rank sort), tabulate the packs' key tiles as prefix
 //     sums, and clear the trunk's split-pack counters;
 //   the other workgroups: rotary embedding of branch queries (times qmul) and
-//     keys, one thread per (node, four consecutive pairs), angles in fp64.
+//     keys, a few nodes at a time, angles in fp64.
 __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
   const int tid = threadIdx.x;
   if (int(blockIdx.x) < p.T) {
     const int t = blockIdx.x;
     const size_t tB = size_t(t) * p.B;
-    __shared__ int keys[kSortLds];
-    for (int b = tid; b < p.B; b += 256) plan_branch(p, tB + b);
-    __syncthreads();
-    const bool in_lds = p.B <= kSortLds;
-    if (in_lds)
-      for (int b = tid; b < p.B; b += 256) keys[b] = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
-    __syncthreads();
-    for (int b = tid; b < p.B; b += 256) {
-      const int kb = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
-      int rank = 0;
-      for (int o = 0; o < p.B; ++o) {
-        const int ko = in_lds ? keys[o] : (p.branch_ok[tB + o] ? p.anchors[tB + o] : -1);
-        rank += (ko > kb) || (ko == kb && o < b);
+    const int B = p.B, Wn = p.Wn;
+    __shared__ int8_t s_par[kPlanLds];  // parent of every node of the trunk
+    __shared__ __attribute__((aligned(16))) int s_key[kSortLds + 4];  // anchor, then sort key (-1: malformed)
+    __shared__ int s_bad[kSortLds];
+    __shared__ int s_ord[kSortLds];
+    __shared__ int run[256];
+    const int nodes = B * Wn;
+    const bool staged = B <= kSortLds && nodes <= kPlanLds;
+    if (staged) {
+      for (int b = tid; b < B; b += 256) {
+        s_key[b] = p.anchors[tB + b];
+        s_bad[b] = 0;
       }
-      p.order[tB + rank] = b;
+      for (int i = tid; i < nodes; i += 256) {
+        const int pj = p.parent[tB * Wn + i];
+        s_par[i] = int8_t((pj >= -1 && pj < 64) ? pj : -2);  // -2: invalid
+      }
+      __syncthreads();
+      // one thread per node: walk the parent chain (each step must go to an
+      // earlier node, so the walk ends); the visited nodes are the node's
+      // ancestor mask, their count fixes the depth
+      for (int i = tid; i < nodes; i += 256) {
+        const int b = i / Wn, j = i - b * Wn;
+        uint64_t m = 0;
+        bool ok = true;
+        for (int k = j;;) {
+          m |= uint64_t(1) << k;
+          const int pk = s_par[b * Wn + k];
+          if (pk == -1) break;
+          if (pk < 0 || pk >= k) {
+            ok = false;
+            break;
+          }
+          k = pk;
+        }
+        const int depth = __popcll(m) - 1;
+        if (p.pos[tB * Wn + i] != s_key[b] + 1 + depth) ok = false;
+        p.anc[tB * Wn + i] = m;
+        if (!ok) s_bad[b] = 1;
+      }
+      __syncthreads();
+      for (int b = tid; b < B; b += 256) {
+        const int a = s_key[b];
+        const bool ok = !s_bad[b] && a >= 0 && a < p.L;
+        p.branch_ok[tB + b] = ok ? 1 : 0;
+        s_key[b] = ok ? a : -1;
+      }
+      __syncthreads();
+      // rank sort; keys are read four at a time (s_key is padded with keys
+      // that rank below every branch)
+      for (int b = B + tid; b < ((B + 3) & ~3); b += 256) s_key[b] = -2;
+      __syncthreads();
+      for (int b = tid; b < B; b += 256) {
+        const int kb = s_key[b];
+        int rank = 0;
+#pragma unroll 4
+        for (int o = 0; o < B; o += 4) {
+          const int4 ko = *reinterpret_cast<const int4*>(s_key + o);
+          rank += (ko.x > kb) || (ko.x == kb && o < b);
+          rank += (ko.y > kb) || (ko.y == kb && o + 1 < b);
+          rank += (ko.z > kb) || (ko.z == kb && o + 2 < b);
+          rank += (ko.w > kb) || (ko.w == kb && o + 3 < b);
+        }
+        s_ord[rank] = b;
+        p.order[tB + rank] = b;
+      }
+      __syncthreads();
+    } else {
+      for (int b = tid; b < B; b += 256) plan_branch(p, tB + b);
+      __syncthreads();
+      for (int b = tid; b < B; b += 256) {
+        const int kb = p.branch_ok[tB + b] ? p.anchors[tB + b] : -1;
+        int rank = 0;
+        for (int o = 0; o < B; ++o) {
+          const int ko = p.branch_ok[tB + o] ? p.anchors[tB + o] : -1;
+          rank += (ko > kb) || (ko == kb && o < b);
+        }
+        p.order[tB + rank] = b;
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    // key tiles of pack pk: trunk tiles up to its longest anchor, then tail
+    // tiles holding the pack's branch nodes
+    auto tiles = [&](int pk) {
+      const int b0 = pk * p.bpp;
+      const int nbr = min(p.bpp, B - b0);
+      int a;
+      if (staged) {
+        a = s_key[s_ord[b0]];
+      } else {
+        const int bl = p.order[tB + b0];
+        a = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
+      }
+      return (a + 32) / 32 + (nbr * Wn + 31) / 32;
+    };
     // exclusive prefix sums of the packs' tiles: per-thread runs, then a scan
     // of the 256 run totals
-    __shared__ int run[256];
     const int np = p.npacks;
     const int per = (np + 255) / 256;
     const int lo = min(tid * per, np), hi = min(lo + per, np);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += pack_tiles(p, t, i);
+    for (int i = lo; i < hi; ++i) sum += tiles(i);
     run[tid] = sum;
     __syncthreads();
     int32_t* ps = p.pstart + size_t(t) * (np + 1);
-    if (tid == 0) {
-      int acc = 0;
-      for (int i = 0; i < 256; ++i) {
-        const int x = run[i];
-        run[i] = acc;
-        acc += x;
+    {
+      // exclusive scan of the 256 run totals: within each wave by shuffles,
+      // then across the four waves
+      const int lane = tid & 63, w = tid >> 6;
+      int x = run[tid];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
       }
-      ps[np] = acc;
+      __shared__ int wsum[4];
+      if (lane == 63) wsum[w] = x;
+      __syncthreads();
+      int base = 0;
+      for (int i = 0; i < w; ++i) base += wsum[i];
+      const int excl = base + x - run[tid];
+      __syncthreads();
+      run[tid] = excl;
+      if (tid == 255) ps[np] = base + x;
     }
     __syncthreads();
     int acc = run[tid];
     for (int i = lo; i < hi; ++i) {
       ps[i] = acc;
-      acc += pack_tiles(p, t, i);
+      acc += tiles(i);
     }
     int32_t* c = p.ctr + size_t(t) * p.Hkv * np;
     for (int i = tid; i < p.Hkv * np; i += 256) c[i] = 0;
     return;
   }
-  const int quads = p.D / 8;  // four pairs (i, i + D/2) per thread
+  // rotary: kRopeNodes nodes per workgroup pass.  Frequencies are tabulated
+  // once per workgroup (fp64); an angle is formed and reduced modulo 2 pi in
+  // fp64 (positions reach tens of thousands of radians) and its sine and
+  // cosine taken in fp32 on the reduced argument.  The workgroup's threads
+  // then take (node, head, eight pairs) units of all query and key heads.
+  __shared__ double s_theta[128];            // D/2 <= 128
+  __shared__ float2 s_cs[kRopeNodes * 128];  // (cos, sin)
   const int half = p.D / 2;
-  const size_t total = size_t(p.T) * p.B * p.Wn * quads;
-  const size_t stride = size_t(gridDim.x - p.T) * 256;
-  for (size_t idx = size_t(blockIdx.x - p.T) * 256 + tid; idx < total; idx += stride) {
-    const size_t node = idx / quads;
-    const int i0 = int(idx - node * quads) * 4;
-    const double ps = double(p.pos[node]);
-    float c[4], sn[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const double theta = exp2(-(2.0 * (i0 + e) / p.D) * p.log2_base);
-      double sd, cd;
-      sincos(ps * theta, &sd, &cd);
-      c[e] = float(cd);
-      sn[e] = float(sd);
+  const int octs = p.D / 16;
+  const int H = p.Hq + p.Hkv;
+  const size_t nodes = size_t(p.T) * p.B * p.Wn;
+  if (tid < half) s_theta[tid] = exp2(-(2.0 * tid / p.D) * p.log2_base);
+  for (size_t n0 = size_t(blockIdx.x - p.T) * kRopeNodes; n0 < nodes;
+       n0 += size_t(gridDim.x - p.T) * kRopeNodes) {
+    const int nn = int(min(size_t(kRopeNodes), nodes - n0));
+    __syncthreads();  // the previous pass's angles are no longer read
+    for (int idx = tid; idx < nn * half; idx += 256) {
+      const int ln = idx / half, i = idx - ln * half;
+      const double ang = double(p.pos[n0 + ln]) * s_theta[i];
+      const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+      const float r = float(fma(-k, 6.283185307179586, ang));
+      float sn, cs;
+      sincosf(r, &sn, &cs);
+      s_cs[idx] = make_float2(cs, sn);
     }
-    auto rotate = [&](const uint16_t* src, uint16_t* dst, int H, float mul) {
-      for (int hd = 0; hd < H; ++hd) {
-        const size_t off = (node * H + hd) * p.D + i0;
-        const u32x2 a = *reinterpret_cast<const u32x2*>(src + off);
-        const u32x2 b = *reinterpret_cast<const u32x2*>(src + off + half);
-        const float x1[4] = {bf16_lo(a[0]), bf16_hi(a[0]), bf16_lo(a[1]), bf16_hi(a[1])};
-        const float x2[4] = {bf16_lo(b[0]), bf16_hi(b[0]), bf16_lo(b[1]), bf16_hi(b[1])};
-        float y1[4], y2[4];
+    __syncthreads();
+    for (int u = tid; u < nn * H * octs; u += 256) {
+      const int lnh = u / octs;
+      const int i0 = (u - lnh * octs) * 8;
+      const int ln = lnh / H, hd = lnh - ln * H;
+      const size_t node = n0 + ln;
+      const bool isq = hd < p.Hq;
+      const uint16_t* __restrict__ src =
+          isq ? p.q + (node * p.Hq + hd) * p.D : p.k + (node * p.Hkv + (hd - p.Hq)) * p.D;
+      uint16_t* __restrict__ dst =
+          isq ? p.qr + (node * p.Hq + hd) * p.D : p.kr + (node * p.Hkv + (hd - p.Hq)) * p.D;
+      const float mul = isq ? p.qmul : 1.0f;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(src + i0);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(src + i0 + half);
+      u32x4 ya, yb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y1[e] = (x1[e] * c[e] - x2[e] * sn[e]) * mul;
-          y2[e] = (x2[e] * c[e] + x1[e] * sn[e]) * mul;
-        }
-        *reinterpret_cast<u32x2*>(dst + off) = u32x2{pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3])};
-        *reinterpret_cast<u32x2*>(dst + off + half) =
-            u32x2{pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3])};
+      for (int e = 0; e < 4; ++e) {
+        const float2 c0 = s_cs[ln * half + i0 + 2 * e], c1 = s_cs[ln * half + i0 + 2 * e + 1];
+        const float x10 = bf16_lo(a[e]), x11 = bf16_hi(a[e]);
+        const float x20 = bf16_lo(b[e]), x21 = bf16_hi(b[e]);
+        ya[e] = pack_bf16x2((x10 * c0.x - x20 * c0.y) * mul, (x11 * c1.x - x21 * c1.y) * mul);
+        yb[e] = pack_bf16x2((x20 * c0.x + x10 * c0.y) * mul, (x21 * c1.x + x11 * c1.y) * mul);
       }
-    };
-    rotate(p.q, p.qr, p.Hq, p.qmul);
-    rotate(p.k, p.kr, p.Hkv, 1.0f);
+      *reinterpret_cast<u32x4*>(dst + i0) = ya;
+      *reinterpret_cast<u32x4*>(dst + i0 + half) = yb;
+    }
   }
 }
 
@@ -408,8 +501,7 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     pp.bpp = bpp; pp.npacks = np;
     pp.log2_base = log2(double(a.rope_base));
     pp.qmul = a.scale * kLog2e;
-    const size_t rope_threads = size_t(nodes) * (d.D / 8);
-    const unsigned rope_blocks = unsigned(std::min<size_t>((rope_threads + 255) / 256, 8192));
+    const unsigned rope_blocks = unsigned(std::min<size_t>((size_t(nodes) + kRopeNodes - 1) / kRopeNodes, 16384));
     tree_prep_kernel<<<unsigned(d.T) + rope_blocks, 256, 0, s>>>(pp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     MfmaParams p{};
