@@ -45,9 +45,10 @@
 // per tile.  Lanes whose 16 bytes land on a row's pad chunk load a harmless
 // in-bounds chunk that is never read.
 //
-// Softmax is online in log2 units against a per-row reference maximum m that
+// Softmax is online in log2 units.  The score product starts from -m (m the
+// row's reference maximum), so scores arrive already shifted; the reference
 // moves only when a score exceeds it by more than 2^8, so the common tile
-// costs no rescale of the accumulators.
+// costs no rescale.
 #include "device_common.h"
 #include "internal.h"
 
@@ -140,10 +141,12 @@ __device__ __forceinline__ void post_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// Raw scores (log2 units) of a staged K tile against this wave's queries.
+// Scores (log2 units) of a staged K tile against this wave's queries, shifted
+// by -m (the product starts from cinit = -m).
 template <int D>
 __device__ __forceinline__ void tile_scores(const char* kl,
                                             const bf16x8 (&qop)[Geo<D>::NB][D / 16],
+                                            const f32x16 (&cinit)[Geo<D>::NB],
                                             f32x16 (&S)[Geo<D>::NB]) {
   constexpr int NB = Geo<D>::NB;
 #pragma unroll
@@ -151,8 +154,7 @@ __device__ __forceinline__ void tile_scores(const char* kl,
     const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kl + 32 * s2);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      S[nb] = s2 == 0 ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s2], f32x16{}, 0, 0, 0)
-                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s2], S[nb], 0, 0, 0);
+      S[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[nb][s2], s2 == 0 ? cinit[nb] : S[nb], 0, 0, 0);
   }
 }
 
@@ -181,16 +183,16 @@ __device__ __forceinline__ void tile_pv(const char* __restrict__ vl,
 
 // Probabilities of one tile (bf16, as the V product uses them) and their sum.
 template <int D>
-__device__ __forceinline__ void tile_probs(const f32x16 (&S)[Geo<D>::NB], const float (&mref)[Geo<D>::NB],
-                                           float (&lsum)[Geo<D>::NB], bf16x8 (&P)[Geo<D>::NB][2]) {
+__device__ __forceinline__ void tile_probs(const f32x16 (&S)[Geo<D>::NB], float (&lsum)[Geo<D>::NB],
+                                           bf16x8 (&P)[Geo<D>::NB][2]) {
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
   for (int nb = 0; nb < Geo<D>::NB; ++nb) {
     float acc = lsum[nb];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
-      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(S[nb][i] - mref[nb])),
-                         static_cast<__bf16>(fast_exp2(S[nb][i + 1] - mref[nb]))};
+      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(S[nb][i])),
+                         static_cast<__bf16>(fast_exp2(S[nb][i + 1]))};
       P[nb][i >> 3][i & 7] = e2[0];
       P[nb][i >> 3][(i & 7) + 1] = e2[1];
       acc = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc, false);  // sums the bf16 weights used below
@@ -208,9 +210,18 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
                                          int wave, const uint16_t* tk, const uint16_t* tv,
                                          const uint16_t* bk, const uint16_t* bv,
                                          const int32_t* pord, char* lb,
-                                         const int (&dcode)[Geo<D>::JPW]) {
+                                         const int (&dcode)[Geo<D>::JPW],
+                                         const uint16_t* const* qsrc) {
   using Gm = Geo<D>;
   const bool trunk = v < ntrunk;
+  if (trunk && (v + 1) * KT <= Lk) {  // whole trunk tile: one add per load
+    const size_t step = size_t(v) * KT * kvrow;
+#pragma unroll
+    for (int q = 0; q < Gm::JPW; ++q)
+      __builtin_amdgcn_global_load_lds(qsrc[q] + step, (__attribute__((address_space(3))) void*)(
+                                                           lb + (wave + Gm::NW * q) * 1024), 16, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < Gm::JPW; ++q) {
     const int code = dcode[q];
@@ -245,15 +256,17 @@ __device__ __forceinline__ void tile_step(char* dbuf, const char* kbuf,
                                           const uint16_t* tk, const uint16_t* tv, const uint16_t* bk,
                                           const uint16_t* bv, const int32_t* pord,
                                           const int (&dcode)[Geo<D>::JPW],
+                                          const uint16_t* const* qsrc,
                                           const bf16x8 (&qop)[Geo<D>::NB][D / 16],
+                                          const f32x16 (&cinit)[Geo<D>::NB],
                                           const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
-                                          const float (&mref)[Geo<D>::NB], float (&lsum)[Geo<D>::NB],
+                                          float (&lsum)[Geo<D>::NB],
                                           f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
   if (load)
-    dma_tile<D>(vload, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, pord, dbuf, dcode);
-  tile_scores<D>(kbuf, qop, Snext);
+    dma_tile<D>(vload, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, pord, dbuf, dcode, qsrc);
+  tile_scores<D>(kbuf, qop, cinit, Snext);
   bf16x8 P[Geo<D>::NB][2];
-  tile_probs<D>(Scur, mref, lsum, P);
+  tile_probs<D>(Scur, lsum, P);
   tile_pv<D>(vbuf, P, oacc);
 }
 
@@ -355,6 +368,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     const uint16_t* bk = p.kr + (tB * p.Wn * p.Hkv + g) * D;
     const uint16_t* bv = p.v + (tB * p.Wn * p.Hkv + g) * D;
     const int kvrow = p.Hkv * D;  // elements between consecutive keys
+    // this lane's source of each of its tile loads for trunk tile 0
+    const uint16_t* qsrc[Gm::JPW];
+#pragma unroll
+    for (int q = 0; q < Gm::JPW; ++q) {
+      const int code = dcode[q];
+      qsrc[q] = (((code >> 12) & 1) ? tv : tk) + (code & 31) * kvrow + ((code >> 5) & 127) * 8;
+    }
 
     // ---- this lane's rows: metadata and the Q^T operand
     int ra[NB], rslot[NB];
@@ -388,18 +408,20 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     const int wave_amin = __builtin_amdgcn_readfirstlane(wmin);
 
     // ---- tile loads: global -> LDS buffer b
-#define DMA_TILE(v, b) dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode)
+#define DMA_TILE(v, b) \
+  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
     const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
     const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
 
     // ---- running state
-    f32x16 oacc[NB][OREG];
+    f32x16 oacc[NB][OREG], cinit[NB];
     float mref[NB], lim[NB], lsum[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       mref[nb] = 0.f;
       lim[nb] = kUnset;
       lsum[nb] = 0.f;
+      cinit[nb] = f32x16{};
 #pragma unroll
       for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
     }
@@ -444,17 +466,24 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       if (__any(any)) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const float m = fmaxf(mx[nb], __shfl_xor(mx[nb], 32, 64));  // whole row
+          const float m = fmaxf(mx[nb], __shfl_xor(mx[nb], 32, 64));  // whole row, relative to mref
           const bool nd = m > lim[nb];
-          const float f = (nd && lim[nb] != kUnset) ? fast_exp2(mref[nb] - m) : 1.0f;
+          const float delta = nd ? m : 0.f;
+          const float f = (nd && lim[nb] != kUnset) ? fast_exp2(-delta) : 1.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) S[nb][i] -= delta;
           lsum[nb] *= f;
 #pragma unroll
           for (int db = 0; db < OREG; ++db) oacc[nb][db] *= f;
-          mref[nb] = nd ? m : mref[nb];
-          lim[nb] = nd ? m + kRescale : lim[nb];
+          mref[nb] += delta;
+          lim[nb] = nd ? kRescale : lim[nb];
+          const float c = -mref[nb];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) cinit[nb][i] = c;
         }
       }
     };
+
     // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight
     DMA_TILE(v0, 0);
     if (n > 1) DMA_TILE(v0 + 1, 1);
@@ -463,7 +492,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     lds_barrier();
 
     f32x16 Sa[NB], Sb[NB];
-    tile_scores<D>(smem + koff, qop, Sa);
+    tile_scores<D>(smem + koff, qop, cinit, Sa);
     mask(v0, Sa);
     settle(Sa);
 
@@ -475,7 +504,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       // block straight)
       tile_step<D>(smem + ((i + 3) & 3) * Gm::BUFB, smem + ((i + 1) & 3) * Gm::BUFB + koff,
                    smem + (i & 3) * Gm::BUFB + voff, i + 3 < n, v0 + i + 3, ntrunk, nt_total, Lk, kvrow,
-                   Wn, wave, tk, tv, bk, bv, ord + b0, dcode, qop, Sa, Sb, mref, lsum, oacc);
+                   Wn, wave, tk, tv, bk, bv, ord + b0, dcode, qsrc, qop, cinit, Sa, Sb, lsum, oacc);
       if (more) {
         mask(v0 + i + 1, Sb);
         settle(Sb);
