@@ -19,8 +19,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   order      int32  [T*B]      branches of each trunk by anchor, longest first
 //   rot        rotated branch queries and keys
 //   pstart     int32  [T][npacks+1]  first key tile of each pack (prefix sums)
-//   ctr        int32  [T][Hkv][npacks]  segments of a split pack that finished
-//   part       partial results, two slots per workgroup of the matrix-core grid
+//   ctr        int32  [T][Hkv][npacks]  splits of a pack that finished
+//   part       partial results, one slot per (pack, split) when packs are split
 struct TreeAttnWs {
   size_t anc, branch_ok, order, rot, pstart, ctr, part, total;
 };
@@ -43,8 +43,14 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
 constexpr int mfma_waves(int D) { return D == 256 ? 4 : 8; }
 constexpr int mfma_row_blocks(int) { return 1; }
 constexpr int mfma_rows_per_wg(int D) { return mfma_waves(D) * 32 * mfma_row_blocks(D); }
-constexpr int kMfmaGrid = 256;  // workgroups of the matrix-core launch (one per CU)
 size_t mfma_slot_bytes(int D);
+// Key-range splits per pack: packs are split only when there are too few of
+// them to give every CU a couple of workgroups.
+inline int mfma_nsplit(long long units) {
+  if (units >= 512) return 1;
+  const long long s = (512 + units - 1) / units;
+  return int(s < 16 ? s : 16);
+}
 
 struct MfmaParams {
   const uint16_t *trunk_k, *trunk_v;  // [T][L][Hkv][D]
@@ -57,13 +63,16 @@ struct MfmaParams {
   const int32_t* order;               // [T][B] branches by anchor, longest first
   const int32_t* pstart;              // [T][npacks+1]
   int32_t* ctr;                       // [T][Hkv][npacks], zero on entry
-  char* part;                         // 2 * nwg slots of slot_bytes
+  char* part;                         // nunits slots of slot_bytes (nsplit > 1)
   size_t slot_bytes;
   uint16_t* out;                      // [T][B][Wn][Hq][D]
   int T, B, L, Wn, Hq, Hkv, G;
   int bpp;     // branches per pack
   int npacks;  // packs per trunk
-  int nwg;     // workgroups (multiple of 8, at most kMfmaGrid)
+  int nsplit;  // key-range splits per pack
+  int nunits;  // T * Hkv * npacks * nsplit
+  int nwg;     // workgroups: nunits rounded up to a multiple of 8
+  int ilv;     // XCD blocks a kv head's units are dealt across (1: none)
 };
 hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s);
 

@@ -438,7 +438,9 @@ TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * esz, 256);
   w.pstart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
   w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
-  w.part = off;       off = align_up(off + (mf ? 2 * size_t(kMfmaGrid) * mfma_slot_bytes(d.D) : 0), 256);
+  const long long units = mf ? (long long)d.T * d.Hkv * np : 0;
+  const int nsplit = mf ? mfma_nsplit(units) : 1;
+  w.part = off;       off = align_up(off + (nsplit > 1 ? size_t(units) * nsplit * mfma_slot_bytes(d.D) : 0), 256);
   w.total = off;
   return w;
 }
@@ -522,7 +524,11 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.T = d.T; p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
     p.bpp = bpp;
     p.npacks = np;
-    p.nwg = kMfmaGrid;
+    p.nsplit = mfma_nsplit((long long)d.T * d.Hkv * np);
+    p.nunits = d.T * d.Hkv * np * p.nsplit;
+    p.nwg = (p.nunits + 7) / 8 * 8;
+    const int per = p.nwg / 8, ug = np * p.nsplit;
+    p.ilv = (ug % per == 0 && ug / per >= 2) ? ug / per : 1;
     return launch_tree_attn_mfma(d.D, p, s);
   }
   tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);

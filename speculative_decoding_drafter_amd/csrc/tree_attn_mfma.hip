@@ -16,14 +16,14 @@
 // tiles masked by the ancestor bitmask and by branch identity.  A pack's key
 // tiles (trunk tiles, then tail tiles) are its units of work.
 //
-// Work split (stream-K).  The units of all (trunk, kv head, pack) triples are
-// laid end to end and a fixed grid cuts the line into equal ranges, one per
-// workgroup, so every compute unit gets the same number of key tiles whatever
-// the anchors are.  A pack cut between workgroups leaves partial results
-// (unnormalised output in bf16, running max and sum in fp32) in the
-// workspace; the workgroup that finishes last merges them in segment order,
-// so the result does not depend on timing.  Consecutive ranges go to the
-// same XCD, so workgroups that read the same trunk rows share an L2.
+// Work split.  A workgroup takes one pack, or one of `nsplit` key ranges of a
+// pack when there are too few packs to fill the chip.  A split pack leaves
+// partial results (unnormalised output in bf16, running max and sum in fp32)
+// in the workspace; the workgroup that finishes last merges them in split
+// order, so the result does not depend on timing.  Packs of one kv head are
+// consecutive units and run side by side on one XCD, reading the same trunk
+// tiles at about the same time, so the trunk is fetched into that XCD's L2
+// about once.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, lane l = r + 32h):
 //   S^T[key][row] = K[key][:] . Q[row][:]      A = K tile (LDS, 16-byte
@@ -94,15 +94,6 @@ __device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int Wn, 
   if (anc == 0 || base >= KT || base <= -64) return 0u;
   const uint64_t w = base >= 0 ? (anc << base) : (anc >> (-base));
   return uint32_t(w);
-}
-
-// Workgroup holding line position x when the line of W units is cut into
-// nwg ranges [floor(w W / nwg), floor((w+1) W / nwg)).
-__device__ __forceinline__ int range_owner(long long x, long long W, int nwg) {
-  return int(((x + 1) * nwg - 1) / W);
-}
-__device__ __forceinline__ long long range_begin(int w, long long W, int nwg) {
-  return (long long)w * W / nwg;
 }
 
 // Wait until at most n of this wave's vector-memory operations are in flight
@@ -286,17 +277,32 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   const int gi = lane >> 4, rq = lane & 15;
   const int nwg = gridDim.x;
 
-  // XCD-aware range order: workgroups are dealt to the 8 XCDs round robin, so
-  // workgroup u below takes a range next to those of the other workgroups on
-  // its XCD.
-  const int u = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int np = p.npacks;
-  const int psz = np + 1;
-
-  long long W = 0;
-  for (int t = 0; t < p.T; ++t) W += (long long)p.Hkv * p.pstart[size_t(t) * psz + np];
-  const long long s0 = range_begin(u, W, nwg), s1 = range_begin(u + 1, W, nwg);
-  if (s0 >= s1) return;
+  // Work unit u = ((t * Hkv + g) * npacks + pack) * nsplit + split.  Units are
+  // dealt to the XCDs in consecutive blocks (workgroups go to the 8 XCDs round
+  // robin), so the packs of one kv head run side by side on one XCD and stream
+  // the same trunk rows through its L2.  When a kv head's units fill `ilv`
+  // XCD blocks, its packs are dealt to those blocks alternately, so that each
+  // XCD gets a like share of long and short packs.
+  const int ub = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  if (ub >= p.nunits) return;
+  const int np = p.npacks, S = p.nsplit;
+  const int ug = np * S;                   // units per (trunk, kv head)
+  const int tg = ub / ug;
+  int jj = ub - tg * ug;
+  if (p.ilv > 1) {
+    const int c = ug / p.ilv;
+    jj = (jj % c) * p.ilv + jj / c;
+  }
+  const int pk = jj / S, rsp = jj - pk * S;
+  const int upk = tg * np + pk;
+  const int g = tg % p.Hkv, t = tg / p.Hkv;
+  const int* ps = p.pstart + size_t(t) * (np + 1);
+  const int nvt = ps[pk + 1] - ps[pk];
+  // split rsp takes the pack's key tiles [rsp * nvt / S, (rsp + 1) * nvt / S)
+  auto split_begin = [=](int r2) __attribute__((always_inline)) { return int((long long)r2 * nvt / S); };
+  const int v0 = split_begin(rsp);
+  const int n = split_begin(rsp + 1) - v0;
+  if (n == 0) return;  // pack shorter than its split count
 
   const int rows_per_branch = p.Wn * p.G;
   // scalars the helper lambdas use, copied so that no lambda takes the
@@ -327,31 +333,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     dcode[q] = key | (c << 5) | (isv << 12);
   }
 
-  long long s = s0, base = 0;
-  int t = 0;
-  while (s < s1) {
-    const int* ps = p.pstart + size_t(t) * psz;
-    const int Wt = ps[np];
-    const long long rel = s - base;
-    if (rel >= (long long)p.Hkv * Wt) {
-      base += (long long)p.Hkv * Wt;
-      ++t;
-      continue;
-    }
-    const int g = int(rel / Wt);
-    const int r = int(rel - (long long)g * Wt);
-    int lo = 0, hi = np;  // largest pack whose first unit is <= r
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ps[mid] <= r) lo = mid; else hi = mid;
-    }
-    const int pk = lo;
-    const int v0 = r - ps[pk];
-    const int nvt = ps[pk + 1] - ps[pk];
-    const int n = int(min((long long)(nvt - v0), s1 - s));
-    const long long pack_start = base + (long long)g * Wt + ps[pk];
-    s += n;
-
+  {
     // ---- pack geometry
     const size_t tB = size_t(t) * p.B;
     const int32_t* ord = p.order + tB;
@@ -517,28 +499,17 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 
 #undef DMA_TILE
 
-    // ---- finish the pack (or this workgroup's segment of it)
-    const bool whole = (v0 == 0) && (n == nvt);
+    // ---- finish the pack (or this split of it)
+    const int nseg = min(S, nvt);  // non-empty splits of the pack
+    const bool whole = nseg == 1;
     bool write = whole;
     if (!whole) {
-      // segment bookkeeping
-      const long long pend = pack_start + nvt;
-      // workgroups whose (non-empty) ranges cut this pack; with fewer units
-      // than workgroups some ranges in between are empty
-      const int wfirst = range_owner(pack_start, W, nwg);
-      const int wlast = range_owner(pend - 1, W, nwg);
-      auto nonempty = [=](int w) __attribute__((always_inline)) {
-        return range_begin(w + 1, W, nwg) > range_begin(w, W, nwg);
-      };
-      int nseg = 0;
-      for (int w = wfirst; w <= wlast; ++w) nseg += nonempty(w);
-      const size_t ctr_i = (size_t(t) * p.Hkv + g) * np + pk;
-      auto slot_of = [=](int w) __attribute__((always_inline)) -> char* {
-        const int side = (w == wfirst && range_begin(w, W, nwg) < pack_start) ? 1 : 0;
-        return part + size_t(2 * w + side) * slot_bytes;
+      const size_t ctr_i = upk;  // one counter per (trunk, kv head, pack)
+      auto slot_of = [=](int r2) __attribute__((always_inline)) -> char* {
+        return part + (size_t(upk) * S + r2) * slot_bytes;
       };
       constexpr int OWORDS = NB * OREG * 8;  // bf16 pairs per lane
-      char* mine = slot_of(u);
+      char* mine = slot_of(rsp);
       uint32_t* po = reinterpret_cast<uint32_t*>(mine) + wave * OWORDS * 64 + lane;
       float* pm = reinterpret_cast<float*>(mine + Gm::NW * OWORDS * 64 * 4) + wave * NB * 128 + lane;
 #pragma unroll
@@ -572,9 +543,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 #pragma unroll
           for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
         }
-        for (int w = wfirst; w <= wlast; ++w) {
-          if (!nonempty(w)) continue;
-          const char* sl = slot_of(w);
+        for (int r2 = 0; r2 < S; ++r2) {
+          if (split_begin(r2 + 1) == split_begin(r2)) continue;
+          const char* sl = slot_of(r2);
           const uint32_t* qo = reinterpret_cast<const uint32_t*>(sl) + wave * OWORDS * 64 + lane;
           const float* qm = reinterpret_cast<const float*>(sl + Gm::NW * OWORDS * 64 * 4) +
                             wave * NB * 128 + lane;
