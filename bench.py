@@ -220,7 +220,9 @@ def main():
     loss_gbs = lb / (loss_ms / 1e3) / 1e9
     t_loss = measured_traffic(f"e2etv_fused_{wl.name}",
                               ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
-                               "speculative_decoding_drafter_amd/csrc/device_common.h"])
+                               "speculative_decoding_drafter_amd/csrc/device_common.h",
+                               "speculative_decoding_drafter_amd/csrc/internal.h",
+                               "speculative_decoding_drafter_amd/build.py"])
     roof_loss = {"bound": "hbm", "achieved": loss_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": loss_gbs / HBM_PEAK_GBS,
                  "traffic": None if t_loss is None else t_loss / (loss_ms / 1e3) / 1e9,
@@ -237,7 +239,9 @@ def main():
         peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
         t_attn = measured_traffic(f"tree_attn_mfma_{wl.name}",
                                   ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
-                                   "speculative_decoding_drafter_amd/csrc/device_common.h"])
+                                   "speculative_decoding_drafter_amd/csrc/device_common.h",
+                               "speculative_decoding_drafter_amd/csrc/internal.h",
+                               "speculative_decoding_drafter_amd/build.py"])
         roofs["attn"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
                          "frac": tf / peak,
                          "traffic": None if t_attn is None else t_attn / (attn_ms / 1e3) / 1e9,
