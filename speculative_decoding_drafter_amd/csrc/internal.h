@@ -36,12 +36,14 @@ struct TreeAttnArgs {
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
 
 // Matrix-core path (tree_attn_mfma.hip).  bf16 tensors are passed as uint16_t.
-// Waves per workgroup: 8 (two per SIMD) where a wave's accumulators and
-// query operand fit in 256 registers, 4 (one per SIMD, 512 registers) for
-// head size 256.  A wave owns one block of 32 rows (the kernel is written for
-// several blocks per wave, which more registers would allow).
-constexpr int mfma_waves(int D) { return D == 256 ? 4 : 8; }
-constexpr int mfma_row_blocks(int) { return 1; }
+// Four waves per workgroup, one per SIMD, so that a wave may hold 512
+// registers.  A wave owns two blocks of 32 rows for head sizes 64 and 128:
+// each K and V operand read from LDS then feeds two matrix products, which
+// halves the LDS traffic per flop (with one block per wave, LDS bandwidth
+// and not the matrix cores sets the pace).  Head size 256 keeps one block:
+// two would not fit the registers.
+constexpr int mfma_waves(int) { return 4; }
+constexpr int mfma_row_blocks(int D) { return D == 256 ? 1 : 2; }
 constexpr int mfma_rows_per_wg(int D) { return mfma_waves(D) * 32 * mfma_row_blocks(D); }
 size_t mfma_slot_bytes(int D);
 // Key-range splits per pack: packs are split only when there are too few of

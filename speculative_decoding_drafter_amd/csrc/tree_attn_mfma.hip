@@ -37,13 +37,17 @@
 // LDS rows are padded (K by 16 bytes, V by 32) so that both read patterns hit
 // distinct banks of the 64-bank LDS.
 //
-// Pipeline per wave: while the exponentials of tile i are formed on the
-// vector ALU, the matrix core already computes the scores of tile i + 1; the
-// products with V of tile i follow.  Tiles go from global memory straight
-// into LDS (global_load_lds: each lane of a wave-wide load writes 16 bytes at
-// base + 16 * lane), three tiles ahead through four LDS buffers, one barrier
+// Pipeline per wave (four waves, one per SIMD, each owning 64 rows for head
+// sizes up to 128, so that every K and V operand read from LDS feeds two
+// products): the score product of tile i + 1 is issued step by step together
+// with the exponentials of tile i and the LDS reads of tile i's V operands;
+// the products with V of tile i follow, during which the K operands of tile
+// i + 2 are read.  Tiles go from global memory straight into LDS
+// (global_load_lds: each lane of a wave-wide load writes 16 bytes at base +
+// 16 * lane), through five LDS buffers (four for head size 256), one barrier
 // per tile.  Lanes whose 16 bytes land on a row's pad chunk load a harmless
-// in-bounds chunk that is never read.
+// in-bounds chunk that is never read.  Tiles that need no mask for any row
+// of the wave run through a branch-free copy of the step.
 //
 // Softmax is online in log2 units.  The score product starts from -m (m the
 // row's reference maximum), so scores arrive already shifted; the reference
@@ -58,6 +62,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
 namespace {
 
@@ -78,7 +83,10 @@ struct Geo {
   static constexpr int NJ = (KBYTES + KT * VROW + 1023) / 1024;  // 1 KB writes a tile needs
   static constexpr int JPW = (NJ + NW - 1) / NW; // wave writes per tile (every wave the same)
   static constexpr int BUFB = JPW * NW * 1024;   // bytes of one staged K+V tile, with slack
-  static constexpr int NBUF = 4;
+  // staged tiles: five where they fit in LDS (the K operands of a tile can
+  // then be read one tile early), else four
+  static constexpr int NBUF = (5 * BUFB + 16 <= 160 * 1024) ? 5 : 4;
+  static constexpr bool EARLYK = NBUF == 5;
 };
 
 __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
@@ -192,6 +200,19 @@ __device__ __forceinline__ void tile_probs(const f32x16 (&S)[Geo<D>::NB], float 
   }
 }
 
+// Loads whole trunk tile v (every key < L) into LDS buffer lb: one add per
+// load from this lane's tile-0 source.
+template <int D>
+__device__ __forceinline__ void dma_whole(int v, int kvrow, int wave, char* lb,
+                                          const uint16_t* const* qsrc) {
+  using Gm = Geo<D>;
+  const size_t step = size_t(v) * KT * kvrow;
+#pragma unroll
+  for (int q = 0; q < Gm::JPW; ++q)
+    __builtin_amdgcn_global_load_lds(qsrc[q] + step, (__attribute__((address_space(3))) void*)(
+                                                         lb + (wave + Gm::NW * q) * 1024), 16, 0, 0);
+}
+
 // Loads key tile v (trunk tile, or tail tile of branch nodes) of the current
 // pack into LDS buffer b: this wave's share of the wave-wide 1 KB writes.
 // A plain function rather than a lambda: a lambda's closure here stays in
@@ -205,12 +226,8 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
                                          const uint16_t* const* qsrc) {
   using Gm = Geo<D>;
   const bool trunk = v < ntrunk;
-  if (trunk && (v + 1) * KT <= Lk) {  // whole trunk tile: one add per load
-    const size_t step = size_t(v) * KT * kvrow;
-#pragma unroll
-    for (int q = 0; q < Gm::JPW; ++q)
-      __builtin_amdgcn_global_load_lds(qsrc[q] + step, (__attribute__((address_space(3))) void*)(
-                                                           lb + (wave + Gm::NW * q) * 1024), 16, 0, 0);
+  if (trunk && (v + 1) * KT <= Lk) {
+    dma_whole<D>(v, kvrow, wave, lb, qsrc);
     return;
   }
 #pragma unroll
@@ -237,28 +254,91 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
   }
 }
 
-// One steady-state tile: start the load of a later tile into dbuf, score the
-// next tile (K in kbuf) and accumulate this one (V in vbuf); the three
-// buffers are distinct.
+// LDS address of this lane's first transposed V read in a staged tile, as an
+// opaque value: the tile's reads then share one base register with immediate
+// offsets (otherwise the compiler hoists one address register per read out of
+// the loop and adds the buffer offset to each).  The callee takes it as a
+// restrict parameter, which tells the compiler that these reads do not touch
+// the tiles still being loaded.
+__device__ __forceinline__ lds_cchar* v_base(const char* p) {
+  lds_cchar* b = (lds_cchar*)(p);
+  asm("" : "+v"(b));
+  return b;
+}
+
+// K operands of a staged tile (this lane's 16-byte reads).
 template <int D>
-__device__ __forceinline__ void tile_step(char* dbuf, const char* kbuf,
-                                          const char* vbuf, bool load, int vload,
-                                          int ntrunk, int nt_total, int Lk, int kvrow, int Wn, int wave,
-                                          const uint16_t* tk, const uint16_t* tv, const uint16_t* bk,
-                                          const uint16_t* bv, const int32_t* pord,
-                                          const int (&dcode)[Geo<D>::JPW],
-                                          const uint16_t* const* qsrc,
-                                          const bf16x8 (&qop)[Geo<D>::NB][D / 16],
-                                          const f32x16 (&cinit)[Geo<D>::NB],
-                                          const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
-                                          float (&lsum)[Geo<D>::NB],
-                                          f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
-  if (load)
-    dma_tile<D>(vload, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, pord, dbuf, dcode, qsrc);
-  tile_scores<D>(kbuf, qop, cinit, Snext);
-  bf16x8 P[Geo<D>::NB][2];
-  tile_probs<D>(Scur, lsum, P);
-  tile_pv<D>(vbuf, P, oacc);
+__device__ __forceinline__ void load_k(const char* kl, bf16x8 (&kop)[D / 16]) {
+#pragma unroll
+  for (int s2 = 0; s2 < D / 16; ++s2) kop[s2] = *reinterpret_cast<const bf16x8*>(kl + 32 * s2);
+}
+
+// The matrix-core work of one steady-state tile, in an explicit order (one
+// wave per SIMD, so the wave's own instruction stream has to keep the matrix
+// core busy).  Each k-step of the next tile's score product (K operands kop,
+// already in registers) is issued together with a share of the V operand
+// reads and of the exponentials of the current tile, so that LDS latency and
+// vector work hide under the matrix products; then, when knext is given, the
+// K operands of the tile after next are read into kop while the V products of
+// the current tile run.  sched_barrier(0) keeps the compiler from regrouping
+// the steps.
+template <int D, bool KNEXT>
+__device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* knext,
+                                             lds_cchar* __restrict__ vl,
+                                             const bf16x8 (&qop)[Geo<D>::NB][D / 16],
+                                             const f32x16 (&cinit)[Geo<D>::NB],
+                                             const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
+                                             float (&lsum)[Geo<D>::NB],
+                                             f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
+  using Gm = Geo<D>;
+  constexpr int NB = Gm::NB, KS = D / 16, OREG = Gm::OREG;
+  constexpr int NPAIR = NB * 8;               // pairs of probabilities per lane
+  constexpr int PPS = (NPAIR + KS - 1) / KS;  // pairs per k-step
+  constexpr int NVO = OREG * 2;               // V operands (two transposed reads each)
+  constexpr int VPS = (NVO + KS - 1) / KS;    // V operands per k-step
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  bf16x8 vop[NVO];
+  bf16x8 P[NB][2];
+  float acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = lsum[nb];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      Snext[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s2], qop[nb][s2], s2 == 0 ? cinit[nb] : Snext[nb],
+                                                          0, 0, 0);
+#pragma unroll
+    for (int o = s2 * VPS; o < (s2 + 1) * VPS && o < NVO; ++o) {
+      const int db = o >> 1, h2 = o & 1;
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vl + 16 * h2 * Gm::VROW + 64 * db));
+      const s16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vl + (16 * h2 + 8) * Gm::VROW + 64 * db));
+      vop[o] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int q = s2 * PPS; q < (s2 + 1) * PPS && q < NPAIR; ++q) {
+      const int nb = q >> 3, i = 2 * (q & 7);
+      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(Scur[nb][i])),
+                         static_cast<__bf16>(fast_exp2(Scur[nb][i + 1]))};
+      P[nb][i >> 3][i & 7] = e2[0];
+      P[nb][i >> 3][(i & 7) + 1] = e2[1];
+      acc[nb] = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc[nb], false);  // sums the bf16 weights used
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (KNEXT) load_k<D>(knext, kop);
+#pragma unroll
+  for (int db = 0; db < OREG; ++db)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[2 * db + h2], P[nb][h2], oacc[nb][db], 0, 0, 0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) lsum[nb] = acc[nb];
 }
 
 template <int D>
@@ -446,6 +526,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         any |= m > lim[nb];
       }
       if (__any(any)) {
+        // keeps this rare path a branch: without a side effect the compiler
+        // would fold it into the common path as unconditional multiplies
+        asm volatile("; rescale" ::: "memory");
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const float m = fmaxf(mx[nb], __shfl_xor(mx[nb], 32, 64));  // whole row, relative to mref
@@ -466,32 +549,60 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       }
     };
 
-    // ---- prologue: tiles 0 and 1 in LDS, tile 2 in flight
-    DMA_TILE(v0, 0);
-    if (n > 1) DMA_TILE(v0 + 1, 1);
-    if (n > 2) DMA_TILE(v0 + 2, 2);
-    wait_vm(n > 2 ? Gm::JPW : 0);
+    // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF, AH
+    // tiles ahead of the tile being accumulated; tile j is waited for at the
+    // end of iteration j - AH + 1, two iterations after its load started, and
+    // its buffer is reloaded in iteration j + 1 (its last reads, of V, are in
+    // iteration j).
+    constexpr int NBUF = Gm::NBUF, AH = NBUF - 1;
+    constexpr bool EK = Gm::EARLYK;  // K operands read one tile early
+    auto buf = [&](int j) __attribute__((always_inline)) { return smem + (j % NBUF) * Gm::BUFB; };
+
+#pragma unroll
+    for (int q = 0; q < AH; ++q)
+      if (q < n) DMA_TILE(v0 + q, q);
+    wait_vm(n > AH - 1 ? Gm::JPW : 0);  // tiles 0 .. AH-2 have landed
     lds_barrier();
 
     f32x16 Sa[NB], Sb[NB];
     tile_scores<D>(smem + koff, qop, cinit, Sa);
     mask(v0, Sa);
     settle(Sa);
+    bf16x8 kop[D / 16];
+    if constexpr (EK) load_k<D>(smem + Gm::BUFB + koff, kop);  // tile 1 (stale data if n == 1: unused)
 
-    // one tile: scores of tile i+1 overlap the probabilities of tile i
-    for (int i = 0; i < n; ++i) {
-      const bool more = i + 1 < n;
-      // load tile i+3 into the buffer of tile i-1 (free since the last barrier);
-      // the scores of tile i+1 are unused after the last tile (they keep the
-      // block straight)
-      tile_step<D>(smem + ((i + 3) & 3) * Gm::BUFB, smem + ((i + 1) & 3) * Gm::BUFB + koff,
-                   smem + (i & 3) * Gm::BUFB + voff, i + 3 < n, v0 + i + 3, ntrunk, nt_total, Lk, kvrow,
-                   Wn, wave, tk, tv, bk, bv, ord + b0, dcode, qsrc, qop, cinit, Sa, Sb, lsum, oacc);
-      if (more) {
+    // Fast iterations: the scored tile needs no mask for this wave's rows and
+    // the tile loaded (if any) is a whole trunk tile, so the step is straight
+    // code.  Tiles [0, nomask) of the pack are visible to every row of the wave.
+    const int nomask = min(ntrunk, (wave_amin + 1) / KT);
+    const int nwhole = min(ntrunk, Lk / KT);
+    int nfast = min(nomask - v0 - 1, n - 1);
+    if (v0 + n > nwhole) nfast = min(nfast, nwhole - v0 - AH);
+    auto fast = [&](int i, const f32x16 (&Sc)[NB], f32x16 (&Sn)[NB]) __attribute__((always_inline)) {
+      if (i + AH < n) dma_whole<D>(v0 + i + AH, kvrow, wave, buf(i + AH), qsrc);
+      if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
+      tile_compute<D, EK>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum, oacc);
+      settle(Sn);
+      wait_vm(i + AH < n ? Gm::JPW : 0);
+      lds_barrier();
+    };
+    int i = 0;
+    for (; i + 1 < nfast; i += 2) {
+      fast(i, Sa, Sb);
+      fast(i + 1, Sb, Sa);
+    }
+    // remaining iterations: scores of tile i+1 overlap the probabilities of
+    // tile i; after the last tile the scores are unused (they keep the block
+    // straight)
+    for (; i < n; ++i) {
+      if (i + AH < n) DMA_TILE(v0 + i + AH, (i + AH) % NBUF);
+      if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
+      tile_compute<D, EK>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sa, Sb, lsum, oacc);
+      if (i + 1 < n) {
         mask(v0 + i + 1, Sb);
         settle(Sb);
       }
-      wait_vm(i + 3 < n ? Gm::JPW : 0);  // tile i+2 has landed
+      wait_vm(i + AH < n ? Gm::JPW : 0);
       lds_barrier();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) Sa[nb] = Sb[nb];
