@@ -83,10 +83,14 @@ struct Geo {
   static constexpr int NJ = (KBYTES + KT * VROW + 1023) / 1024;  // 1 KB writes a tile needs
   static constexpr int JPW = (NJ + NW - 1) / NW; // wave writes per tile (every wave the same)
   static constexpr int BUFB = JPW * NW * 1024;   // bytes of one staged K+V tile, with slack
-  // staged tiles: five where they fit in LDS (the K operands of a tile can
-  // then be read one tile early), else four
-  static constexpr int NBUF = (5 * BUFB + 16 <= 160 * 1024) ? 5 : 4;
-  static constexpr bool EARLYK = NBUF == 5;
+  // staged tiles: up to six where they fit in LDS, at least four.  With
+  // five or more, the K operands of a tile are read one tile early.
+  static constexpr int NBUF = (6 * BUFB + 16 <= 160 * 1024) ? 6 : (5 * BUFB + 16 <= 160 * 1024) ? 5 : 4;
+  static constexpr bool EARLYK = NBUF >= 5;
+  // tiles ahead of the accumulated one that must be readable after a
+  // tile's barrier, and tiles whose loads may stay in flight across it
+  static constexpr int NEED = EARLYK ? 3 : 2;
+  static constexpr int INFL = NBUF - 1 - NEED;
 };
 
 __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
@@ -104,20 +108,21 @@ __device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int Wn, 
   return uint32_t(w);
 }
 
-// Wait until at most n of this wave's vector-memory operations are in flight
-// (n is wave-uniform and small).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-    case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-    case 7: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most k tiles' loads (JPW each) of this wave are in flight,
+// k in [0, 3] (wave-uniform).
+template <int JPW>
+__device__ __forceinline__ void wait_tiles(int k) {
+  static_assert(3 * JPW <= 63, "vmcnt holds at most 63");
+  switch (k) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<JPW>(); break;
+    case 2: wait_vm<2 * JPW>(); break;
+    default: wait_vm<3 * JPW>(); break;
   }
 }
 // Workgroup barrier for LDS traffic: this wave's LDS reads and writes are
@@ -275,13 +280,16 @@ __device__ __forceinline__ void load_k(const char* kl, bf16x8 (&kop)[D / 16]) {
 
 // The matrix-core work of one steady-state tile, in an explicit order (one
 // wave per SIMD, so the wave's own instruction stream has to keep the matrix
-// core busy).  Each k-step of the next tile's score product (K operands kop,
-// already in registers) is issued together with a share of the V operand
-// reads and of the exponentials of the current tile, so that LDS latency and
-// vector work hide under the matrix products; then, when knext is given, the
-// K operands of the tile after next are read into kop while the V products of
-// the current tile run.  sched_barrier(0) keeps the compiler from regrouping
-// the steps.
+// core busy while the vector unit forms the probabilities).  The exponentials
+// of the current tile are spread over the matrix products: most of them
+// between the k-steps of the next tile's score product (K operands kop,
+// already in registers), together with the reads of the current tile's V
+// operands; with two row blocks, the last quarter (the probabilities of the
+// second block's upper 16 keys) between the first V products, which are
+// ordered by (row block, key half) so that each waits only for its own
+// probabilities.  When knext is given, the K operands of the tile after next
+// are read into kop during the V products.  sched_barrier(0) keeps the
+// compiler from regrouping the steps.
 template <int D, bool KNEXT>
 __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* knext,
                                              lds_cchar* __restrict__ vl,
@@ -292,16 +300,25 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
                                              f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
   using Gm = Geo<D>;
   constexpr int NB = Gm::NB, KS = D / 16, OREG = Gm::OREG;
-  constexpr int NPAIR = NB * 8;               // pairs of probabilities per lane
-  constexpr int PPS = (NPAIR + KS - 1) / KS;  // pairs per k-step
-  constexpr int NVO = OREG * 2;               // V operands (two transposed reads each)
-  constexpr int VPS = (NVO + KS - 1) / KS;    // V operands per k-step
+  constexpr int NPAIR = NB * 8;                    // pairs of probabilities per lane
+  constexpr int LATE = NB == 2 ? 4 : 0;            // pairs formed during the V products
+  constexpr int EARLY = NPAIR - LATE;              // pairs formed during the score product
+  constexpr int NVO = OREG * 2;                    // V operands (two transposed reads each)
+  constexpr int VPS = (NVO + KS - 1) / KS;         // V operands per k-step
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
   bf16x8 vop[NVO];
   bf16x8 P[NB][2];
   float acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = lsum[nb];
+  auto pair = [&](int q) __attribute__((always_inline)) {
+    const int nb = q >> 3, i = 2 * (q & 7);
+    const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(Scur[nb][i])),
+                       static_cast<__bf16>(fast_exp2(Scur[nb][i + 1]))};
+    P[nb][i >> 3][i & 7] = e2[0];
+    P[nb][i >> 3][(i & 7) + 1] = e2[1];
+    acc[nb] = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc[nb], false);  // sums the bf16 weights used
+  };
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int s2 = 0; s2 < KS; ++s2) {
@@ -319,24 +336,29 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
       vop[o] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int q = s2 * PPS; q < (s2 + 1) * PPS && q < NPAIR; ++q) {
-      const int nb = q >> 3, i = 2 * (q & 7);
-      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(Scur[nb][i])),
-                         static_cast<__bf16>(fast_exp2(Scur[nb][i + 1]))};
-      P[nb][i >> 3][i & 7] = e2[0];
-      P[nb][i >> 3][(i & 7) + 1] = e2[1];
-      acc[nb] = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc[nb], false);  // sums the bf16 weights used
-    }
+    for (int q = s2 * EARLY / KS; q < (s2 + 1) * EARLY / KS; ++q) pair(q);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (KNEXT) load_k<D>(knext, kop);
+  // V products by (row block, key half); the late pairs go between the first
+  // half of them
+  constexpr int NPV = NB * 2 * OREG;
 #pragma unroll
-  for (int db = 0; db < OREG; ++db)
+  for (int g = 0; g < NB * 2; ++g) {
+    const int nb = g >> 1, h2 = g & 1;
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int db = 0; db < OREG; ++db) {
+      const int sl = g * OREG + db;  // V product slot
+      oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[2 * db + h2], P[nb][h2], oacc[nb][db], 0, 0, 0);
+      if constexpr (LATE > 0) {
+        if (sl < NPV / 2) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[2 * db + h2], P[nb][h2], oacc[nb][db], 0, 0, 0);
+          for (int q = EARLY + sl * LATE / (NPV / 2); q < EARLY + (sl + 1) * LATE / (NPV / 2); ++q) pair(q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (KNEXT && g == NB * 2 - 2) load_k<D>(knext, kop);
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) lsum[nb] = acc[nb];
 }
@@ -350,7 +372,6 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   // scopes and then waits for every global-to-LDS load before any LDS read.
   __shared__ __attribute__((aligned(1024))) char smem[Gm::NBUF * Gm::BUFB + 16];
   int* const s_last = reinterpret_cast<int*>(smem + Gm::NBUF * Gm::BUFB);
-  static_assert(Gm::JPW <= 9, "wait_vm covers at most 9 loads per tile");
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
@@ -549,19 +570,23 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       }
     };
 
-    // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF, AH
-    // tiles ahead of the tile being accumulated; tile j is waited for at the
-    // end of iteration j - AH + 1, two iterations after its load started, and
-    // its buffer is reloaded in iteration j + 1 (its last reads, of V, are in
-    // iteration j).
-    constexpr int NBUF = Gm::NBUF, AH = NBUF - 1;
-    constexpr bool EK = Gm::EARLYK;  // K operands read one tile early
+    // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF and is
+    // loaded AH = NBUF - 1 tiles ahead of the tile being accumulated, in
+    // iteration j - AH (the buffer's previous tile, j - NBUF, had its last
+    // reads in iteration j - NBUF).  Iteration i needs tiles up to i + NEED
+    // readable after its barrier (K of tile i + NEED is read one tile early
+    // when EARLYK), so the loads of the INFL tiles after that may stay in
+    // flight across the barrier.
+    constexpr int NBUF = Gm::NBUF, AH = NBUF - 1, NEED = Gm::NEED, INFL = Gm::INFL;
+    constexpr bool EK = Gm::EARLYK;
     auto buf = [&](int j) __attribute__((always_inline)) { return smem + (j % NBUF) * Gm::BUFB; };
+    // tiles issued beyond tile `last`, capped at INFL
+    auto inflight = [&](int last) __attribute__((always_inline)) { return max(0, min(INFL, n - 1 - last)); };
 
 #pragma unroll
     for (int q = 0; q < AH; ++q)
       if (q < n) DMA_TILE(v0 + q, q);
-    wait_vm(n > AH - 1 ? Gm::JPW : 0);  // tiles 0 .. AH-2 have landed
+    wait_tiles<Gm::JPW>(inflight(NEED - 1));  // tiles 0 .. NEED-1 have landed
     lds_barrier();
 
     f32x16 Sa[NB], Sb[NB];
@@ -583,7 +608,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
       tile_compute<D, EK>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum, oacc);
       settle(Sn);
-      wait_vm(i + AH < n ? Gm::JPW : 0);
+      wait_tiles<Gm::JPW>(inflight(i + NEED));
       lds_barrier();
     };
     int i = 0;
@@ -602,7 +627,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         mask(v0 + i + 1, Sb);
         settle(Sb);
       }
-      wait_vm(i + AH < n ? Gm::JPW : 0);
+      wait_tiles<Gm::JPW>(inflight(i + NEED));
       lds_barrier();
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) Sa[nb] = Sb[nb];
