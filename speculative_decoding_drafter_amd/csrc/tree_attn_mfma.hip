@@ -162,49 +162,6 @@ __device__ __forceinline__ void tile_scores(const char* kl,
   }
 }
 
-// O^T += V^T P^T for a staged V tile (vl: this lane's first transposed read).
-// vl is restrict-qualified so that the transposed reads carry alias
-// information; without any, the compiler makes them wait for every
-// global-to-LDS load in flight.
-template <int D>
-__device__ __forceinline__ void tile_pv(const char* __restrict__ vl,
-                                        const bf16x8 (&P)[Geo<D>::NB][2],
-                                        f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
-  using Gm = Geo<D>;
-#pragma unroll
-  for (int db = 0; db < Gm::OREG; ++db) {
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const s16x4 va = lds_read_tr(vl + 16 * s2 * Gm::VROW + 64 * db);
-      const s16x4 vc = lds_read_tr(vl + (16 * s2 + 8) * Gm::VROW + 64 * db);
-      const bf16x8 vop = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int nb = 0; nb < Gm::NB; ++nb)
-        oacc[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, P[nb][s2], oacc[nb][db], 0, 0, 0);
-    }
-  }
-}
-
-// Probabilities of one tile (bf16, as the V product uses them) and their sum.
-template <int D>
-__device__ __forceinline__ void tile_probs(const f32x16 (&S)[Geo<D>::NB], float (&lsum)[Geo<D>::NB],
-                                           bf16x8 (&P)[Geo<D>::NB][2]) {
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-#pragma unroll
-  for (int nb = 0; nb < Geo<D>::NB; ++nb) {
-    float acc = lsum[nb];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const bf16x2 e2 = {static_cast<__bf16>(fast_exp2(S[nb][i])),
-                         static_cast<__bf16>(fast_exp2(S[nb][i + 1]))};
-      P[nb][i >> 3][i & 7] = e2[0];
-      P[nb][i >> 3][(i & 7) + 1] = e2[1];
-      acc = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, acc, false);  // sums the bf16 weights used below
-    }
-    lsum[nb] = acc;
-  }
-}
-
 // Loads whole trunk tile v (every key < L) into LDS buffer lb: one add per
 // load from this lane's tile-0 source.
 template <int D>
@@ -411,7 +368,6 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   const int Lk = p.L, Wn = p.Wn;
   char* const part = p.part;
   const size_t slot_bytes = p.slot_bytes;
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   // This lane's 16-byte slot in each of its wave's tile loads: key row,
   // chunk, K or V.  Pad chunks and the slack after the V rows load chunk 0 of
