@@ -188,6 +188,25 @@ specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
                                            int32_t* bad_branches, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Kernel timing, for measurement harnesses.
+ *
+ * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd and
+ * specopd_e2etv_fwd_bwd call record a pair of HIP events on its stream
+ * around its main kernel (the attention kernel proper, after the preparation
+ * kernel; the fused E2E-TV kernel, without the small zero and finalize
+ * kernels), so that a harness can divide a kernel's algorithmic work by that
+ * kernel's own duration.  specopd_kernel_timing(0) stops recording and
+ * discards what was recorded.  The events belong to the library (a pool is
+ * created when timing is switched on and kept for the process).
+ *
+ * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
+ * 1 E2E-TV.  Waits for the recorded events and returns the summed elapsed
+ * milliseconds and the number of recorded launches.  Returns
+ * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
+ * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while
+ * another thread is launching calls of this library. */
+specopd_status specopd_kernel_timing(int enable);
+specopd_status specopd_kernel_time(int which, double* total_ms, int* launches);
 
 const char* specopd_status_string(specopd_status status);
 int specopd_version(void);

@@ -10,5 +10,6 @@ from ._lib import (  # noqa: F401
     SPECOPD_ERR_DEVICE_VALIDATION, SPECOPD_F32, SPECOPD_BF16, status_string, specopd_version,
     tree_attn_desc, e2etv_desc, specopd_tree_attn_workspace_size, specopd_tree_attn_fwd,
     specopd_tree_attn_device_status, specopd_e2etv_workspace_size, specopd_e2etv_fwd_bwd,
-    specopd_e2etv_device_status, workspace, tree_attn, e2etv,
+    specopd_e2etv_device_status, specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn,
+    e2etv,
 )

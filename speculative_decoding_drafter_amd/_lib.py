@@ -30,6 +30,7 @@ SPECOPD_BF16 = 1
 EXPORTS = (
     "specopd_tree_attn_workspace_size", "specopd_tree_attn_fwd", "specopd_tree_attn_device_status",
     "specopd_e2etv_workspace_size", "specopd_e2etv_fwd_bwd", "specopd_e2etv_device_status",
+    "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
 
@@ -66,6 +67,8 @@ def _load():
     lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P, c_size_t, P]
     lib.specopd_e2etv_device_status.argtypes = [POINTER(E2etvDesc), P, c_size_t,
                                                 POINTER(c_int32), P]
+    lib.specopd_kernel_timing.argtypes = [c_int]
+    lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
     lib.specopd_status_string.restype = ctypes.c_char_p
     lib.specopd_version.argtypes = []
@@ -84,6 +87,22 @@ def status_string(status: int) -> str:
 
 def specopd_version() -> int:
     return LIB.specopd_version()
+
+
+def specopd_kernel_timing(enable: bool) -> None:
+    """Start (or stop and discard) event recording around each call's main kernel."""
+    st = LIB.specopd_kernel_timing(1 if enable else 0)
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_kernel_timing")
+
+
+def specopd_kernel_time(which: int):
+    """(total ms, launches) recorded for the attention (0) or E2E-TV (1) kernel."""
+    ms, n = c_double(0.0), c_int(0)
+    st = LIB.specopd_kernel_time(int(which), ctypes.byref(ms), ctypes.byref(n))
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_kernel_time")
+    return ms.value, n.value
 
 
 def _ptr(t):

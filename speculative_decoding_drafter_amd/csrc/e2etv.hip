@@ -445,12 +445,14 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.grad = a.grad;
   e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.bcount, f.branch_ok, R);
   const unsigned grid = unsigned(N);
+  timing_mark(1, 0, s);
   if (!a.grad)
     e2etv_fused_kernel<BF16, VECTOR, false, false><<<grid, kThreads, 0, s>>>(f);
   else if (d.grad_dtype == SPECOPD_BF16)
     e2etv_fused_kernel<BF16, VECTOR, true, true><<<grid, kThreads, 0, s>>>(f);
   else
     e2etv_fused_kernel<BF16, VECTOR, true, false><<<grid, kThreads, 0, s>>>(f);
+  timing_mark(1, 1, s);
   e2etv_finalize_kernel<<<1, kFinThreads, 0, s>>>(f.numer, R, f.count, a.loss_out);
   return hipGetLastError();
 }

@@ -102,4 +102,9 @@ struct E2etvArgs {
 };
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s);
 
+// Kernel timing (specopd_kernel_timing): records an event on s before
+// (phase 0) or after (phase 1) the main kernel of call kind `which`
+// (0 attention, 1 E2E-TV) when timing is on; otherwise does nothing.
+void timing_mark(int which, int phase, hipStream_t s);
+
 }  // namespace specopd

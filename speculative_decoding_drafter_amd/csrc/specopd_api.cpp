@@ -7,6 +7,7 @@
 
 #include <vector>
 
+#include <mutex>
 #include "internal.h"
 
 using namespace specopd;
@@ -49,6 +50,54 @@ specopd_status check_e2etv_desc(const specopd_e2etv_desc* d) {
 
 }  // namespace
 
+// ---- kernel timing
+namespace {
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  bool failed = false;
+  std::vector<hipEvent_t> ev[2];  // per call kind: start, stop, start, stop, ...
+  std::vector<hipEvent_t> pool;   // created up front, so recording costs no allocation
+  void clear() {
+    for (auto& v : ev) {
+      for (hipEvent_t e : v) pool.push_back(e);
+      v.clear();
+    }
+    failed = false;
+  }
+};
+constexpr int kTimingPool = 256;
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+}  // namespace
+
+namespace specopd {
+void timing_mark(int which, int phase, hipStream_t s) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (!t.on || which < 0 || which > 1) return;
+  auto& v = t.ev[which];
+  if (phase == 1 && v.size() % 2 == 0) return;  // no open start
+  if (phase == 0 && v.size() % 2 == 1) return;  // already open
+  hipEvent_t e = nullptr;
+  if (!t.pool.empty()) {
+    e = t.pool.back();
+    t.pool.pop_back();
+  } else if (hipEventCreate(&e) != hipSuccess) {
+    t.failed = true;
+    return;
+  }
+  if (hipEventRecord(e, s) != hipSuccess) {
+    t.pool.push_back(e);
+    t.failed = true;
+    return;
+  }
+  v.push_back(e);
+}
+}  // namespace specopd
+
 extern "C" {
 
 const char* specopd_status_string(specopd_status s) {
@@ -64,6 +113,41 @@ const char* specopd_status_string(specopd_status s) {
 }
 
 int specopd_version(void) { return SPECOPD_VERSION; }
+
+
+specopd_status specopd_kernel_timing(int enable) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (hipDeviceSynchronize() != hipSuccess) return SPECOPD_ERR_HIP;
+  t.clear();
+  t.on = enable != 0;
+  while (t.on && t.pool.size() < size_t(kTimingPool)) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return SPECOPD_ERR_HIP;
+    t.pool.push_back(e);
+  }
+  return SPECOPD_OK;
+}
+
+specopd_status specopd_kernel_time(int which, double* total_ms, int* launches) {
+  if (which < 0 || which > 1 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.failed) return SPECOPD_ERR_HIP;
+  const auto& v = t.ev[which];
+  double tot = 0.0;
+  int n = 0;
+  for (size_t i = 0; i + 1 < v.size(); i += 2) {
+    if (hipEventSynchronize(v[i + 1]) != hipSuccess) return SPECOPD_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, v[i], v[i + 1]) != hipSuccess) return SPECOPD_ERR_HIP;
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return SPECOPD_OK;
+}
 
 specopd_status specopd_tree_attn_workspace_size(const specopd_tree_attn_desc* desc, size_t* bytes) {
   specopd_status st = check_tree_desc(desc);

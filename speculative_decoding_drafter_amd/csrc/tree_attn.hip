@@ -456,6 +456,7 @@ static hipError_t launch_generic(const specopd_tree_attn_desc& d, const TreeAttn
       static_cast<const T*>(a.trunk_k), static_cast<const T*>(a.trunk_v), qr, kr,              \
       static_cast<const T*>(a.v), a.anchors, anc, ok, d.B, d.L, d.Wn, d.Hq, d.Hkv,             \
       static_cast<T*>(a.out))
+  timing_mark(0, 0, s);
   switch (d.D) {
     case 64: SPECOPD_GEN(64); break;
     case 128: SPECOPD_GEN(128); break;
@@ -463,6 +464,7 @@ static hipError_t launch_generic(const specopd_tree_attn_desc& d, const TreeAttn
     default: return hipErrorInvalidValue;
   }
 #undef SPECOPD_GEN
+  timing_mark(0, 1, s);
   return hipGetLastError();
 }
 
@@ -529,7 +531,10 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.nwg = (p.nunits + 7) / 8 * 8;
     const int per = p.nwg / 8, ug = np * p.nsplit;
     p.ilv = (ug % per == 0 && ug / per >= 2) ? ug / per : 1;
-    return launch_tree_attn_mfma(d.D, p, s);
+    timing_mark(0, 0, s);
+    e = launch_tree_attn_mfma(d.D, p, s);
+    timing_mark(0, 1, s);
+    return e;
   }
   tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);
   float* qr = reinterpret_cast<float*>(a.ws + L.rot);

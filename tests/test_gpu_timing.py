@@ -1,0 +1,45 @@
+"""Kernel timing hook of the C ABI (specopd_kernel_timing / specopd_kernel_time):
+one recorded launch per call of each kind, durations positive and no longer
+than the whole call, and nothing recorded once timing is off."""
+
+import pytest
+import torch
+
+import speculative_decoding_drafter_amd as sd
+from synthetic import WORKLOADS, gen_attn, gen_loss, shrink_attn, shrink_loss
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_kernel_timing_records_each_call(gpu_ok):
+    acfg = shrink_attn(WORKLOADS[2].attn, L=1024, P=256, B=16)
+    ainp = gen_attn(acfg, 3, device=DEV, cid=2)
+    lcfg = shrink_loss(WORKLOADS[2].loss, R=8, V=151936)
+    linp = gen_loss(lcfg, 3, device=DEV, cid=2)
+    out, desc, ws = sd.tree_attn(ainp)
+    lo = sd.e2etv(linp["draft"], linp["target"], linp["parent"])
+    torch.cuda.synchronize()
+
+    sd.specopd_kernel_timing(True)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record()
+    for _ in range(3):
+        sd.tree_attn(ainp, out=out, ws=ws)
+    e1.record()
+    for _ in range(2):
+        sd.e2etv(linp["draft"], linp["target"], linp["parent"], ws=lo["ws"], outs=lo)
+    e2.record()
+    torch.cuda.synchronize()
+    ta, na = sd.specopd_kernel_time(0)
+    tl, nl = sd.specopd_kernel_time(1)
+    assert (na, nl) == (3, 2)
+    assert 0 < ta <= e0.elapsed_time(e1) * 1.05
+    assert 0 < tl <= e1.elapsed_time(e2) * 1.05
+
+    sd.specopd_kernel_timing(False)
+    sd.tree_attn(ainp, out=out, ws=ws)
+    torch.cuda.synchronize()
+    assert sd.specopd_kernel_time(0) == (0.0, 0)
+    with pytest.raises(sd.SpecopdError):
+        sd.specopd_kernel_time(2)
