@@ -47,10 +47,11 @@ constexpr int mfma_row_blocks(int D) { return D == 256 ? 1 : 2; }
 constexpr int mfma_rows_per_wg(int D) { return mfma_waves(D) * 32 * mfma_row_blocks(D); }
 size_t mfma_slot_bytes(int D);
 // Key-range splits per pack: packs are split only when there are too few of
-// them to give every CU a couple of workgroups.
+// them to give every CU one workgroup (a workgroup fills a CU, and merging
+// split partials costs more than a second round of workgroups saves).
 inline int mfma_nsplit(long long units) {
-  if (units >= 512) return 1;
-  const long long s = (512 + units - 1) / units;
+  if (units >= 256) return 1;
+  const long long s = (256 + units - 1) / units;
   return int(s < 16 ? s : 16);
 }
 

@@ -67,6 +67,8 @@ typedef __attribute__((address_space(3))) const char lds_cchar;
 namespace {
 
 constexpr int KT = 32;            // keys per tile
+constexpr int kMaxSplit = 16;     // key-range splits per pack (at most)
+constexpr int kMergeBatch = 4;    // split partials loaded per merge round trip
 constexpr float kRescale = 8.0f;  // log2 headroom before the reference max moves
 constexpr float kUnset = -3.0e38f;
 
@@ -391,15 +393,15 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   }
 
   {
-    // ---- pack geometry
+    // ---- pack geometry: its trunk tiles are its tile count less the tail
+    // tiles of its branch nodes, so the tile loads can start before any
+    // per-branch metadata has arrived
     const size_t tB = size_t(t) * p.B;
     const int32_t* ord = p.order + tB;
     const int b0 = pk * p.bpp;
     const int nbr = min(p.bpp, p.B - b0);
-    const int bl = ord[b0];
-    const int amax = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
-    const int ntrunk = (amax + KT) / KT;
     const int nt_total = nbr * p.Wn;
+    const int ntrunk = nvt - (nt_total + KT - 1) / KT;
 
     // per-segment bases (uniform); per-lane offsets below stay in 32 bits
     const uint16_t* tk = p.trunk_k + (size_t(t) * p.L * p.Hkv + g) * D;
@@ -415,6 +417,28 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       qsrc[q] = (((code >> 12) & 1) ? tv : tk) + (code & 31) * kvrow + ((code >> 5) & 127) * 8;
     }
 
+    // ---- tile loads: global -> LDS buffer b
+#define DMA_TILE(v, b) \
+  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
+    const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
+    const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
+
+    // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF and is
+    // loaded AH = NBUF - 1 tiles ahead of the tile being accumulated, in
+    // iteration j - AH (the buffer's previous tile, j - NBUF, had its last
+    // reads in iteration j - NBUF).  Iteration i needs tiles up to i + NEED
+    // readable after its barrier (K of tile i + NEED is read one tile early
+    // when EARLYK), so the loads of the INFL tiles after that may stay in
+    // flight across the barrier.
+    constexpr int NBUF = Gm::NBUF, AH = NBUF - 1, NEED = Gm::NEED, INFL = Gm::INFL;
+    constexpr bool EK = Gm::EARLYK;
+    auto buf = [&](int j) __attribute__((always_inline)) { return smem + (j % NBUF) * Gm::BUFB; };
+    // tiles issued beyond tile `last`, capped at INFL
+    auto inflight = [&](int last) __attribute__((always_inline)) { return max(0, min(INFL, n - 1 - last)); };
+
+#pragma unroll
+    for (int q = 0; q < AH; ++q)
+      if (q < n) DMA_TILE(v0 + q, q);
     // ---- this lane's rows: metadata and the Q^T operand
     int ra[NB], rslot[NB];
     uint64_t rmask[NB];
@@ -432,7 +456,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         const bool exists = slot < nbr;
         const int b = exists ? ord[b0 + slot] : 0;
         const bool ok = exists && p.branch_ok[tB + b];
-        ra[nb] = ok ? p.anchors[tB + b] : amax;  // rows without output never force a mask
+        ra[nb] = ok ? p.anchors[tB + b] : ntrunk * KT - 1;  // rows without output never force a mask
         rslot[nb] = slot;
         rmask[nb] = ok ? p.anc[(tB + b) * p.Wn + j] : 0ull;
         wmin = min(wmin, ra[nb]);
@@ -445,12 +469,6 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wmin = min(wmin, __shfl_xor(wmin, o, 64));
     const int wave_amin = __builtin_amdgcn_readfirstlane(wmin);
-
-    // ---- tile loads: global -> LDS buffer b
-#define DMA_TILE(v, b) \
-  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
-    const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
-    const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
 
     // ---- running state
     f32x16 oacc[NB][OREG], cinit[NB];
@@ -526,22 +544,6 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       }
     };
 
-    // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF and is
-    // loaded AH = NBUF - 1 tiles ahead of the tile being accumulated, in
-    // iteration j - AH (the buffer's previous tile, j - NBUF, had its last
-    // reads in iteration j - NBUF).  Iteration i needs tiles up to i + NEED
-    // readable after its barrier (K of tile i + NEED is read one tile early
-    // when EARLYK), so the loads of the INFL tiles after that may stay in
-    // flight across the barrier.
-    constexpr int NBUF = Gm::NBUF, AH = NBUF - 1, NEED = Gm::NEED, INFL = Gm::INFL;
-    constexpr bool EK = Gm::EARLYK;
-    auto buf = [&](int j) __attribute__((always_inline)) { return smem + (j % NBUF) * Gm::BUFB; };
-    // tiles issued beyond tile `last`, capped at INFL
-    auto inflight = [&](int last) __attribute__((always_inline)) { return max(0, min(INFL, n - 1 - last)); };
-
-#pragma unroll
-    for (int q = 0; q < AH; ++q)
-      if (q < n) DMA_TILE(v0 + q, q);
     wait_tiles<Gm::JPW>(inflight(NEED - 1));  // tiles 0 .. NEED-1 have landed
     lds_barrier();
 
@@ -626,39 +628,73 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       __syncthreads();
       write = *s_last != 0;
       if (write) {
-        // merge every segment, this one included, from the stored values in
-        // segment order, so the result does not depend on who merges
+        // merge every non-empty segment, this one included, from the stored
+        // values in segment order, so the result does not depend on who
+        // merges.  Each step is a round trip to memory, so the loads are
+        // batched: every segment's (m, l) first, then the outputs of
+        // kMergeBatch segments at a time.
+        uint32_t fmask = 0;  // non-empty segments (wave-uniform)
+        for (int r2 = 0; r2 < S; ++r2)
+          if (split_begin(r2 + 1) > split_begin(r2)) fmask |= 1u << r2;
+        // a segment that does not exist reads this workgroup's own slot, so
+        // every load stays inside the workspace (its values are not used)
+        const char* const sbase = part + size_t(upk) * S * slot_bytes;
+        auto slot_ptr = [&](int r2) __attribute__((always_inline)) {
+          return sbase + size_t(((fmask >> r2) & 1u) ? r2 : rsp) * slot_bytes;
+        };
+        float sm[NB][kMaxSplit], wgt[NB][kMaxSplit];
+#pragma unroll
+        for (int r2 = 0; r2 < kMaxSplit; ++r2) {
+          const float* qm = reinterpret_cast<const float*>(slot_ptr(r2) + Gm::NW * OWORDS * 64 * 4) +
+                            wave * NB * 128 + lane;
+          const bool f = (fmask >> r2) & 1u;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const float m2 = peek_f32(qm + nb * 128), l2 = peek_f32(qm + nb * 128 + 64);
+            sm[nb][r2] = f ? m2 : kNegInf;
+            wgt[nb][r2] = f ? l2 : 0.f;  // l for now
+          }
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          mref[nb] = kNegInf;
-          lsum[nb] = 0.f;
+          float mx = kNegInf;
+#pragma unroll
+          for (int r2 = 0; r2 < kMaxSplit; ++r2) mx = fmaxf(mx, sm[nb][r2]);
+          float l = 0.f;
+#pragma unroll
+          for (int r2 = 0; r2 < kMaxSplit; ++r2) {
+            const float a = sm[nb][r2] == kNegInf ? 0.f : fast_exp2(sm[nb][r2] - mx);
+            l += a * wgt[nb][r2];
+            wgt[nb][r2] = a;
+          }
+          lsum[nb] = l;
 #pragma unroll
           for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
         }
-        for (int r2 = 0; r2 < S; ++r2) {
-          if (split_begin(r2 + 1) == split_begin(r2)) continue;
-          const char* sl = slot_of(r2);
-          const uint32_t* qo = reinterpret_cast<const uint32_t*>(sl) + wave * OWORDS * 64 + lane;
-          const float* qm = reinterpret_cast<const float*>(sl + Gm::NW * OWORDS * 64 * 4) +
-                            wave * NB * 128 + lane;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float m2 = peek_f32(qm + nb * 128);
-            const float l2 = peek_f32(qm + nb * 128 + 64);
-            const float mn = fmaxf(mref[nb], m2);
-            const float a0 = mref[nb] == kNegInf ? 0.f : fast_exp2(mref[nb] - mn);
-            const float a1 = m2 == kNegInf ? 0.f : fast_exp2(m2 - mn);
+        for (int r0 = 0; r0 < kMaxSplit; r0 += kMergeBatch) {
+          if (r0 >= S) break;
+          uint32_t wv[kMergeBatch][OWORDS];
 #pragma unroll
-            for (int db = 0; db < OREG; ++db)
+          for (int e = 0; e < kMergeBatch; ++e) {
+            const uint32_t* qo = reinterpret_cast<const uint32_t*>(slot_ptr(r0 + e)) + wave * OWORDS * 64 + lane;
 #pragma unroll
-              for (int k = 0; k < 8; ++k) {
-                const uint32_t w2 = peek_u32(qo + ((nb * OREG + db) * 8 + k) * 64);
-                oacc[nb][db][2 * k] = oacc[nb][db][2 * k] * a0 + bf16_lo(w2) * a1;
-                oacc[nb][db][2 * k + 1] = oacc[nb][db][2 * k + 1] * a0 + bf16_hi(w2) * a1;
-              }
-            lsum[nb] = lsum[nb] * a0 + l2 * a1;
-            mref[nb] = mn;
+            for (int x = 0; x < OWORDS; ++x) wv[e][x] = peek_u32(qo + x * 64);
           }
+#pragma unroll
+          for (int e = 0; e < kMergeBatch; ++e)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              const float a = wgt[nb][r0 + e];  // 0 for a missing segment
+#pragma unroll
+              for (int db = 0; db < OREG; ++db)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                  const uint32_t w2 = wv[e][(nb * OREG + db) * 8 + k];
+                  oacc[nb][db][2 * k] += a == 0.f ? 0.f : bf16_lo(w2) * a;
+                  oacc[nb][db][2 * k + 1] += a == 0.f ? 0.f : bf16_hi(w2) * a;
+                }
+            }
         }
       }
     }
