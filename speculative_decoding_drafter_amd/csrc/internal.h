@@ -22,7 +22,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   ctr        int32  [T][Hkv][npacks]  splits of a pack that finished
 //   part       partial results, one slot per (pack, split) when packs are split
 struct TreeAttnWs {
-  size_t anc, branch_ok, order, rot, pstart, ctr, part, total;
+  size_t anc, branch_ok, order, rot, pstart, ustart, umap, ctr, part, total;
 };
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d);
 
@@ -32,6 +32,7 @@ struct TreeAttnArgs {
   void* out;
   char* ws;
   float rope_base, scale;
+  int timing_kind;  // call kind the attention kernel is timed as (timing_mark)
 };
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
 
@@ -65,6 +66,8 @@ struct MfmaParams {
   const int32_t* branch_ok;           // [T][B]
   const int32_t* order;               // [T][B] branches by anchor, longest first
   const int32_t* pstart;              // [T][npacks+1]
+  const int32_t* ustart;              // [T][npacks+1] first unit of each pack (per kv head)
+  const int32_t* umap;                // [T][npacks*nsplit] pack of each unit
   int32_t* ctr;                       // [T][Hkv][npacks], zero on entry
   char* part;                         // nunits slots of slot_bytes (nsplit > 1)
   size_t slot_bytes;
@@ -73,11 +76,57 @@ struct MfmaParams {
   int bpp;     // branches per pack
   int npacks;  // packs per trunk
   int nsplit;  // key-range splits per pack
-  int nunits;  // T * Hkv * npacks * nsplit
-  int nwg;     // workgroups: nunits rounded up to a multiple of 8
-  int ilv;     // XCD blocks a kv head's units are dealt across (1: none)
+  int ugp;      // units per (trunk, kv head) group, padded to a multiple of ilv
+  int nunits;   // T * Hkv * ugp
+  int nwg;      // workgroups: nunits rounded up to a multiple of 8
+  int ilv;      // XCD blocks a group's units are dealt across (1: none)
+  int chunked;  // 1: consecutive units to one XCD; 0: units by block index
 };
+// Grid of the matrix-core kernel from T, Hkv, npacks and nsplit.  With a
+// multiple of 8 (trunk, kv head) groups every XCD gets whole groups; with 1,
+// 2 or 4 groups each spans 8/groups XCDs, its packs dealt to them
+// alternately; any other count goes by block index, which balances the XCDs
+// without keeping a group on one of them.
+inline void mfma_grid(MfmaParams& p) {
+  const int ug = p.npacks * p.nsplit, ng = p.T * p.Hkv;
+  p.ilv = 1;
+  p.ugp = ug;
+  p.chunked = 1;
+  if (ng % 8 != 0) {
+    if (8 % ng == 0) {
+      p.ilv = 8 / ng;
+      p.ugp = (ug + p.ilv - 1) / p.ilv * p.ilv;
+    } else {
+      p.chunked = 0;
+    }
+  }
+  p.nunits = ng * p.ugp;
+  p.nwg = (p.nunits + 7) / 8 * 8;
+}
 hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------- trunk prefill
+// Workspace layout (prefill.hip).  Matrix-core path (bf16):
+//   anchors    int32  [L-1]           anchor of branch b (= token b+1) is b
+//   qr         bf16   [T][L-1][Hq][D] rotated, scaled queries of tokens 1..L-1
+//   branch_ok, order, anc, pstart, ustart, umap: the tree kernel's plan of the
+//              L-1 one-node branches (the same for every trunk)
+//   ctr        int32  [T][Hkv][npacks]
+//   part       split partials (one trunk's launch at a time)
+// fp32 path: anchors, parent (-1), pos (b+1), then the tree workspace.
+struct PrefillWs {
+  size_t anchors, qr, branch_ok, order, anc, pstart, ustart, umap, ctr, part;
+  size_t parent, pos, tree, total;
+};
+PrefillWs prefill_ws_layout(const specopd_prefill_desc& d);
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  void *cache_k, *cache_v, *out;
+  char* ws;
+  float rope_base, scale;
+};
+hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- E2E-TV
 // Workspace layout:
@@ -105,7 +154,8 @@ hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStre
 
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`
-// (0 attention, 1 E2E-TV) when timing is on; otherwise does nothing.
+// (0 attention, 1 E2E-TV, 2 prefill) when timing is on; otherwise does
+// nothing (also for a negative `which`).
 void timing_mark(int which, int phase, hipStream_t s);
 
 }  // namespace specopd

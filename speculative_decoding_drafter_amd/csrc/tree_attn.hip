@@ -87,9 +87,9 @@ struct PrepParams {
   const int32_t *anchors, *parent, *pos;
   const uint16_t *q, *k;
   uint64_t* anc;
-  int32_t *branch_ok, *order, *pstart, *ctr;
+  int32_t *branch_ok, *order, *pstart, *ustart, *umap, *ctr;
   uint16_t *qr, *kr;
-  int T, B, L, Wn, Hq, Hkv, D, bpp, npacks;
+  int T, B, L, Wn, Hq, Hkv, D, bpp, npacks, nsplit;
   double log2_base;
   float qmul;
 };
@@ -261,6 +261,25 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
     for (int i = lo; i < hi; ++i) {
       ps[i] = acc;
       acc += tiles(i);
+    }
+    // units of the matrix-core kernel per (trunk, kv head): U = npacks *
+    // nsplit, one per pack plus the other U - npacks dealt to the packs in
+    // proportion to their key tiles (cumulatively, so they add up exactly)
+    __syncthreads();
+    {
+      const int U = np * p.nsplit, extra = U - np;
+      const long long NT = ps[np];
+      int32_t* us = p.ustart + size_t(t) * (np + 1);
+      int32_t* um = p.umap + size_t(t) * U;
+      for (int i = tid; i <= np; i += 256) {
+        const long long e = NT > 0 ? (long long)extra * ps[i] / NT : 0;
+        us[i] = i == np ? U : i + int(e);
+      }
+      for (int i = tid; i < np; i += 256) {
+        const long long e0 = NT > 0 ? (long long)extra * ps[i] / NT : 0;
+        const long long e1 = i + 1 == np ? extra : (NT > 0 ? (long long)extra * ps[i + 1] / NT : 0);
+        for (int u = i + int(e0); u < i + 1 + int(e1); ++u) um[u] = i;
+      }
     }
     int32_t* c = p.ctr + size_t(t) * p.Hkv * np;
     for (int i = tid; i < p.Hkv * np; i += 256) c[i] = 0;
@@ -437,9 +456,11 @@ TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   const size_t esz = mf ? sizeof(uint16_t) : sizeof(float);
   w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * esz, 256);
   w.pstart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
-  w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
   const long long units = mf ? (long long)d.T * d.Hkv * np : 0;
   const int nsplit = mf ? mfma_nsplit(units) : 1;
+  w.ustart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
+  w.umap = off;       off = align_up(off + (mf ? size_t(d.T) * np * nsplit * sizeof(int32_t) : 0), 256);
+  w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
   w.part = off;       off = align_up(off + (nsplit > 1 ? size_t(units) * nsplit * mfma_slot_bytes(d.D) : 0), 256);
   w.total = off;
   return w;
@@ -456,7 +477,7 @@ static hipError_t launch_generic(const specopd_tree_attn_desc& d, const TreeAttn
       static_cast<const T*>(a.trunk_k), static_cast<const T*>(a.trunk_v), qr, kr,              \
       static_cast<const T*>(a.v), a.anchors, anc, ok, d.B, d.L, d.Wn, d.Hq, d.Hkv,             \
       static_cast<T*>(a.out))
-  timing_mark(0, 0, s);
+  timing_mark(a.timing_kind, 0, s);
   switch (d.D) {
     case 64: SPECOPD_GEN(64); break;
     case 128: SPECOPD_GEN(128); break;
@@ -464,7 +485,7 @@ static hipError_t launch_generic(const specopd_tree_attn_desc& d, const TreeAttn
     default: return hipErrorInvalidValue;
   }
 #undef SPECOPD_GEN
-  timing_mark(0, 1, s);
+  timing_mark(a.timing_kind, 1, s);
   return hipGetLastError();
 }
 
@@ -499,6 +520,9 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     pp.k = static_cast<const uint16_t*>(a.k);
     pp.anc = anc; pp.branch_ok = ok; pp.order = order;
     pp.pstart = reinterpret_cast<int32_t*>(a.ws + L.pstart);
+    pp.ustart = reinterpret_cast<int32_t*>(a.ws + L.ustart);
+    pp.umap = reinterpret_cast<int32_t*>(a.ws + L.umap);
+    pp.nsplit = mfma_nsplit((long long)d.T * d.Hkv * np);
     pp.ctr = reinterpret_cast<int32_t*>(a.ws + L.ctr);
     pp.qr = qr; pp.kr = kr;
     pp.T = d.T; pp.B = d.B; pp.L = d.L; pp.Wn = d.Wn; pp.Hq = d.Hq; pp.Hkv = d.Hkv; pp.D = d.D;
@@ -519,6 +543,8 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.branch_ok = ok;
     p.order = order;
     p.pstart = pp.pstart;
+    p.ustart = pp.ustart;
+    p.umap = pp.umap;
     p.ctr = pp.ctr;
     p.part = a.ws + L.part;
     p.slot_bytes = mfma_slot_bytes(d.D);
@@ -526,14 +552,11 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.T = d.T; p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
     p.bpp = bpp;
     p.npacks = np;
-    p.nsplit = mfma_nsplit((long long)d.T * d.Hkv * np);
-    p.nunits = d.T * d.Hkv * np * p.nsplit;
-    p.nwg = (p.nunits + 7) / 8 * 8;
-    const int per = p.nwg / 8, ug = np * p.nsplit;
-    p.ilv = (ug % per == 0 && ug / per >= 2) ? ug / per : 1;
-    timing_mark(0, 0, s);
+    p.nsplit = pp.nsplit;
+    mfma_grid(p);
+    timing_mark(a.timing_kind, 0, s);
     e = launch_tree_attn_mfma(d.D, p, s);
-    timing_mark(0, 1, s);
+    timing_mark(a.timing_kind, 1, s);
     return e;
   }
   tree_plan_kernel<<<(TB + 255) / 256, 256, 0, s>>>(a.anchors, a.parent, a.pos, TB, d.Wn, d.L, anc, ok);

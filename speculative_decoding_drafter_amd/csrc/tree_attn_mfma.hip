@@ -67,7 +67,6 @@ typedef __attribute__((address_space(3))) const char lds_cchar;
 namespace {
 
 constexpr int KT = 32;            // keys per tile
-constexpr int kMaxSplit = 16;     // key-range splits per pack (at most)
 constexpr int kMergeBatch = 4;    // split partials loaded per merge round trip
 constexpr float kRescale = 8.0f;  // log2 headroom before the reference max moves
 constexpr float kUnset = -3.0e38f;
@@ -337,25 +336,34 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   const int gi = lane >> 4, rq = lane & 15;
   const int nwg = gridDim.x;
 
-  // Work unit u = ((t * Hkv + g) * npacks + pack) * nsplit + split.  Units are
-  // dealt to the XCDs in consecutive blocks (workgroups go to the 8 XCDs round
-  // robin), so the packs of one kv head run side by side on one XCD and stream
-  // the same trunk rows through its L2.  When a kv head's units fill `ilv`
-  // XCD blocks, its packs are dealt to those blocks alternately, so that each
-  // XCD gets a like share of long and short packs.
-  const int ub = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  // Work unit u = (t * Hkv + g) * ugp + j, j < npacks * nsplit the j-th split
+  // of the (trunk, kv head) group in pack order; ugp >= that count pads the
+  // group to a multiple of ilv.  In chunked mode units are dealt to the XCDs
+  // in consecutive blocks (workgroups go to the 8 XCDs round robin), so the
+  // packs of one kv head run side by side on one XCD and stream the same
+  // trunk rows through its L2; when a group spans `ilv` XCD blocks, its packs
+  // are dealt to those blocks alternately, so that each XCD gets a like share
+  // of long and short packs.  Otherwise units follow the block index.
+  const int ub = p.chunked ? (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : int(blockIdx.x);
   if (ub >= p.nunits) return;
-  const int np = p.npacks, S = p.nsplit;
-  const int ug = np * S;                   // units per (trunk, kv head)
-  const int tg = ub / ug;
-  int jj = ub - tg * ug;
+  const int np = p.npacks;
+  const int ug = np * p.nsplit;            // units per (trunk, kv head)
+  const int tg = ub / p.ugp;
+  int jj = ub - tg * p.ugp;
   if (p.ilv > 1) {
-    const int c = ug / p.ilv;
+    const int c = p.ugp / p.ilv;
     jj = (jj % c) * p.ilv + jj / c;
   }
-  const int pk = jj / S, rsp = jj - pk * S;
-  const int upk = tg * np + pk;
+  if (jj >= ug) return;  // padding
   const int g = tg % p.Hkv, t = tg / p.Hkv;
+  // the pack of this unit and its splits: packs get units in proportion to
+  // their key tiles (at least one each), so splits are of similar length
+  const int pk = p.umap[size_t(t) * ug + jj];
+  const int* us = p.ustart + size_t(t) * (np + 1);
+  const int u0 = us[pk];
+  const int S = us[pk + 1] - u0;  // splits of this pack
+  const int rsp = jj - u0;
+  const int upk = tg * np + pk;
   const int* ps = p.pstart + size_t(t) * (np + 1);
   const int nvt = ps[pk + 1] - ps[pk];
   // split rsp takes the pack's key tiles [rsp * nvt / S, (rsp + 1) * nvt / S)
@@ -600,7 +608,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     if (!whole) {
       const size_t ctr_i = upk;  // one counter per (trunk, kv head, pack)
       auto slot_of = [=](int r2) __attribute__((always_inline)) -> char* {
-        return part + (size_t(upk) * S + r2) * slot_bytes;
+        return part + (size_t(tg) * ug + u0 + r2) * slot_bytes;
       };
       constexpr int OWORDS = NB * OREG * 8;  // bf16 pairs per lane
       char* mine = slot_of(rsp);
@@ -633,68 +641,65 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         // merges.  Each step is a round trip to memory, so the loads are
         // batched: every segment's (m, l) first, then the outputs of
         // kMergeBatch segments at a time.
-        uint32_t fmask = 0;  // non-empty segments (wave-uniform)
-        for (int r2 = 0; r2 < S; ++r2)
-          if (split_begin(r2 + 1) > split_begin(r2)) fmask |= 1u << r2;
         // a segment that does not exist reads this workgroup's own slot, so
         // every load stays inside the workspace (its values are not used)
-        const char* const sbase = part + size_t(upk) * S * slot_bytes;
-        auto slot_ptr = [&](int r2) __attribute__((always_inline)) {
-          return sbase + size_t(((fmask >> r2) & 1u) ? r2 : rsp) * slot_bytes;
+        const char* const sbase = part + (size_t(tg) * ug + u0) * slot_bytes;
+        auto present = [&](int r2) __attribute__((always_inline)) {
+          return r2 < S && split_begin(r2 + 1) > split_begin(r2);
         };
-        float sm[NB][kMaxSplit], wgt[NB][kMaxSplit];
-#pragma unroll
-        for (int r2 = 0; r2 < kMaxSplit; ++r2) {
-          const float* qm = reinterpret_cast<const float*>(slot_ptr(r2) + Gm::NW * OWORDS * 64 * 4) +
-                            wave * NB * 128 + lane;
-          const bool f = (fmask >> r2) & 1u;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-            const float m2 = peek_f32(qm + nb * 128), l2 = peek_f32(qm + nb * 128 + 64);
-            sm[nb][r2] = f ? m2 : kNegInf;
-            wgt[nb][r2] = f ? l2 : 0.f;  // l for now
-          }
-        }
+        float mx[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          float mx = kNegInf;
-#pragma unroll
-          for (int r2 = 0; r2 < kMaxSplit; ++r2) mx = fmaxf(mx, sm[nb][r2]);
-          float l = 0.f;
-#pragma unroll
-          for (int r2 = 0; r2 < kMaxSplit; ++r2) {
-            const float a = sm[nb][r2] == kNegInf ? 0.f : fast_exp2(sm[nb][r2] - mx);
-            l += a * wgt[nb][r2];
-            wgt[nb][r2] = a;
-          }
-          lsum[nb] = l;
+          mx[nb] = kNegInf;
+          lsum[nb] = 0.f;
 #pragma unroll
           for (int db = 0; db < OREG; ++db) oacc[nb][db] = f32x16{};
         }
-#pragma unroll
-        for (int r0 = 0; r0 < kMaxSplit; r0 += kMergeBatch) {
-          if (r0 >= S) break;
+        for (int r0 = 0; r0 < S; r0 += kMergeBatch) {
+          bool f[kMergeBatch];
+          float m2[kMergeBatch][NB], l2[kMergeBatch][NB];
           uint32_t wv[kMergeBatch][OWORDS];
 #pragma unroll
           for (int e = 0; e < kMergeBatch; ++e) {
-            const uint32_t* qo = reinterpret_cast<const uint32_t*>(slot_ptr(r0 + e)) + wave * OWORDS * 64 + lane;
+            f[e] = present(r0 + e);
+            const char* sl = sbase + size_t(f[e] ? r0 + e : rsp) * slot_bytes;
+            const uint32_t* qo = reinterpret_cast<const uint32_t*>(sl) + wave * OWORDS * 64 + lane;
+            const float* qm = reinterpret_cast<const float*>(sl + Gm::NW * OWORDS * 64 * 4) + wave * NB * 128 + lane;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+              m2[e][nb] = peek_f32(qm + nb * 128);
+              l2[e][nb] = peek_f32(qm + nb * 128 + 64);
+            }
 #pragma unroll
             for (int x = 0; x < OWORDS; ++x) wv[e][x] = peek_u32(qo + x * 64);
           }
 #pragma unroll
-          for (int e = 0; e < kMergeBatch; ++e)
+          for (int nb = 0; nb < NB; ++nb) {
+            // new reference max over the running one and this batch
+            float mn = mx[nb];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              const float a = wgt[nb][r0 + e];  // 0 for a missing segment
+            for (int e = 0; e < kMergeBatch; ++e)
+              if (f[e]) mn = fmaxf(mn, m2[e][nb]);
+            const float a0 = mx[nb] == kNegInf ? 0.f : fast_exp2(mx[nb] - mn);
+            lsum[nb] *= a0;
+#pragma unroll
+            for (int db = 0; db < OREG; ++db) oacc[nb][db] *= a0;
+            mx[nb] = mn;
+#pragma unroll
+            for (int e = 0; e < kMergeBatch; ++e) {
+              const float a = (!f[e] || m2[e][nb] == kNegInf) ? 0.f : fast_exp2(m2[e][nb] - mn);
+              if (a == 0.f) continue;
+              lsum[nb] += a * l2[e][nb];
 #pragma unroll
               for (int db = 0; db < OREG; ++db)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                   const uint32_t w2 = wv[e][(nb * OREG + db) * 8 + k];
-                  oacc[nb][db][2 * k] += a == 0.f ? 0.f : bf16_lo(w2) * a;
-                  oacc[nb][db][2 * k + 1] += a == 0.f ? 0.f : bf16_hi(w2) * a;
+                  oacc[nb][db][2 * k] += bf16_lo(w2) * a;
+                  oacc[nb][db][2 * k + 1] += bf16_hi(w2) * a;
                 }
             }
+          }
         }
       }
     }
