@@ -1,7 +1,7 @@
 /*
  * libspecopd — branch-parallel target scoring for SpecOPD on MI355X (gfx950).
  *
- * Two operations, both defined by the pages describing arXiv 2611.02846,
+ * Three operations, all defined by the pages describing arXiv 2611.02846,
  * "SpecOPD: Branch-Parallel On-Policy Distillation for Speculative Decoding":
  *
  *   specopd_tree_attn_fwd   tree-masked GQA attention of every branch node
@@ -12,6 +12,8 @@
  *                           its gradient with respect to the draft logits
  *                           (jaehun.me review, §1.1 and §3.3, Eqs. 8, 9, 13;
  *                           §3.2, Eq. 18; rustineverything.app summary, §2.3).
+ *   specopd_prefill_fwd     the causal pass over each trunk that fills that
+ *                           cache (jaehun.me review, §3.1 step 1, §3.2(a)).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -128,6 +130,53 @@ specopd_status specopd_tree_attn_device_status(const specopd_tree_attn_desc* des
                                                int32_t* bad_branches, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Trunk prefill                                                             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Problem sizes: T trunks of length L >= 1, Hq query heads and Hkv kv heads
+ * (Hq % Hkv == 0), head size D in {64, 128, 256}.
+ */
+typedef struct {
+  int32_t T, L, Hq, Hkv, D;
+  specopd_dtype dtype; /* of q, k, v, cache_k, cache_v and out              */
+  float rope_base;     /* rotary base; <= 0 means 10000                       */
+  float scale;         /* score scale; <= 0 means 1/sqrt(D)                   */
+  uint32_t flags;      /* reserved, must be 0                                 */
+} specopd_prefill_desc;
+
+specopd_status specopd_prefill_workspace_size(const specopd_prefill_desc* desc, size_t* bytes);
+
+/*
+ * The one pass over the reference trajectory that every branch attaches to
+ * (jaehun.me review §3.1 step 1 and §3.2(a); rustineverything.app summary
+ * §2.2): causal GQA self-attention of each trunk, token s reading tokens
+ * 0..s, with rotary embedding at the trunk positions 0..L-1 (the same
+ * rotate-half convention as specopd_tree_attn_fwd).  It also leaves the KV
+ * cache that specopd_tree_attn_fwd takes as trunk_k / trunk_v.
+ *
+ *   q        [T][L][Hq][D]   queries, NOT rotated
+ *   k, v     [T][L][Hkv][D]  keys (NOT rotated) and values
+ *   cache_k  [T][L][Hkv][D]  out: keys rotated at their trunk positions
+ *   cache_v  [T][L][Hkv][D]  out: the values, copied
+ *   out      [T][L][Hq][D]   out: attention output of every token
+ *   workspace / workspace_bytes  device scratch of at least
+ *                            specopd_prefill_workspace_size bytes, 16-byte
+ *                            aligned
+ *
+ * Row s >= 1 of a trunk is scored exactly as a one-node branch anchored at
+ * s-1 whose key and value are token s's (the specopd_tree_attn_fwd kernels,
+ * reading the branch key from the cache just written); row 0 is its own
+ * value.  bf16 inputs use the matrix cores with fp32 accumulation; fp32
+ * inputs use fp32 arithmetic throughout.  Outputs must not alias inputs or
+ * each other.  All pointers 16-byte aligned.
+ */
+specopd_status specopd_prefill_fwd(const specopd_prefill_desc* desc, const void* q,
+                                   const void* k, const void* v, void* cache_k, void* cache_v,
+                                   void* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* E2E-TV surrogate                                                          */
 /* ------------------------------------------------------------------------ */
 
@@ -190,17 +239,18 @@ specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
 /* ------------------------------------------------------------------------ */
 /* Kernel timing, for measurement harnesses.
  *
- * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd and
- * specopd_e2etv_fwd_bwd call record a pair of HIP events on its stream
- * around its main kernel (the attention kernel proper, after the preparation
- * kernel; the fused E2E-TV kernel, without the small zero and finalize
- * kernels), so that a harness can divide a kernel's algorithmic work by that
- * kernel's own duration.  specopd_kernel_timing(0) stops recording and
+ * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd,
+ * specopd_e2etv_fwd_bwd and specopd_prefill_fwd call record a pair of HIP
+ * events on its stream around each launch of its main kernel (the attention
+ * kernel proper, after the preparation kernel; the fused E2E-TV kernel,
+ * without the small zero and finalize kernels; the attention kernel of each
+ * prefilled trunk), so that a harness can divide a kernel's algorithmic work
+ * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is
  * created when timing is switched on and kept for the process).
  *
  * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
- * 1 E2E-TV.  Waits for the recorded events and returns the summed elapsed
+ * 1 E2E-TV, 2 prefill.  Waits for the recorded events and returns the summed elapsed
  * milliseconds and the number of recorded launches.  Returns
  * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
  * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while

@@ -11,5 +11,5 @@ from ._lib import (  # noqa: F401
     tree_attn_desc, e2etv_desc, specopd_tree_attn_workspace_size, specopd_tree_attn_fwd,
     specopd_tree_attn_device_status, specopd_e2etv_workspace_size, specopd_e2etv_fwd_bwd,
     specopd_e2etv_device_status, specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn,
-    e2etv,
+    e2etv, PrefillDesc, prefill_desc, specopd_prefill_workspace_size, specopd_prefill_fwd, prefill,
 )

@@ -30,6 +30,7 @@ SPECOPD_BF16 = 1
 EXPORTS = (
     "specopd_tree_attn_workspace_size", "specopd_tree_attn_fwd", "specopd_tree_attn_device_status",
     "specopd_e2etv_workspace_size", "specopd_e2etv_fwd_bwd", "specopd_e2etv_device_status",
+    "specopd_prefill_workspace_size", "specopd_prefill_fwd",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
@@ -47,6 +48,11 @@ class E2etvDesc(ctypes.Structure):
                 ("flags", c_uint32)]
 
 
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("L", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32),
+                ("dtype", c_int), ("rope_base", c_float), ("scale", c_float), ("flags", c_uint32)]
+
+
 class SpecopdError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -56,7 +62,7 @@ class SpecopdError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
-                          "(python -m speculative_decoding_drafter_amd.build)")
+                          "(python speculative_decoding_drafter_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     lib.specopd_tree_attn_workspace_size.argtypes = [POINTER(TreeAttnDesc), POINTER(c_size_t)]
@@ -67,6 +73,8 @@ def _load():
     lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P, c_size_t, P]
     lib.specopd_e2etv_device_status.argtypes = [POINTER(E2etvDesc), P, c_size_t,
                                                 POINTER(c_int32), P]
+    lib.specopd_prefill_workspace_size.argtypes = [POINTER(PrefillDesc), POINTER(c_size_t)]
+    lib.specopd_prefill_fwd.argtypes = [POINTER(PrefillDesc)] + [P] * 6 + [P, c_size_t, P]
     lib.specopd_kernel_timing.argtypes = [c_int]
     lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
@@ -97,7 +105,7 @@ def specopd_kernel_timing(enable: bool) -> None:
 
 
 def specopd_kernel_time(which: int):
-    """(total ms, launches) recorded for the attention (0) or E2E-TV (1) kernel."""
+    """(total ms, launches) recorded for the attention (0), E2E-TV (1) or prefill (2) kernel."""
     ms, n = c_double(0.0), c_int(0)
     st = LIB.specopd_kernel_time(int(which), ctypes.byref(ms), ctypes.byref(n))
     if st != SPECOPD_OK:
@@ -132,6 +140,32 @@ def e2etv_desc(R, Wn, V, logits_dtype, grad_dtype=torch.float32, norm_count=0.0,
     ld = _DT.get(logits_dtype, logits_dtype) if not isinstance(logits_dtype, int) else logits_dtype
     gd = _DT.get(grad_dtype, grad_dtype) if not isinstance(grad_dtype, int) else grad_dtype
     return E2etvDesc(R, Wn, V, ld, gd, norm_count, grad_scale, flags)
+
+
+def prefill_desc(T, L, Hq, Hkv, D, dtype, rope_base=10000.0, scale=0.0, flags=0):
+    return PrefillDesc(T, L, Hq, Hkv, D, _DT.get(dtype, dtype) if not isinstance(dtype, int) else dtype,
+                       rope_base, scale, flags)
+
+
+def specopd_prefill_workspace_size(desc: PrefillDesc) -> int:
+    n = c_size_t(0)
+    st = LIB.specopd_prefill_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_prefill_workspace_size")
+    return n.value
+
+
+def specopd_prefill_fwd(desc, q, k, v, cache_k, cache_v, out, workspace, stream=None, raw_status=False):
+    st = LIB.specopd_prefill_fwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(cache_k), _ptr(cache_v), _ptr(out),
+        _ptr(workspace),
+        c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+        _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_prefill_fwd")
+    return out
 
 
 def specopd_tree_attn_workspace_size(desc: TreeAttnDesc) -> int:
@@ -218,6 +252,21 @@ def tree_attn(inp: dict, rope_base=10000.0, scale=0.0, ws=None, out=None):
     specopd_tree_attn_fwd(desc, inp["trunk_k"], inp["trunk_v"], q, inp["k"], inp["v"],
                           inp["anchors"], inp["parent"], inp["pos"], out, ws)
     return out, desc, ws
+
+
+def prefill(q, k, v, rope_base=10000.0, scale=0.0, ws=None, outs=None):
+    """Trunk prefill of q [T][L][Hq][D], k, v [T][L][Hkv][D] (device tensors);
+    returns (out, cache_k, cache_v, desc, ws)."""
+    T, L, Hq, D = q.shape
+    Hkv = k.shape[2]
+    desc = prefill_desc(T, L, Hq, Hkv, D, q.dtype, rope_base, scale)
+    if ws is None:
+        ws = workspace(specopd_prefill_workspace_size(desc), q.device)
+    if outs is None:
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    out, ck, cv = outs
+    specopd_prefill_fwd(desc, q, k, v, ck, cv, out, ws)
+    return out, ck, cv, desc, ws
 
 
 def e2etv(draft, target, parent, grad=True, grad_dtype=torch.float32, norm_count=0.0,

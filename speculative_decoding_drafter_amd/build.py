@@ -1,6 +1,6 @@
 """Builds libspecopd.so in-tree with hipcc for gfx950.
 
-    python -m speculative_decoding_drafter_amd.build
+    python speculative_decoding_drafter_amd/build.py
 
 Every source is compiled on every call (the caller wants a fresh check that
 the tree builds); objects go to ``_build/`` next to this file.
@@ -30,7 +30,7 @@ COMMON = [
     "-I", os.path.join(HERE, "..", "include"),
 ]
 
-SOURCES = ["specopd_api.cpp", "e2etv.hip", "tree_attn.hip", "tree_attn_mfma.hip"]
+SOURCES = ["specopd_api.cpp", "e2etv.hip", "tree_attn.hip", "tree_attn_mfma.hip", "prefill.hip"]
 
 # Matrix-core accumulators live in ordinary VGPRs (the AGPR half of the file
 # serves as extra room): with one wave per SIMD the attention kernel's

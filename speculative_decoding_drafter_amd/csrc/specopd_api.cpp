@@ -34,6 +34,20 @@ specopd_status check_tree_desc(const specopd_tree_attn_desc* d) {
   return SPECOPD_OK;
 }
 
+specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
+  if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->T < 1 || d->L < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->Hq % d->Hkv != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->D != 64 && d->D != 128 && d->D != 256) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->dtype != SPECOPD_F32 && d->dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(d->rope_base) && isfinite(d->scale))) return SPECOPD_ERR_INVALID_ARGUMENT;
+  // one trunk is one tree call of L-1 one-node branches: the same index limits
+  if (double(d->L) * d->Hq > 2147483647.0 || double(d->T) * d->L * (d->Hq + d->Hkv) * d->D > 9.0e15)
+    return SPECOPD_ERR_UNSUPPORTED;
+  return SPECOPD_OK;
+}
+
 specopd_status check_e2etv_desc(const specopd_e2etv_desc* d) {
   if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->R < 1 || d->Wn < 1 || d->V < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
@@ -56,7 +70,7 @@ struct TimingState {
   std::mutex mu;
   bool on = false;
   bool failed = false;
-  std::vector<hipEvent_t> ev[2];  // per call kind: start, stop, start, stop, ...
+  std::vector<hipEvent_t> ev[3];  // per call kind: start, stop, start, stop, ...
   std::vector<hipEvent_t> pool;   // created up front, so recording costs no allocation
   void clear() {
     for (auto& v : ev) {
@@ -77,7 +91,7 @@ namespace specopd {
 void timing_mark(int which, int phase, hipStream_t s) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on || which < 0 || which > 1) return;
+  if (!t.on || which < 0 || which > 2) return;
   auto& v = t.ev[which];
   if (phase == 1 && v.size() % 2 == 0) return;  // no open start
   if (phase == 0 && v.size() % 2 == 1) return;  // already open
@@ -130,7 +144,7 @@ specopd_status specopd_kernel_timing(int enable) {
 }
 
 specopd_status specopd_kernel_time(int which, double* total_ms, int* launches) {
-  if (which < 0 || which > 1 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (which < 0 || which > 2 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   if (t.failed) return SPECOPD_ERR_HIP;
@@ -181,6 +195,43 @@ specopd_status specopd_tree_attn_fwd(const specopd_tree_attn_desc* desc, const v
   a.rope_base = desc->rope_base > 0.f ? desc->rope_base : 10000.f;
   a.scale = desc->scale > 0.f ? desc->scale : float(1.0 / sqrt(double(desc->D)));
   hipError_t e = launch_tree_attn(*desc, a, stream);
+  return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_prefill_workspace_size(const specopd_prefill_desc* desc, size_t* bytes) {
+  specopd_status st = check_prefill_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!bytes) return SPECOPD_ERR_INVALID_ARGUMENT;
+  *bytes = prefill_ws_layout(*desc).total;
+  return SPECOPD_OK;
+}
+
+specopd_status specopd_prefill_fwd(const specopd_prefill_desc* desc, const void* q, const void* k,
+                                   const void* v, void* cache_k, void* cache_v, void* out,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  specopd_status st = check_prefill_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const void* ptrs[] = {q, k, v, cache_k, cache_v, out};
+  for (const void* p : ptrs)
+    if (!p) return SPECOPD_ERR_INVALID_ARGUMENT;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  // outputs may alias neither an input nor each other
+  const void* outs[] = {cache_k, cache_v, out};
+  for (const void* o : outs) {
+    if (o == q || o == k || o == v) return SPECOPD_ERR_INVALID_ARGUMENT;
+  }
+  if (cache_k == cache_v || cache_k == out || cache_v == out) return SPECOPD_ERR_INVALID_ARGUMENT;
+  const size_t need = prefill_ws_layout(*desc).total;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return SPECOPD_ERR_WORKSPACE;
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v;
+  a.cache_k = cache_k; a.cache_v = cache_v; a.out = out;
+  a.ws = static_cast<char*>(workspace);
+  a.rope_base = desc->rope_base > 0.f ? desc->rope_base : 10000.f;
+  a.scale = desc->scale > 0.f ? desc->scale : float(1.0 / sqrt(double(desc->D)));
+  hipError_t e = launch_prefill(*desc, a, stream);
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
 }
 

@@ -36,6 +36,7 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 # tensor ids for seed derivation
 _T_TRUNK_K, _T_TRUNK_V, _T_Q, _T_K, _T_V, _T_ANCH = 1, 2, 3, 4, 5, 6
 _T_DRAFT, _T_TARGET, _T_PERM, _T_PEAK = 11, 12, 13, 14
+_T_PF_Q, _T_PF_K, _T_PF_V = 21, 22, 23
 
 
 def derive_seed(seed: int, cid: int, tensor: int) -> int:
@@ -94,6 +95,19 @@ def gen_attn(cfg: AttnConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict
     out["parent"] = torch.from_numpy(parent).to(device)
     out["pos"] = torch.from_numpy(pos).to(device)
     return out
+
+
+def gen_prefill(cfg: AttnConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[str, torch.Tensor]:
+    """Trunk-prefill inputs of a workload's trunks: q [T][L][Hq][D] and k, v
+    [T][L][Hkv][D], i.i.d. N(0, 1) rounded to the workload dtype, keys NOT
+    rotated (the prefill rotates them)."""
+    dt = _DT[cfg.dtype]
+    T, L, Hq, Hkv, D = cfg.T, cfg.L, cfg.Hq, cfg.Hkv, cfg.D
+    return {
+        "q": _normal((T * L, Hq, D), dt, device, _gen(device, seed, cid, _T_PF_Q), 8192).view(T, L, Hq, D),
+        "k": _normal((T * L, Hkv, D), dt, device, _gen(device, seed, cid, _T_PF_K), 8192).view(T, L, Hkv, D),
+        "v": _normal((T * L, Hkv, D), dt, device, _gen(device, seed, cid, _T_PF_V), 8192).view(T, L, Hkv, D),
+    }
 
 
 def stress_classes(cfg: LossConfig, seed: int, cid: int) -> np.ndarray:

@@ -162,3 +162,63 @@ def test_status_readback_rejects_bad_workspace_before_gpu():
     e = _edesc()
     assert sd.LIB.specopd_e2etv_device_status(ctypes.byref(e), ctypes.c_void_p(FAKE), 1,
                                               ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE
+
+
+def _pdesc(**kw):
+    base = dict(T=2, L=300, Hq=8, Hkv=2, D=128, dtype=sd.SPECOPD_BF16)
+    base.update(kw)
+    return sd.prefill_desc(**base)
+
+
+def _pcall(desc, ws_bytes=1 << 30, **over):
+    args = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, cache_k=FAKE + 48, cache_v=FAKE + 64,
+                out=FAKE + 80, ws=FAKE + 96)
+    args.update(over)
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_prefill_fwd(
+        ctypes.byref(desc), P(args["q"]), P(args["k"]), P(args["v"]), P(args["cache_k"]),
+        P(args["cache_v"]), P(args["out"]), P(args["ws"]), ctypes.c_size_t(ws_bytes), P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 96, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("D", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("Hq", 7, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("T", -1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("dtype", 5, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("scale", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 300_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # L * Hq beyond 32-bit row indexing
+])
+def test_prefill_desc_errors(field, value, code):
+    d = _pdesc()
+    setattr(d, field, value)
+    assert _pcall(d) == code
+    n = ctypes.c_size_t(0)
+    assert sd.LIB.specopd_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(cache_v=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(out=FAKE + 88), sd.SPECOPD_ERR_INVALID_ARGUMENT),       # misaligned
+    (dict(out=FAKE), sd.SPECOPD_ERR_INVALID_ARGUMENT),            # out aliases q
+    (dict(cache_k=FAKE + 16), sd.SPECOPD_ERR_INVALID_ARGUMENT),   # cache aliases k
+    (dict(cache_v=FAKE + 48), sd.SPECOPD_ERR_INVALID_ARGUMENT),   # the two caches alias
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+])
+def test_prefill_pointer_errors(over, code):
+    assert _pcall(_pdesc(), **over) == code
+
+
+def test_prefill_workspace_size_and_too_small():
+    d = _pdesc()
+    need = sd.specopd_prefill_workspace_size(d)
+    # the rotated, scaled queries of tokens 1..L-1 of every trunk, in bf16
+    assert need >= 2 * 299 * 8 * 128 * 2
+    assert _pcall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+    # a trunk of one token needs no plan
+    assert sd.specopd_prefill_workspace_size(_pdesc(L=1)) < need
+    # fp32 takes the exact per-trunk tree path and its own workspace
+    assert sd.specopd_prefill_workspace_size(_pdesc(dtype=sd.SPECOPD_F32)) > 0

@@ -41,5 +41,6 @@ def test_kernel_timing_records_each_call(gpu_ok):
     sd.tree_attn(ainp, out=out, ws=ws)
     torch.cuda.synchronize()
     assert sd.specopd_kernel_time(0) == (0.0, 0)
+    assert sd.specopd_kernel_time(2) == (0.0, 0)  # prefill: nothing recorded
     with pytest.raises(sd.SpecopdError):
-        sd.specopd_kernel_time(2)
+        sd.specopd_kernel_time(3)
