@@ -10,8 +10,10 @@ over the scored rows (specopd_e2etv_fwd_bwd).
 Prints one JSON line.  `value` is scored branch rows per second through the
 whole step.  `roofline` describes the kernel that takes most of the step,
 timed with HIP events on the stream it runs on; `roofline_attn` /
-`roofline_loss` give both parts.  `cpu_baseline` times the fp64 CPU oracle on
-a bounded sample of the same workload (reported, not a target).
+`roofline_loss` give both parts.  `prefill` measures, separately, the trunk
+prefill that fills the cache (specopd_prefill_fwd) on the workload's trunks.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload (reported, not a target).
 """
 
 from __future__ import annotations
@@ -73,6 +75,65 @@ def measured_traffic(kernel_tag, src_files):
         return None
 
 
+def prefill_flops(cfg):
+    """Algorithmic FLOPs of one trunk's causal prefill: token s reads s + 1
+    keys, 4*D*Hq per (row, key)."""
+    return 4.0 * cfg.D * cfg.Hq * cfg.L * (cfg.L + 1) / 2.0
+
+
+def bench_prefill(sd, wl, seed, steps, warmup, dev, stream):
+    """Trunk prefill of the workload's trunks (specopd_prefill_fwd), timed on
+    its own: it precedes the scoring step and is not part of it."""
+    import torch
+    from synthetic import gen_prefill
+    ac = wl.attn
+    pi = gen_prefill(ac, seed, device=dev, cid=wl.cid)
+    desc = sd.prefill_desc(ac.T, ac.L, ac.Hq, ac.Hkv, ac.D, pi["q"].dtype)
+    ws = sd.workspace(sd.specopd_prefill_workspace_size(desc), dev)
+    out, ck, cv = torch.empty_like(pi["q"]), torch.empty_like(pi["k"]), torch.empty_like(pi["v"])
+
+    def call():
+        sd.specopd_prefill_fwd(desc, pi["q"], pi["k"], pi["v"], ck, cv, out, ws)
+
+    for _ in range(max(1, warmup)):
+        call()
+    n = max(1, min(steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / n
+    sd.specopd_kernel_timing(True)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    tot, cnt = sd.specopd_kernel_time(2)
+    sd.specopd_kernel_timing(False)
+    kern_ms = tot / cnt  # one launch per trunk
+    fl = prefill_flops(ac)
+    tf = fl / (kern_ms / 1e3) / 1e12
+    peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
+    t_pf = measured_traffic(f"prefill_mfma_{wl.name}",
+                            ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
+                             "speculative_decoding_drafter_amd/csrc/device_common.h",
+                             "speculative_decoding_drafter_amd/csrc/internal.h",
+                             "speculative_decoding_drafter_amd/build.py"])
+    return {
+        "metric": "trunk prefill tokens/s", "value": ac.T * ac.L / (call_ms / 1e3),
+        "unit": "tokens/s", "calls": n, "call_ms": call_ms,
+        "config": {"T": ac.T, "L": ac.L, "Hq": ac.Hq, "Hkv": ac.Hkv, "D": ac.D, "dtype": ac.dtype},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": tf / peak,
+                     "traffic": None if t_pf is None else t_pf / (kern_ms / 1e3) / 1e9,
+                     "traffic_unit": "GB/s", "traffic_bytes_per_launch": t_pf,
+                     "kernel": "tree_attn_mfma_kernel<D, true> (specopd_prefill_fwd, one launch per trunk)",
+                     "ms": kern_ms, "alg_flops_per_launch": fl},
+    }
+
+
 def cpu_baseline(wl, attn_inp_cpu, loss_inp_cpu, budget_s=20.0):
     """The fp64 oracle as it stands, single BLAS thread, on a bounded sample:
     whole branches (every node, every head) of attention and their loss rows.
@@ -115,6 +176,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -272,6 +334,9 @@ def main():
     res["roofline_loss"] = roofs["loss"]
     if "attn" in roofs:
         res["roofline_attn"] = roofs["attn"]
+
+    if ai is not None and not args.no_prefill:
+        res["prefill"] = bench_prefill(sd, wl, args.seed, args.steps, args.warmup, dev, stream)
 
     if not args.no_cpu:
         ai_c = {k: v.cpu() for k, v in ai.items()} if ai is not None else None

@@ -103,7 +103,8 @@ inline void mfma_grid(MfmaParams& p) {
   p.nunits = ng * p.ugp;
   p.nwg = (p.nunits + 7) / 8 * 8;
 }
-hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s);
+// prefill: launch the kernel under its prefill name (same code)
+hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s, bool prefill = false);
 
 // ---------------------------------------------------------------- trunk prefill
 // Workspace layout (prefill.hip).  Matrix-core path (bf16):

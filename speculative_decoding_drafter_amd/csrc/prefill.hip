@@ -341,7 +341,7 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
       p.nsplit = g.nsplit;
       mfma_grid(p);
       timing_mark(2, 0, s);
-      e = launch_tree_attn_mfma(d.D, p, s);
+      e = launch_tree_attn_mfma(d.D, p, s, true);
       timing_mark(2, 1, s);
     } else {
       TreeAttnArgs ta{};

@@ -321,7 +321,10 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
   for (int nb = 0; nb < NB; ++nb) lsum[nb] = acc[nb];
 }
 
-template <int D>
+// PREFILL changes nothing in the code: the kernel is instantiated under a
+// second name for trunk prefills, so that profiles attribute tree calls and
+// prefills separately.
+template <int D, bool PREFILL>
 __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(const MfmaParams p) {
   using Gm = Geo<D>;
   constexpr int NB = Gm::NB, OREG = Gm::OREG;
@@ -740,11 +743,21 @@ size_t mfma_slot_bytes(int D) {
   return align_up(size_t(nw) * nb * (D / 32) * 8 * 64 * 4 + size_t(nw) * nb * 128 * 4, 256);
 }
 
-hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s) {
+hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s, bool prefill) {
+  const dim3 grid(p.nwg), block(mfma_waves(D) * 64);
   switch (D) {
-    case 64: tree_attn_mfma_kernel<64><<<p.nwg, mfma_waves(64) * 64, 0, s>>>(p); break;
-    case 128: tree_attn_mfma_kernel<128><<<p.nwg, mfma_waves(128) * 64, 0, s>>>(p); break;
-    case 256: tree_attn_mfma_kernel<256><<<p.nwg, mfma_waves(256) * 64, 0, s>>>(p); break;
+    case 64:
+      if (prefill) tree_attn_mfma_kernel<64, true><<<grid, block, 0, s>>>(p);
+      else tree_attn_mfma_kernel<64, false><<<grid, block, 0, s>>>(p);
+      break;
+    case 128:
+      if (prefill) tree_attn_mfma_kernel<128, true><<<grid, block, 0, s>>>(p);
+      else tree_attn_mfma_kernel<128, false><<<grid, block, 0, s>>>(p);
+      break;
+    case 256:
+      if (prefill) tree_attn_mfma_kernel<256, true><<<grid, block, 0, s>>>(p);
+      else tree_attn_mfma_kernel<256, false><<<grid, block, 0, s>>>(p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
