@@ -69,15 +69,15 @@ __device__ __forceinline__ void lse_update(float& m, float& s, const float (&x)[
 
 // Stream units [u0, u1) of a row (16-byte vectors, or single elements when
 // the row is not 16-byte aligned), pairs (draft, target): thread tid takes
-// u0 + tid + k * kThreads.  Two register batches alternate so the next
+// u0 + tid + k * THREADS.  Two register batches alternate so the next
 // batch's loads are in flight while f() consumes the current one.
-template <bool VECTOR, bool NT, typename F>
+template <bool VECTOR, bool NT, int THREADS = kThreads, int KU = kU, typename F>
 __device__ __forceinline__ void stream_pairs(const void* zrow, const void* trow, int u0, int u1,
                                              int esize, F&& f) {
-  constexpr int STEP = kThreads * kU;
+  constexpr int STEP = THREADS * KU;
   using T = typename std::conditional<VECTOR, u32x4, uint32_t>::type;
   const int base = u0 + int(threadIdx.x);
-  T za[kU], ta[kU], zb[kU], tb[kU];
+  T za[KU], ta[KU], zb[KU], tb[KU];
   auto ld = [&](const void* row, int u) -> T {
     if constexpr (VECTOR) {
       const u32x4* p = reinterpret_cast<const u32x4*>(row) + u;
@@ -88,20 +88,20 @@ __device__ __forceinline__ void stream_pairs(const void* zrow, const void* trow,
                         : reinterpret_cast<const uint32_t*>(row)[u];
     }
   };
-  auto load = [&](T(&z)[kU], T(&t)[kU], int b) {
+  auto load = [&](T(&z)[KU], T(&t)[KU], int b) {
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const int u = b + k * kThreads;
+    for (int k = 0; k < KU; ++k) {
+      const int u = b + k * THREADS;
       if (u < u1) {
         z[k] = ld(zrow, u);
         t[k] = ld(trow, u);
       }
     }
   };
-  auto run = [&](const T(&z)[kU], const T(&t)[kU], int b) {
+  auto run = [&](const T(&z)[KU], const T(&t)[KU], int b) {
 #pragma unroll
-    for (int k = 0; k < kU; ++k) {
-      const int u = b + k * kThreads;
+    for (int k = 0; k < KU; ++k) {
+      const int u = b + k * THREADS;
       if (u < u1) f(z[k], t[k], u);
     }
   };
@@ -210,6 +210,59 @@ struct FusedArgs {
   void* grad;
 };
 
+// Thread 0 of a row's workgroup: publish the row's (alpha, G), count it into
+// its branch, and -- if the row needs the branch (gradient rows, and the
+// branch's first row, which reports the branch) -- wait for every row of the
+// branch, then scan it in fp64: prefix products, suffix sums
+// S_k = 1 + sum over children c of alpha_c S_c, and this row's gradient
+// coefficients s_val[0] (where q < p) and s_val[1] (elsewhere).  Every row
+// of a branch repeats the same tiny scan in the same order.
+__device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j, float al, float g,
+                                           bool need_scan, float* s_val, double* sA, double* sP,
+                                           double* sS) {
+  const bool lead = j == 0;
+  const float qnan = __builtin_nanf("");
+  post_f32(a.segB + size_t(n) * 2 + 0, al);
+  post_f32(a.segB + size_t(n) * 2 + 1, g);
+  post_count(&a.bcount[size_t(r) * kCtrStride]);
+  if (!need_scan) return;
+  bool ok = wait_count(&a.bcount[size_t(r) * kCtrStride], a.Wn, a.spin_limit);
+  const int32_t* par = a.parent + size_t(r) * a.Wn;
+  const float* sb = a.segB + size_t(r) * a.Wn * 2;
+  double sum = 0.0, Gj = 0.0;
+  for (int k = 0; k < a.Wn; ++k) {
+    int pk = par[k];
+    if (pk < -1 || pk >= k) {
+      ok = false;
+      pk = -1;
+    }
+    const float ak = peek_f32(sb + 2 * k), gk = peek_f32(sb + 2 * k + 1);
+    if (k == j) Gj = gk;
+    sA[k] = double(ak);
+    sP[k] = double(ak) * (pk < 0 ? 1.0 : sP[pk]);
+    sS[k] = 1.0;
+    sum += sP[k];
+  }
+  // children come after their parent, so a backward sweep sees them complete
+  for (int k = a.Wn - 1; k >= 0; --k) {
+    const int pk = par[k];
+    if (pk >= 0 && pk < k) sS[pk] += sA[k] * sS[k];
+  }
+  const int pj = par[j];
+  const double pp = (pj >= 0 && pj < j) ? sP[pj] : 1.0;
+  const double c = -double(a.grad_scale) * pp * sS[j] / a.count;
+  s_val[0] = ok ? float(c * (1.0 - Gj)) : qnan;  // coefficient where q < p
+  s_val[1] = ok ? float(-c * Gj) : qnan;         // elsewhere
+  if (!ok) a.branch_ok[r] = 0;
+  if (lead) {
+    a.numer[r] = ok ? sum : double(qnan);
+    for (int k = 0; k < a.Wn; ++k) {
+      if (a.alpha_out) a.alpha_out[size_t(r) * a.Wn + k] = ok ? float(sA[k]) : qnan;
+      if (a.prefix_out) a.prefix_out[size_t(r) * a.Wn + k] = ok ? float(sP[k]) : qnan;
+    }
+  }
+}
+
 __global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ bcount,
                                   int32_t* __restrict__ branch_ok, int R) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -259,7 +312,6 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   const void* trow = static_cast<const char*>(a.target) + row * ESZ;
   const int units = V / NV;  // whole units; a vector row's ragged tail is done element-wise
   const int e0 = units * NV;
-  const float qnan = __builtin_nanf("");
   auto load1 = [&](const void* rowp, int e) -> float {
     if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[e]);
     else return reinterpret_cast<const float*>(rowp)[e];
@@ -304,51 +356,7 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   block_sum2<kThreads>(al, g, red);
 
   // ---- post, wait for the branch, scan
-  const bool lead = j == 0;
-  const bool need_scan = GRAD || lead;
-  if (tid == 0) {
-    post_f32(a.segB + size_t(n) * 2 + 0, al);
-    post_f32(a.segB + size_t(n) * 2 + 1, g);
-    post_count(&a.bcount[size_t(r) * kCtrStride]);
-    if (need_scan) {
-      bool ok = wait_count(&a.bcount[size_t(r) * kCtrStride], a.Wn, a.spin_limit);
-      const int32_t* par = a.parent + size_t(r) * a.Wn;
-      const float* sb = a.segB + size_t(r) * a.Wn * 2;
-      double sum = 0.0, Gj = 0.0;
-      for (int k = 0; k < a.Wn; ++k) {
-        int pk = par[k];
-        if (pk < -1 || pk >= k) {
-          ok = false;
-          pk = -1;
-        }
-        const float ak = peek_f32(sb + 2 * k), gk = peek_f32(sb + 2 * k + 1);
-        if (k == j) Gj = gk;
-        sA[k] = double(ak);
-        sP[k] = double(ak) * (pk < 0 ? 1.0 : sP[pk]);
-        sS[k] = 1.0;
-        sum += sP[k];
-      }
-      // suffix sums S_k = 1 + sum over children c of alpha_c S_c (children
-      // come after their parent, so a backward sweep sees them complete)
-      for (int k = a.Wn - 1; k >= 0; --k) {
-        const int pk = par[k];
-        if (pk >= 0 && pk < k) sS[pk] += sA[k] * sS[k];
-      }
-      const int pj = par[j];
-      const double pp = (pj >= 0 && pj < j) ? sP[pj] : 1.0;
-      const double c = -double(a.grad_scale) * pp * sS[j] / a.count;
-      s_val[0] = ok ? float(c * (1.0 - Gj)) : qnan;  // coefficient where q < p
-      s_val[1] = ok ? float(-c * Gj) : qnan;         // elsewhere
-      if (!ok) a.branch_ok[r] = 0;
-      if (lead) {
-        a.numer[r] = ok ? sum : double(qnan);
-        for (int k = 0; k < a.Wn; ++k) {
-          if (a.alpha_out) a.alpha_out[size_t(r) * a.Wn + k] = ok ? float(sA[k]) : qnan;
-          if (a.prefix_out) a.prefix_out[size_t(r) * a.Wn + k] = ok ? float(sP[k]) : qnan;
-        }
-      }
-    }
-  }
+  if (tid == 0) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val, sA, sP, sS);
   if constexpr (!GRAD) return;
   __syncthreads();
 
@@ -395,6 +403,301 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
     else
       reinterpret_cast<float*>(a.grad)[row + e] = gv;
   }
+}
+
+// ---------------------------------------------------------------- resident rows
+// bf16 logits with 16-byte aligned rows: the same three passes, but most of
+// the row stays on chip between them, so passes B and C re-read only the
+// remainder.  One workgroup of 512 threads fills a CU (its registers and
+// LDS).  Thread tid keeps the 8-element units k * 512 + tid, k < kResUnits,
+// in registers (16-byte loads); the next kResLds blocks of 4096 elements go
+// to LDS straight from memory (16 bytes per lane); the elements past those
+// are streamed in every pass, 4 at a time.  Every gradient store is a
+// contiguous 16 bytes per lane (1 KB per wave), which the memory system
+// writes at full rate (per-lane stores 32 bytes apart do not combine as
+// well): the LDS blocks and the streamed elements are read as quads of 4 in
+// pass C, and the gradients of register units go through a per-wave LDS
+// staging area (the space of the first LDS block, once it is done) that
+// turns 8 consecutive values per lane into 4.  Pass A loads the streamed quads last and passes B and C
+// take them first, so their re-reads find them in L2 while they are the
+// most recently used lines; the resident elements are loaded with a
+// non-temporal hint, which keeps them from pushing the streamed ones out.
+constexpr int kResThreads = 512;
+constexpr int kResUnits = 24;  // 8-element units per thread held in registers (192 VGPRs)
+constexpr int kResLds = 9;     // LDS blocks of 4096 elements (144 KiB)
+constexpr int kResRegElems = kResUnits * kResThreads * 8;
+constexpr int kResElems = kResRegElems + kResLds * 4096;
+constexpr int kStreamBatch = 4;  // streamed loads per thread in flight
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void unpack8(const u32x4& w, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_lo(w[e]);
+    x[2 * e + 1] = bf16_hi(w[e]);
+  }
+}
+__device__ __forceinline__ void unpack4(const u32x2_t& w, float (&x)[4]) {
+  x[0] = bf16_lo(w[0]);
+  x[1] = bf16_hi(w[0]);
+  x[2] = bf16_lo(w[1]);
+  x[3] = bf16_hi(w[1]);
+}
+
+// Makes the compiler treat the resident registers as rewritten, so that each
+// pass unpacks them afresh instead of keeping the fp32 values of an earlier
+// pass alive (twice the registers).
+template <int N>
+__device__ __forceinline__ void reopen(u32x4 (&x)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) asm volatile("" : "+v"(x[k]));
+}
+
+// Raw buffer access: one per-lane offset register serves every quad (the
+// quad's distance goes in the scalar offset).  Callers keep every access
+// inside the row themselves.
+constexpr int kBufFlags = 0x00020000;  // gfx9 raw buffer resource word 3
+constexpr int kNT = 2;                 // non-temporal cache policy
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, kBufFlags);
+}
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ u32x2_t buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+}
+
+// Gradient of elements [e, e + 4) of a row, e = 4 * (quad), through a buffer
+// resource over the row's gradient: 16 bytes (fp32) or 8 bytes (bf16) per lane.
+template <bool GBF16>
+__device__ __forceinline__ void store_grad4(__amdgpu_buffer_rsrc_t r, int e, const float (&gv)[4]) {
+  const int vo = int(threadIdx.x) * (GBF16 ? 8 : 16);
+  const int so = (e - 4 * int(threadIdx.x)) * (GBF16 ? 2 : 4);
+  if constexpr (GBF16) {
+    const u32x2_t w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), r, vo, so, kNT);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{gv[0], gv[1], gv[2], gv[3]}), r,
+                                           vo, so, kNT);
+  }
+}
+
+template <bool GRAD, bool GBF16>
+__global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const FusedArgs a) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  // LDS-resident elements: [block][tensor][4096 elements]
+  __shared__ __attribute__((aligned(16))) uint16_t s_row[kResLds * 2 * 4096];
+  __shared__ float red[4 * (kResThreads / 64)];
+  __shared__ int s_unit;
+  __shared__ float s_val[4];
+  __shared__ double sA[64], sP[64], sS[64];
+
+  const int tid = threadIdx.x, wave = tid >> 6;
+  if (tid == 0)
+    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __syncthreads();
+  // uniform: the row's addresses and buffer resources stay in scalar registers
+  const int n = __builtin_amdgcn_readfirstlane(s_unit);
+  const int r = n / a.Wn;
+  const int j = n - r * a.Wn;
+  const int V = a.V;
+  const size_t row = size_t(n) * size_t(V);
+  const uint16_t* zrow = static_cast<const uint16_t*>(a.draft) + row;
+  const uint16_t* trow = static_cast<const uint16_t*>(a.target) + row;
+  const __amdgpu_buffer_rsrc_t zres = buf_rsrc(zrow, V * 2), tres = buf_rsrc(trow, V * 2);
+  const int sbeg = min(V, kResElems);  // first streamed element (a multiple of 4)
+
+  // first element of register unit k
+  auto reg_e = [&](int k) { return (k * kResThreads + tid) * 8; };
+  // one pass over the streamed elements, W per lane per load (8: 16-byte
+  // loads, 4: quads), kStreamBatch loads per thread at a time, the next
+  // batch in flight while the current one is used.  Every access below is
+  // guarded by the row length (the buffer range check is a second line only)
+  auto stream = [&](auto wtag, auto&& f) {
+    constexpr int W = decltype(wtag)::value;
+    using VT = typename std::conditional<W == 8, u32x4, u32x2_t>::type;
+    constexpr int SB = W == 8 ? kStreamBatch / 2 : kStreamBatch, STEP = kResThreads * W, BSTEP = STEP * SB;
+    if (sbeg + tid * W >= V) return;
+    VT zc[SB], tc[SB], zn[SB], tn[SB];
+    auto load = [&](VT(&z)[SB], VT(&t)[SB], int e0) {
+#pragma unroll
+      for (int i = 0; i < SB; ++i)
+        if (e0 + i * STEP + tid * W < V) {
+          if constexpr (W == 8) {
+            z[i] = buf_load16<0>(zres, tid * 16, (e0 + i * STEP) * 2);
+            t[i] = buf_load16<0>(tres, tid * 16, (e0 + i * STEP) * 2);
+          } else {
+            z[i] = buf_load8<0>(zres, tid * 8, (e0 + i * STEP) * 2);
+            t[i] = buf_load8<0>(tres, tid * 8, (e0 + i * STEP) * 2);
+          }
+        }
+    };
+    load(zc, tc, sbeg);
+    for (int e0 = sbeg; e0 < V; e0 += BSTEP) {
+      load(zn, tn, e0 + BSTEP);
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int e = e0 + i * STEP + tid * W;
+        if (e < V) f(zc[i], tc[i], e);
+      }
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        zc[i] = zn[i];
+        tc[i] = tn[i];
+      }
+    }
+  };
+  using W8 = std::integral_constant<int, 8>;
+  using W4 = std::integral_constant<int, 4>;
+
+  // ---- pass A: load the resident elements, then stream the rest; log-sum-exps
+  u32x4 zr[kResUnits], tr[kResUnits];
+#pragma unroll
+  for (int k = 0; k < kResUnits; ++k)
+    if (reg_e(k) < V) {
+      zr[k] = buf_load16<kNT>(zres, tid * 16, k * kResThreads * 16);
+      tr[k] = buf_load16<kNT>(tres, tid * 16, k * kResThreads * 16);
+    }
+#pragma unroll
+  for (int k = 0; k < kResLds; ++k)
+    if (kResRegElems + k * 4096 + tid * 8 < V) {
+      // straight into LDS; each lane's 16 bytes land at the wave's base + 16 * lane
+      uint16_t* zb = s_row + (2 * k) * 4096 + wave * 512;
+      const int so = (kResRegElems + k * 4096) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zres, (lds_void*)zb, 16, tid * 16, so, 0, kNT);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (lds_void*)(zb + 4096), 16, tid * 16, so, 0, kNT);
+    }
+  float mz = kNegInf, sz = 0.f, mt = kNegInf, st = 0.f;
+  auto lse8 = [&](const u32x4& zw, const u32x4& tw) {
+    float z[8], t[8];
+    unpack8(zw, z);
+    unpack8(tw, t);
+    lse_update<8>(mz, sz, z);
+    lse_update<8>(mt, st, t);
+  };
+#pragma unroll
+  for (int k = 0; k < kResUnits; ++k)
+    if (reg_e(k) < V) lse8(zr[k], tr[k]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS blocks have landed
+  // each thread reads back the 16 bytes its own lane loaded
+  auto lds8 = [&](int k, int x) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(s_row + (2 * k + x) * 4096 + tid * 8);
+  };
+#pragma unroll 1
+  for (int k = 0; k < kResLds; ++k)
+    if (kResRegElems + k * 4096 + tid * 8 < V) lse8(lds8(k, 0), lds8(k, 1));
+  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { lse8(zw, tw); });
+  block_lse2<kResThreads>(mz, sz, mt, st, red);
+  const float nlz = -(mz * kLog2e + log2f(sz));
+  const float nlt = -(mt * kLog2e + log2f(st));
+
+  // ---- pass B: alpha = sum min(q, p), G = sum_{q<p} q; streamed quads first
+  reopen(zr);
+  reopen(tr);
+  float al = 0.f, g = 0.f;
+  auto overlap8 = [&](const u32x4& zw, const u32x4& tw) {
+    float z[8], t[8];
+    unpack8(zw, z);
+    unpack8(tw, t);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float lq, lp;
+      log2probs(z[i], t[i], nlz, nlt, lq, lp);
+      const float e = fast_exp2(fminf(lq, lp));
+      al += e;
+      g += (lq < lp) ? e : 0.f;
+    }
+  };
+  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { overlap8(zw, tw); });
+#pragma unroll
+  for (int k = 0; k < kResUnits; ++k)
+    if (reg_e(k) < V) overlap8(zr[k], tr[k]);
+#pragma unroll 1
+  for (int k = 0; k < kResLds; ++k)
+    if (kResRegElems + k * 4096 + tid * 8 < V) overlap8(lds8(k, 0), lds8(k, 1));
+  block_sum2<kResThreads>(al, g, red);
+
+  // ---- post, wait for the branch, scan
+  if (tid == 0) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val, sA, sP, sS);
+  if constexpr (!GRAD) return;
+  __syncthreads();
+
+  // ---- pass C: gradient, streamed quads first
+  reopen(zr);
+  reopen(tr);
+  const float c1 = s_val[0], c0 = s_val[1];
+  const __amdgpu_buffer_rsrc_t gres =
+      buf_rsrc(static_cast<char*>(a.grad) + row * (GBF16 ? 2 : 4), V * (GBF16 ? 2 : 4));
+  auto grad4 = [&](const u32x2_t& zw, const u32x2_t& tw, int e) {
+    float z[4], t[4], gv[4];
+    unpack4(zw, z);
+    unpack4(tw, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float lq, lp;
+      log2probs(z[i], t[i], nlz, nlt, lq, lp);
+      gv[i] = fast_exp2(lq) * (lq < lp ? c1 : c0);
+    }
+    store_grad4<GBF16>(gres, e, gv);
+  };
+  stream(W4{}, grad4);
+  // LDS blocks, read as quads here (any wave's block: every wave's loads
+  // completed before the barriers of pass B); block 0 first, so that its
+  // space can then stage the register units' gradients
+  auto lds_block = [&](int k) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = h * 2048 + tid * 4;  // element within the block
+      const int e = kResRegElems + k * 4096 + o;
+      if (e < V) {
+        const u32x2_t zw = *reinterpret_cast<const u32x2_t*>(s_row + (2 * k) * 4096 + o);
+        const u32x2_t tw = *reinterpret_cast<const u32x2_t*>(s_row + (2 * k + 1) * 4096 + o);
+        grad4(zw, tw, e);
+      }
+    }
+  };
+  lds_block(0);
+  __syncthreads();  // block 0 is free
+  // register units: a lane's 8 values go to the wave's 2 KB of staging and
+  // come back as two quads, elements [4 l, 4 l + 4) and [256 + 4 l, ...) of
+  // the wave's 512 (LDS operations of one wave complete in order)
+  float* const stage = reinterpret_cast<float*>(s_row) + wave * 512;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int k = 0; k < kResUnits; ++k) {
+    const int w0 = (k * kResThreads + wave * 64) * 8;  // first element of the wave's span
+    if (w0 < V) {
+      float z[4], t[4], gv[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        unpack4(u32x2_t{zr[k][2 * hh], zr[k][2 * hh + 1]}, z);
+        unpack4(u32x2_t{tr[k][2 * hh], tr[k][2 * hh + 1]}, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float lq, lp;
+          log2probs(z[i], t[i], nlz, nlt, lq, lp);
+          gv[4 * hh + i] = fast_exp2(lq) * (lq < lp ? c1 : c0);
+        }
+      }
+      *reinterpret_cast<f32x4*>(stage + lane * 8) = f32x4{gv[0], gv[1], gv[2], gv[3]};
+      *reinterpret_cast<f32x4*>(stage + lane * 8 + 4) = f32x4{gv[4], gv[5], gv[6], gv[7]};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int o = hh * 256 + lane * 4;
+        if (w0 + o < V) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(stage + o);
+          const float q4[4] = {x[0], x[1], x[2], x[3]};
+          store_grad4<GBF16>(gres, w0 + o, q4);
+        }
+      }
+    }
+  }
+#pragma unroll 1
+  for (int k = 1; k < kResLds; ++k) lds_block(k);
 }
 
 constexpr int kFinThreads = 256;
@@ -446,7 +749,14 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.bcount, f.branch_ok, R);
   const unsigned grid = unsigned(N);
   timing_mark(1, 0, s);
-  if (!a.grad)
+  if constexpr (BF16 && VECTOR) {
+    if (!a.grad)
+      e2etv_resident_kernel<false, false><<<grid, kResThreads, 0, s>>>(f);
+    else if (d.grad_dtype == SPECOPD_BF16)
+      e2etv_resident_kernel<true, true><<<grid, kResThreads, 0, s>>>(f);
+    else
+      e2etv_resident_kernel<true, false><<<grid, kResThreads, 0, s>>>(f);
+  } else if (!a.grad)
     e2etv_fused_kernel<BF16, VECTOR, false, false><<<grid, kThreads, 0, s>>>(f);
   else if (d.grad_dtype == SPECOPD_BF16)
     e2etv_fused_kernel<BF16, VECTOR, true, true><<<grid, kThreads, 0, s>>>(f);
