@@ -145,6 +145,19 @@ __device__ __forceinline__ float peek_f32(const float* p) {
 __device__ __forceinline__ void post_f32(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+// 16-byte accesses to a split partial with the same cache policy as the
+// system-scope accesses above (sc0 sc1: stores write through to memory,
+// loads read from it), through a buffer resource over the partial's slot.
+constexpr int kSysPolicy = 1 | 16;  // sc0 | sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const char* slot, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slot), (short)0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ void post16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSysPolicy);
+}
+__device__ __forceinline__ u32x4 peek16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSysPolicy));
+}
 
 // Scores (log2 units) of a staged K tile against this wave's queries, shifted
 // by -m (the product starts from cinit = -m).
@@ -613,18 +626,26 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       auto slot_of = [=](int r2) __attribute__((always_inline)) -> char* {
         return part + (size_t(tg) * ug + u0 + r2) * slot_bytes;
       };
+      // a slot holds each wave's outputs as 16-byte chunks, chunk c of lane l
+      // at ((wave * OCH + c) * 64 + l) * 16 (four bf16 pairs), then the
+      // waves' (m, l) per row block
       constexpr int OWORDS = NB * OREG * 8;  // bf16 pairs per lane
+      constexpr int OCH = OWORDS / 4;
       char* mine = slot_of(rsp);
-      uint32_t* po = reinterpret_cast<uint32_t*>(mine) + wave * OWORDS * 64 + lane;
+      const __amdgpu_buffer_rsrc_t mres = slot_rsrc(mine, slot_bytes);
       float* pm = reinterpret_cast<float*>(mine + Gm::NW * OWORDS * 64 * 4) + wave * NB * 128 + lane;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int db = 0; db < OREG; ++db)
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t w2 = pack_bf16x2(oacc[nb][db][2 * k], oacc[nb][db][2 * k + 1]);
-            post_u32(po + ((nb * OREG + db) * 8 + k) * 64, w2);
+          for (int k4 = 0; k4 < 2; ++k4) {
+            const f32x16& o = oacc[nb][db];
+            const int k = 4 * k4;
+            const u32x4 w = {pack_bf16x2(o[2 * k], o[2 * k + 1]), pack_bf16x2(o[2 * k + 2], o[2 * k + 3]),
+                             pack_bf16x2(o[2 * k + 4], o[2 * k + 5]), pack_bf16x2(o[2 * k + 6], o[2 * k + 7])};
+            const int c = (nb * OREG + db) * 2 + k4;
+            post16(mres, ((wave * OCH + c) * 64 + lane) * 16, w);
           }
         post_f32(pm + nb * 128, lim[nb] == kUnset ? kNegInf : mref[nb]);
         post_f32(pm + nb * 128 + 64, lsum[nb]);
@@ -661,12 +682,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         for (int r0 = 0; r0 < S; r0 += kMergeBatch) {
           bool f[kMergeBatch];
           float m2[kMergeBatch][NB], l2[kMergeBatch][NB];
-          uint32_t wv[kMergeBatch][OWORDS];
+          u32x4 wv[kMergeBatch][OCH];
 #pragma unroll
           for (int e = 0; e < kMergeBatch; ++e) {
             f[e] = present(r0 + e);
             const char* sl = sbase + size_t(f[e] ? r0 + e : rsp) * slot_bytes;
-            const uint32_t* qo = reinterpret_cast<const uint32_t*>(sl) + wave * OWORDS * 64 + lane;
+            const __amdgpu_buffer_rsrc_t sres = slot_rsrc(sl, slot_bytes);
             const float* qm = reinterpret_cast<const float*>(sl + Gm::NW * OWORDS * 64 * 4) + wave * NB * 128 + lane;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -674,7 +695,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
               l2[e][nb] = peek_f32(qm + nb * 128 + 64);
             }
 #pragma unroll
-            for (int x = 0; x < OWORDS; ++x) wv[e][x] = peek_u32(qo + x * 64);
+            for (int c = 0; c < OCH; ++c) wv[e][c] = peek16(sres, ((wave * OCH + c) * 64 + lane) * 16);
           }
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
@@ -697,7 +718,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
               for (int db = 0; db < OREG; ++db)
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
-                  const uint32_t w2 = wv[e][(nb * OREG + db) * 8 + k];
+                  const uint32_t w2 = wv[e][((nb * OREG + db) * 8 + k) >> 2][k & 3];
                   oacc[nb][db][2 * k] += bf16_lo(w2) * a;
                   oacc[nb][db][2 * k + 1] += bf16_hi(w2) * a;
                 }
