@@ -22,8 +22,8 @@
 // flight while the current one is reduced.  Rows are taken in order from an
 // atomic ticket, so a workgroup only waits for rows of its own branch that
 // were claimed just before or after it; the wait is bounded and a timeout
-// marks the branch malformed rather than hanging.  The exchange goes through
-// memory with cache-bypassing accesses (see post_f32).
+// marks the branch malformed rather than hanging.  The exchange uses
+// device-scope relaxed atomic accesses (see post_f32).
 // A small kernel sums the branch numerators in a fixed order (loss).
 // No floating-point atomics: results are bitwise reproducible.
 #include <type_traits>
@@ -164,25 +164,25 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
 
 // Cross-workgroup exchange.  The XCDs' L2 caches are not coherent with each
 // other, and device-scope release/acquire would write back / invalidate a
-// whole L2 per use.  Instead every exchanged word goes through memory with
-// system-scope relaxed accesses (write-through stores, cache-bypassing
-// loads): a workgroup posts its partials, waits until those stores are
-// acknowledged, and only then bumps the counter; a reader that sees the count
-// reads the partials the same cache-bypassing way.
+// whole L2 per use.  Instead every exchanged word is a device-scope relaxed
+// atomic access (individually coherent across the XCDs, no fence): a
+// workgroup posts its partials, waits until those stores are acknowledged,
+// and only then bumps the counter; a reader that sees the count reads the
+// partials the same way.
 __device__ __forceinline__ void post_f32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float peek_f32(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void post_count(int32_t* ctr) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged first
-  __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Bounded wait until *ctr reaches want.  False on timeout.
 __device__ __forceinline__ bool wait_count(int32_t* ctr, int want, int spin_limit) {
   int spins = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) < want) {
+  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
     if (++spins > spin_limit) return false;
     if (spins < 8)  // back off after the first polls
       __builtin_amdgcn_s_sleep(4);
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
 
   const int tid = threadIdx.x;
   if (tid == 0)
-    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int n = s_unit;
   const int r = n / a.Wn;
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
 
   const int tid = threadIdx.x, wave = tid >> 6;
   if (tid == 0)
-    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   // uniform: the row's addresses and buffer resources stay in scalar registers
   const int n = __builtin_amdgcn_readfirstlane(s_unit);

@@ -133,30 +133,28 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ void post_u32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ uint32_t peek_u32(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
+// Split partials and their counters are exchanged across workgroups with
+// device-scope relaxed atomic accesses: individually coherent across the
+// XCDs' L2 caches, with no fence (a device-scope release / acquire would
+// write back or invalidate a whole L2).
 __device__ __forceinline__ float peek_f32(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void post_f32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16-byte accesses to a split partial with the same cache policy as the
-// system-scope accesses above (sc0 sc1: stores write through to memory,
-// loads read from it), through a buffer resource over the partial's slot.
-constexpr int kSysPolicy = 1 | 16;  // sc0 | sc1
+// device-scope accesses above (sc1: coherent across the XCDs of the device),
+// through a buffer resource over the partial's slot.
+constexpr int kDevPolicy = 16;  // sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const char* slot, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(slot), (short)0, int(bytes), 0x00020000);
 }
 __device__ __forceinline__ void post16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSysPolicy);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kDevPolicy);
 }
 __device__ __forceinline__ u32x4 peek16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSysPolicy));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevPolicy));
 }
 
 // Scores (log2 units) of a staged K tile against this wave's queries, shifted
@@ -654,7 +652,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       __syncthreads();
       if (tid == 0) {
         const int old = __hip_atomic_fetch_add(p.ctr + ctr_i, 1, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_SYSTEM);
+                                               __HIP_MEMORY_SCOPE_AGENT);
         *s_last = old == nseg - 1;
       }
       __syncthreads();
