@@ -75,6 +75,41 @@ def test_reduced_workloads(gpu_ok, cid, R, V):
     _check_full(inp, out)
 
 
+@pytest.mark.parametrize("V", [
+    98312,     # the register-resident units and one element-octet into the first LDS block
+    120000,    # LDS blocks partly filled
+    135168,    # exactly the on-chip capacity: nothing streamed
+    135176,    # one octet streamed
+    139264,    # a streamed tail of 4096 elements
+])
+def test_resident_capacity_boundaries(gpu_ok, V):
+    """Row lengths around the on-chip capacity of the resident loss kernel
+    (registers, then LDS blocks, then streamed quads): every element must be
+    counted once, in every pass."""
+    cfg = shrink_loss(WORKLOADS[2].loss, R=2, V=V)
+    inp = gen_loss(cfg, 7, device=DEV, cid=2)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)
+
+
+@pytest.mark.parametrize("cid,V", [(2, 151936), (1, 1000), (2, 10007)])
+def test_forward_only_matches_full_call(gpu_ok, cid, V):
+    """grad = NULL (forward only) gives bitwise the overlaps, prefix products
+    and loss of the full call, for bf16 rows that stay on chip, fp32 rows and
+    unaligned rows."""
+    cfg = shrink_loss(WORKLOADS[cid].loss, R=3, V=V)
+    inp = gen_loss(cfg, 8, device=DEV, cid=cid)
+    full = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    fwd = sd.e2etv(inp["draft"], inp["target"], inp["parent"], grad=False)
+    torch.cuda.synchronize()
+    assert fwd["grad"] is None
+    for key in ("alpha", "prefix", "loss"):
+        assert torch.equal(fwd[key], full[key]), key
+    ref = oracle.e2etv(inp["draft"].cpu(), inp["target"].cpu(), inp["parent"].cpu(), with_grad=False)
+    check_loss(fwd["loss"][0].item(), ref["loss"])
+
+
 def test_fp32_ragged_and_scale_and_count(gpu_ok):
     cfg = shrink_loss(WORKLOADS[1].loss, R=3, V=999)
     inp = gen_loss(cfg, 2, device=DEV, cid=1)
