@@ -184,9 +184,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU: trunks and whole branches would shard across GPUs, "
-              "see the design notes).", file=sys.stderr)
+        print(f"bench.py: the scoring path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(trunks, and whole branches of the loss, would be the units sharded across GPUs; "
+              "only the loss numerators would then be summed across them).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
