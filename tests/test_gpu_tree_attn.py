@@ -125,3 +125,73 @@ def test_full_size_sampled_branches(gpu_ok, cid):
     for (t, b) in picks:
         check_attention(got[t, b], ref[t, b], what=f"branch ({t},{b})")
     assert torch.isfinite(out.float()).all()
+
+
+def _random_tree(rng, Wn):
+    """A random parent map over Wn nodes (each parent precedes its child) and
+    the depths it implies."""
+    parent = [-1] + [int(rng.integers(-1, j)) for j in range(1, Wn)]
+    depth = []
+    for j in range(Wn):
+        d, k = 0, j
+        while parent[k] != -1:
+            k = parent[k]
+            d += 1
+        depth.append(d)
+    return tuple(parent), tuple(depth)
+
+
+def test_sixty_four_node_trees(gpu_ok):
+    """The largest tree a branch may hold (all 64 bits of the ancestor mask),
+    random shapes, on the matrix-core path (one query head per kv head keeps a
+    branch's 64 rows inside one workgroup)."""
+    parent, depth = _random_tree(np.random.default_rng(11), 64)
+    cfg = shrink_attn(WORKLOADS[2].attn, L=400, P=100, B=5, Hq=2, Hkv=2, parent=parent, depth=depth)
+    inp = gen_attn(cfg, 9, device=DEV, cid=2)
+    out, desc, ws = _run(inp)
+    assert sd.specopd_tree_attn_device_status(desc, ws) == 0
+    check_attention(out.float().cpu().numpy(), _ref(inp))
+
+
+def test_rows_beyond_one_workgroup_take_the_vector_path(gpu_ok):
+    """A branch of 64 nodes with 8 query heads per kv head has 512 rows, more
+    than one matrix-core workgroup holds: the bf16 inputs take the vector
+    path, which must agree just the same."""
+    parent, depth = _random_tree(np.random.default_rng(12), 64)
+    cfg = shrink_attn(WORKLOADS[2].attn, L=200, P=50, B=2, Hq=8, Hkv=1, parent=parent, depth=depth)
+    inp = gen_attn(cfg, 10, device=DEV, cid=2)
+    out, desc, ws = _run(inp)
+    assert sd.specopd_tree_attn_device_status(desc, ws) == 0
+    check_attention(out.float().cpu().numpy(), _ref(inp))
+
+
+def test_anchors_at_the_trunk_ends(gpu_ok):
+    """Anchors 0 (a branch that sees one trunk key) and L-1 (the whole trunk,
+    ending mid-tile) next to ordinary ones."""
+    cfg = shrink_attn(WORKLOADS[2].attn, L=301, P=0, B=4)
+    inp = gen_attn(cfg, 11, device=DEV, cid=2)
+    a = torch.tensor([[0, 300, 150, 1]], dtype=torch.int32, device=DEV)
+    inp["anchors"] = a
+    depth = torch.tensor(cfg.depth, dtype=torch.int32, device=DEV)
+    inp["pos"] = (a[:, :, None] + 1 + depth[None, None, :]).to(torch.int32).contiguous()
+    out, desc, ws = _run(inp)
+    assert sd.specopd_tree_attn_device_status(desc, ws) == 0
+    check_attention(out.float().cpu().numpy(), _ref(inp))
+
+
+def test_more_branches_than_the_staged_plan(gpu_ok):
+    """More branches per trunk than the preparation kernel plans in LDS (the
+    global-memory planning and sort path), checked on sampled branches."""
+    parent, depth = (-1, 0), (0, 1)
+    cfg = shrink_attn(WORKLOADS[2].attn, L=2600, P=100, B=2300, Hq=8, Hkv=2, parent=parent, depth=depth)
+    inp = gen_attn(cfg, 12, device=DEV, cid=2)
+    out, desc, ws = _run(inp)
+    assert sd.specopd_tree_attn_device_status(desc, ws) == 0
+    anch = inp["anchors"][0].cpu().numpy()
+    rng = np.random.default_rng(13)
+    picks = sorted({(0, int(b)) for b in rng.choice(2300, size=12, replace=False)} |
+                   {(0, int(anch.argmax())), (0, int(anch.argmin()))})
+    ref = _ref(inp, branches=picks)
+    got = out.float().cpu().numpy()
+    for (t, b) in picks:
+        check_attention(got[t, b], ref[t, b], what=f"branch {b}")
