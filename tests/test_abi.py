@@ -222,3 +222,24 @@ def test_prefill_workspace_size_and_too_small():
     assert sd.specopd_prefill_workspace_size(_pdesc(L=1)) < need
     # fp32 takes the exact per-trunk tree path and its own workspace
     assert sd.specopd_prefill_workspace_size(_pdesc(dtype=sd.SPECOPD_F32)) > 0
+
+
+def _declared_arities():
+    """Parameter count of every function include/specopd.h declares."""
+    src = re.sub(r"/\*.*?\*/", "", open(HDR).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(specopd_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", src):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else len(params.split(","))
+    return out
+
+
+def test_binding_argument_counts_match_the_header():
+    """The ctypes signatures the binding sets agree with the header's
+    parameter lists (a wrong count would pass garbage through the ABI)."""
+    ar = _declared_arities()
+    assert set(ar) == set(_lib.EXPORTS)
+    for name, n in ar.items():
+        fn = getattr(sd.LIB, name)
+        assert fn.argtypes is not None, name
+        assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
