@@ -3,7 +3,9 @@
 A step is the whole hot path over one batch of synthetic inputs already
 resident in HBM: tree-masked attention of every branch node against the trunk
 cache (specopd_tree_attn_fwd), then the E2E-TV surrogate forward and gradient
-over the scored rows (specopd_e2etv_fwd_bwd).
+over the scored rows (specopd_e2etv_fwd_bwd).  The timed steps replay the step
+captured once as a HIP graph (every kernel of both calls runs in every
+replay); --eager times plain calls, and the JSON line carries both.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
@@ -73,6 +75,30 @@ def measured_traffic(kernel_tag, src_files):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def time_graph(step, stream, steps):
+    """ms per step over `steps` replays of step() captured as one HIP graph
+    (warmed up on a side stream first, one untimed replay)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step(None)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None)
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) / steps
 
 
 def prefill_flops(cfg):
@@ -179,6 +205,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain calls instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -278,7 +306,20 @@ def main():
         raise SystemExit("tree attention reported malformed branches")
     if sd.specopd_e2etv_device_status(ldesc, lws) != 0:
         raise SystemExit("E2E-TV reported malformed or timed-out branches")
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    eager_ms_step = t_start.elapsed_time(t_end) / args.steps
+    # The timed steps: the whole step (every kernel of both calls) captured
+    # once as a HIP graph and replayed, which removes the host launch gaps
+    # between its kernels; --eager times the plain calls instead (above, with
+    # per-call events).
+    graph_ms_step = None
+    graph_note = None
+    if not args.eager:
+        try:
+            graph_ms_step = time_graph(step, stream, args.steps)
+        except RuntimeError as exc:  # capture refused: the eager timing stands
+            torch.cuda.synchronize()
+            graph_note = f"graph capture failed ({exc}); eager calls timed"
+    ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if ai is not None else 0.0
     loss_call_ms = float(np.mean([(e[1] if ai is not None else e[0]).elapsed_time(e[2]) for e in evs])) \
         if ai is not None else float(np.mean([t_start.elapsed_time(t_end) / args.steps]))
@@ -292,7 +333,10 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if lc.dtype == "bf16" else "f32", "data": "synthetic",
+        "graph": graph_ms_step is not None, "eager_ms_per_step": eager_ms_step,
     }
+    if graph_note:
+        res["graph_note"] = graph_note
     conf = {"workload": f"{wl.name} (workload {wl.cid})", "scored_rows": N,
             "loss": {"R": lc.R, "Wn": lc.Wn, "V": lc.V, "logits": lc.dtype, "grad": "f32"}}
     lb = loss_bytes(lc)
