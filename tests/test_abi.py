@@ -243,3 +243,24 @@ def test_binding_argument_counts_match_the_header():
         fn = getattr(sd.LIB, name)
         assert fn.argtypes is not None, name
         assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
+
+
+def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
+    """include/specopd.h compiles as C99 with warnings as errors, and a C
+    program linked against libspecopd.so gets the documented statuses."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = os.path.join(root, "tests", "c", "abi_errors.c")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = str(tmp_path / "abi_errors")
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-I", os.path.join(root, "include"), src, "-o", exe,
+                        "-L", libdir, "-lspecopd", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
