@@ -94,11 +94,6 @@ struct Geo {
   static constexpr int INFL = NBUF - 1 - NEED;
 };
 
-__device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-}
-
 // Visible tail keys of a row within tail tile [tau0, tau0 + 32): the row's own
 // branch occupies tail keys slot*Wn .. slot*Wn + Wn - 1 and it sees the nodes
 // set in its ancestor mask.  Bit q of the result = tail key tau0 + q.
@@ -462,7 +457,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     for (int q = 0; q < AH; ++q)
       if (q < n) DMA_TILE(v0 + q, q);
     // ---- this lane's rows: metadata and the Q^T operand
-    int ra[NB], rslot[NB];
+    int ra[NB], rslot[NB], rbr[NB];  // anchor, pack slot and branch of each row block's row
+    bool rok[NB];                     // the row's branch is well formed
     uint64_t rmask[NB];
     bf16x8 qop[NB][D / 16];
     int wmin = 0x7fffffff;
@@ -480,6 +476,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         const bool ok = exists && p.branch_ok[tB + b];
         ra[nb] = ok ? p.anchors[tB + b] : ntrunk * KT - 1;  // rows without output never force a mask
         rslot[nb] = slot;
+        rbr[nb] = b;
+        rok[nb] = ok;
         rmask[nb] = ok ? p.anc[(tB + b) * p.Wn + j] : 0ull;
         wmin = min(wmin, ra[nb]);
         const uint16_t* qrow = qb + ((b * p.Wn + j) * p.Hq + hh) * D;
@@ -735,8 +733,8 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         const int within = rho - slot * rows_per_branch;
         const int j = within / p.G;
         const int hh = within - j * p.G;
-        const size_t b = size_t(ord[b0 + slot]);
-        const bool ok = p.branch_ok[tB + b] != 0;
+        const size_t b = size_t(rbr[nb]);  // kept from the setup: no reload at the end
+        const bool ok = rok[nb];
         const float inv = ok ? 1.0f / lt : __builtin_nanf("");
         uint16_t* orow = p.out + (tB * p.Wn * p.Hq + size_t(g) * p.G) * D +
                          ((int(b) * p.Wn + j) * p.Hq + hh) * D;
