@@ -8,17 +8,19 @@
 // the prefix products, gradient through q only.
 //
 // One fused kernel, one workgroup per row (row n = branch r, node j):
-//   pass A   stream the row: log-sum-exp of draft and target;
-//   pass B   stream it again (the caches serve it: it was just read):
-//            alpha = sum min(q, p) and G = sum_{q<p} q;
+//   pass A   read the row: log-sum-exp of draft and target;
+//   pass B   alpha = sum min(q, p) and G = sum_{q<p} q;
 //   post     publish (alpha, G) and count the row into its branch;
 //   scan     once every row of the branch has posted, compute prefix
 //            products, suffix sums S and this row's coefficient
 //            c = grad_scale * dLoss/dalpha in fp64 (every row of a branch
 //            repeats the same tiny scan in the same order);
-//   pass C   stream the row a third time and write
-//            grad[u] = c * q_u * ([q_u < p_u] - G).
-// Loads are software-pipelined: the next batch of 16-byte vectors is in
+//   pass C   write grad[u] = c * q_u * ([q_u < p_u] - G).
+// Two forms.  e2etv_resident_kernel (bf16 logits, 16-byte aligned rows)
+// keeps most of the row in registers and LDS from pass A to pass C, so each
+// row is read from memory about once (see the resident-rows section).
+// e2etv_fused_kernel (fp32 logits or unaligned rows) streams the row in every
+// pass with software-pipelined loads: the next batch of 16-byte vectors is in
 // flight while the current one is reduced.  Rows are taken in order from an
 // atomic ticket, so a workgroup only waits for rows of its own branch that
 // were claimed just before or after it; the wait is bounded and a timeout

@@ -16,14 +16,17 @@
 // tiles masked by the ancestor bitmask and by branch identity.  A pack's key
 // tiles (trunk tiles, then tail tiles) are its units of work.
 //
-// Work split.  A workgroup takes one pack, or one of `nsplit` key ranges of a
-// pack when there are too few packs to fill the chip.  A split pack leaves
-// partial results (unnormalised output in bf16, running max and sum in fp32)
-// in the workspace; the workgroup that finishes last merges them in split
-// order, so the result does not depend on timing.  Packs of one kv head are
+// Work split.  A workgroup takes one pack, or one key range of a pack when
+// there are too few packs to fill the chip; packs get key ranges in
+// proportion to their key tiles (at least one each), so ranges are of like
+// length.  A split pack leaves partial results (unnormalised output in bf16,
+// running max and sum in fp32) in the workspace, exchanged with device-scope
+// accesses; the workgroup that finishes last merges them in range order, so
+// the result does not depend on timing.  Packs of one kv head are
 // consecutive units and run side by side on one XCD, reading the same trunk
 // tiles at about the same time, so the trunk is fetched into that XCD's L2
-// about once.
+// about once.  The trunk prefill launches this same kernel (under a second
+// name) on one-node branches, one per trunk token.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16, lane l = r + 32h):
 //   S^T[key][row] = K[key][:] . Q[row][:]      A = K tile (LDS, 16-byte
@@ -44,7 +47,7 @@
 // the products with V of tile i follow, during which the K operands of tile
 // i + 2 are read.  Tiles go from global memory straight into LDS
 // (global_load_lds: each lane of a wave-wide load writes 16 bytes at base +
-// 16 * lane), through five LDS buffers (four for head size 256), one barrier
+// 16 * lane), through six LDS buffers (four for head size 256), one barrier
 // per tile.  Lanes whose 16 bytes land on a row's pad chunk load a harmless
 // in-bounds chunk that is never read.  Tiles that need no mask for any row
 // of the wave run through a branch-free copy of the step.
