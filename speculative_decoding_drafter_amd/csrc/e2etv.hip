@@ -69,6 +69,26 @@ __device__ __forceinline__ void lse_update(float& m, float& s, const float (&x)[
   }
 }
 
+// The same update with the reference moved only when it must be: the group
+// is summed against the current reference m first, and that sum is kept
+// unless it exceeds 2^64 (a value more than 64 binary orders of magnitude
+// above m), is NaN or infinite (m still -inf, or infinite logits); then the
+// group is redone by the exact update above.  s stays a sum of terms scaled
+// by 2^(-m log2 e), so the log-sum-exp m + ln s is unchanged, and the common
+// case needs no maximum and no rescaling.
+constexpr float kLazyLimit = 0x1p64f;
+template <int NV>
+__device__ __forceinline__ void lse_update_lazy(float& m, float& s, const float (&x)[NV]) {
+  const float nm = -m * kLog2e;
+  float acc = fast_exp2(__builtin_fmaf(x[0], kLog2e, nm));
+#pragma unroll
+  for (int i = 1; i < NV; ++i) acc += fast_exp2(__builtin_fmaf(x[i], kLog2e, nm));
+  if (__builtin_expect(acc <= kLazyLimit, 1))
+    s += acc;
+  else
+    lse_update<NV>(m, s, x);
+}
+
 // Stream units [u0, u1) of a row (16-byte vectors, or single elements when
 // the row is not 16-byte aligned), pairs (draft, target): thread tid takes
 // u0 + tid + k * THREADS.  Two register batches alternate so the next
@@ -212,55 +232,83 @@ struct FusedArgs {
   void* grad;
 };
 
-// Thread 0 of a row's workgroup: publish the row's (alpha, G), count it into
-// its branch, and -- if the row needs the branch (gradient rows, and the
-// branch's first row, which reports the branch) -- wait for every row of the
-// branch, then scan it in fp64: prefix products, suffix sums
-// S_k = 1 + sum over children c of alpha_c S_c, and this row's gradient
-// coefficients s_val[0] (where q < p) and s_val[1] (elsewhere).  Every row
-// of a branch repeats the same tiny scan in the same order.
+// Lane k of a wave holds node k of a branch (Wn <= 64).  Uniform-index
+// reads of another lane's value.
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  const unsigned long long u = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane(unsigned(u), l);
+  const unsigned hi = __builtin_amdgcn_readlane(unsigned(u >> 32), l);
+  return __longlong_as_double((static_cast<unsigned long long>(hi) << 32) | lo);
+}
+
+// The first wave of a row's workgroup (all 64 lanes): publish the row's
+// (alpha, G), count it into its branch, and -- if the row needs the branch
+// (gradient rows, and the branch's first row, which reports the branch) --
+// wait for every row of the branch, then scan it in fp64: prefix products
+// P_k = alpha_k P_parent, suffix sums S_k = 1 + sum over children c of
+// alpha_c S_c, and this row's gradient coefficients s_val[0] (where q < p)
+// and s_val[1] (elsewhere).  The branch's rows are read one per lane in a
+// single round trip; the scan walks the nodes in index order (children come
+// after their parents) with every value held by its node's lane, so every
+// row of a branch does the same arithmetic in the same order.
 __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j, float al, float g,
-                                           bool need_scan, float* s_val, double* sA, double* sP,
-                                           double* sS) {
-  const bool lead = j == 0;
+                                           bool need_scan, float* s_val) {
+  const int lane = int(threadIdx.x) & 63;
   const float qnan = __builtin_nanf("");
-  post_f32(a.segB + size_t(n) * 2 + 0, al);
-  post_f32(a.segB + size_t(n) * 2 + 1, g);
-  post_count(&a.bcount[size_t(r) * kCtrStride]);
+  int32_t* const ctr = &a.bcount[size_t(r) * kCtrStride];
+  if (lane == 0) {
+    post_f32(a.segB + size_t(n) * 2 + 0, al);
+    post_f32(a.segB + size_t(n) * 2 + 1, g);
+    post_count(ctr);
+  }
   if (!need_scan) return;
-  bool ok = wait_count(&a.bcount[size_t(r) * kCtrStride], a.Wn, a.spin_limit);
-  const int32_t* par = a.parent + size_t(r) * a.Wn;
-  const float* sb = a.segB + size_t(r) * a.Wn * 2;
-  double sum = 0.0, Gj = 0.0;
-  for (int k = 0; k < a.Wn; ++k) {
-    int pk = par[k];
-    if (pk < -1 || pk >= k) {
-      ok = false;
+  bool lok = true;
+  if (lane == 0) lok = wait_count(ctr, a.Wn, a.spin_limit);
+  // read after the wait (the loads follow the spin in program order)
+  const int Wn = a.Wn;
+  int pk = -1;
+  double ak = 0.0;
+  float gk = 0.f;
+  if (lane < Wn) {
+    pk = a.parent[size_t(r) * Wn + lane];
+    if (pk < -1 || pk >= lane) {
+      lok = false;
       pk = -1;
     }
-    const float ak = peek_f32(sb + 2 * k), gk = peek_f32(sb + 2 * k + 1);
-    if (k == j) Gj = gk;
-    sA[k] = double(ak);
-    sP[k] = double(ak) * (pk < 0 ? 1.0 : sP[pk]);
-    sS[k] = 1.0;
-    sum += sP[k];
+    const float* sb = a.segB + (size_t(r) * Wn + lane) * 2;
+    ak = double(peek_f32(sb));
+    gk = peek_f32(sb + 1);
   }
-  // children come after their parent, so a backward sweep sees them complete
-  for (int k = a.Wn - 1; k >= 0; --k) {
-    const int pk = par[k];
-    if (pk >= 0 && pk < k) sS[pk] += sA[k] * sS[k];
+  const bool ok = __builtin_amdgcn_ballot_w64(!lok) == 0;
+  double P = 0.0, sum = 0.0;
+  for (int k = 0; k < Wn; ++k) {
+    const int pkk = __builtin_amdgcn_readlane(pk, k);
+    const double Pk = lane_f64(ak, k) * (pkk < 0 ? 1.0 : lane_f64(P, pkk));
+    if (lane == k) P = Pk;
+    sum += Pk;
   }
-  const int pj = par[j];
-  const double pp = (pj >= 0 && pj < j) ? sP[pj] : 1.0;
-  const double c = -double(a.grad_scale) * pp * sS[j] / a.count;
-  s_val[0] = ok ? float(c * (1.0 - Gj)) : qnan;  // coefficient where q < p
-  s_val[1] = ok ? float(-c * Gj) : qnan;         // elsewhere
-  if (!ok) a.branch_ok[r] = 0;
-  if (lead) {
-    a.numer[r] = ok ? sum : double(qnan);
-    for (int k = 0; k < a.Wn; ++k) {
-      if (a.alpha_out) a.alpha_out[size_t(r) * a.Wn + k] = ok ? float(sA[k]) : qnan;
-      if (a.prefix_out) a.prefix_out[size_t(r) * a.Wn + k] = ok ? float(sP[k]) : qnan;
+  double S = 1.0;
+  for (int k = Wn - 1; k > 0; --k) {
+    const int pkk = __builtin_amdgcn_readlane(pk, k);
+    if (pkk >= 0) {
+      const double v = lane_f64(ak, k) * lane_f64(S, k);
+      if (lane == pkk) S += v;
+    }
+  }
+  const int pj = __builtin_amdgcn_readlane(pk, j);
+  const double pp = pj >= 0 ? lane_f64(P, pj) : 1.0;
+  const double Gj = double(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gk), j)));
+  const double c = -double(a.grad_scale) * pp * lane_f64(S, j) / a.count;
+  if (lane == 0) {
+    s_val[0] = ok ? float(c * (1.0 - Gj)) : qnan;  // coefficient where q < p
+    s_val[1] = ok ? float(-c * Gj) : qnan;         // elsewhere
+    if (!ok) a.branch_ok[r] = 0;
+  }
+  if (j == 0) {
+    if (lane == 0) a.numer[r] = ok ? sum : double(qnan);
+    if (lane < Wn) {
+      if (a.alpha_out) a.alpha_out[size_t(r) * Wn + lane] = ok ? float(ak) : qnan;
+      if (a.prefix_out) a.prefix_out[size_t(r) * Wn + lane] = ok ? float(P) : qnan;
     }
   }
 }
@@ -299,7 +347,6 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   __shared__ float red[4 * (kThreads / 64)];
   __shared__ int s_unit;
   __shared__ float s_val[4];
-  __shared__ double sA[64], sP[64], sS[64];
 
   const int tid = threadIdx.x;
   if (tid == 0)
@@ -328,8 +375,8 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
       z[i] = U::get(zw, i);
       t[i] = U::get(tw, i);
     }
-    lse_update<NV>(mz, sz, z);
-    lse_update<NV>(mt, st, t);
+    lse_update_lazy<NV>(mz, sz, z);
+    lse_update_lazy<NV>(mt, st, t);
   });
   for (int e = e0 + tid; e < V; e += kThreads) {
     float z[1] = {load1(zrow, e)}, t[1] = {load1(trow, e)};
@@ -358,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   block_sum2<kThreads>(al, g, red);
 
   // ---- post, wait for the branch, scan
-  if (tid == 0) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val, sA, sP, sS);
+  if (tid < 64) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val);
   if constexpr (!GRAD) return;
   __syncthreads();
 
@@ -496,7 +543,6 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   __shared__ float red[4 * (kResThreads / 64)];
   __shared__ int s_unit;
   __shared__ float s_val[4];
-  __shared__ double sA[64], sP[64], sS[64];
 
   const int tid = threadIdx.x, wave = tid >> 6;
   if (tid == 0)
@@ -578,8 +624,8 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
     float z[8], t[8];
     unpack8(zw, z);
     unpack8(tw, t);
-    lse_update<8>(mz, sz, z);
-    lse_update<8>(mt, st, t);
+    lse_update_lazy<8>(mz, sz, z);
+    lse_update_lazy<8>(mt, st, t);
   };
 #pragma unroll
   for (int k = 0; k < kResUnits; ++k)
@@ -624,7 +670,7 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   block_sum2<kResThreads>(al, g, red);
 
   // ---- post, wait for the branch, scan
-  if (tid == 0) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val, sA, sP, sS);
+  if (tid < 64) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val);
   if constexpr (!GRAD) return;
   __syncthreads();
 
