@@ -206,10 +206,10 @@ __device__ __forceinline__ bool wait_count(int32_t* ctr, int want, int spin_limi
   int spins = 0;
   while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
     if (++spins > spin_limit) return false;
-    if (spins < 8)  // back off after the first polls
-      __builtin_amdgcn_s_sleep(4);
+    if (spins < 32)  // back off after the first polls
+      __builtin_amdgcn_s_sleep(2);
     else
-      __builtin_amdgcn_s_sleep(32);
+      __builtin_amdgcn_s_sleep(8);
   }
   return true;
 }

@@ -147,6 +147,37 @@ def test_neg_inf_logits_and_eq13(gpu_ok):
     _check_full(inp, outb)
 
 
+@pytest.mark.parametrize("logits", ["fp32", "bf16"])
+def test_log_sum_exp_reference_moves(gpu_ok, logits):
+    """Rows whose logits climb far above every earlier value (ramps over
+    [-300, 300], a lone spike of +400 at the last element, a row shifted
+    by +150, a row of -inf but for its last element): the log-sum-exp's
+    running reference has to move many times, by more than the fp32
+    exponent range, without overflow, and still match the oracle."""
+    V = 151936 if logits == "bf16" else 20480
+    cfg = shrink_loss(WORKLOADS[2].loss, R=1, V=V)
+    inp = gen_loss(cfg, 9, device="cpu", cid=2)
+    z = inp["draft"].float().clone()
+    t = inp["target"].float().clone()
+    ramp = torch.linspace(-300.0, 300.0, V)
+    z[0, 0] = ramp
+    t[0, 0] = ramp.flip(0)
+    z[0, 1, -1] = 400.0
+    t[0, 2] = t[0, 2] + 150.0
+    z[0, 3] = float("-inf")
+    z[0, 3, -1] = 0.0
+    t[0, 4, : V // 2] = ramp[V // 2:]
+    dt = torch.bfloat16 if logits == "bf16" else torch.float32
+    # every node a child of the anchor, so each row's gradient has its own
+    # coefficient (a chain through the ramp row would scale them all to ~0)
+    par = torch.full_like(inp["parent"], -1)
+    cpu = {"draft": z.to(dt), "target": t.to(dt), "parent": par}
+    out = sd.e2etv(cpu["draft"].to(DEV), cpu["target"].to(DEV), cpu["parent"].to(DEV))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out["alpha"]).all() and torch.isfinite(out["grad"]).all()
+    _check_full(cpu, out)
+
+
 def test_malformed_parent_flags_branch(gpu_ok):
     cfg = shrink_loss(WORKLOADS[2].loss, R=4, V=4096)
     inp = gen_loss(cfg, 4, device=DEV, cid=2)
