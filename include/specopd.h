@@ -242,8 +242,8 @@ specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
  * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd,
  * specopd_e2etv_fwd_bwd and specopd_prefill_fwd call record a pair of HIP
  * events on its stream around each launch of its main kernel (the attention
- * kernel proper, after the preparation kernel; the fused E2E-TV kernel,
- * without the small zero and finalize kernels; the attention kernel of each
+ * kernel proper, after the preparation kernel; the E2E-TV kernel, without
+ * the small kernel that clears its counters; the attention kernel of each
  * prefilled trunk), so that a harness can divide a kernel's algorithmic work
  * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is

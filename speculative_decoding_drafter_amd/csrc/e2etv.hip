@@ -26,7 +26,8 @@
 // were claimed just before or after it; the wait is bounded and a timeout
 // marks the branch malformed rather than hanging.  The exchange uses
 // device-scope relaxed atomic accesses (see post_f32).
-// A small kernel sums the branch numerators in a fixed order (loss).
+// The branch that reports last sums the branch numerators in a fixed order
+// (loss), so no further kernel runs after the rows.
 // No floating-point atomics: results are bitwise reproducible.
 #include <type_traits>
 
@@ -197,6 +198,12 @@ __device__ __forceinline__ void post_f32(float* p, float v) {
 __device__ __forceinline__ float peek_f32(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void post_f64(double* p, double v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double peek_f64(const double* p) {
+  return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void post_count(int32_t* ctr) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged first
   __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -225,7 +232,10 @@ struct FusedArgs {
   float* segB;      // [N][2] (alpha, G) of every row
   int32_t* bcount;  // [R] rows of each branch that posted
   int32_t* ticket;
+  int32_t* done;    // branches that reported their numerator
+  int R;
   double* numer;
+  double* loss_out;  // loss, numerator sum, count
   int32_t* branch_ok;
   float* alpha_out;
   float* prefix_out;
@@ -305,18 +315,42 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
     if (!ok) a.branch_ok[r] = 0;
   }
   if (j == 0) {
-    if (lane == 0) a.numer[r] = ok ? sum : double(qnan);
     if (lane < Wn) {
       if (a.alpha_out) a.alpha_out[size_t(r) * Wn + lane] = ok ? float(ak) : qnan;
       if (a.prefix_out) a.prefix_out[size_t(r) * Wn + lane] = ok ? float(P) : qnan;
     }
+    // report the branch's numerator; the branch that reports last (its
+    // count is the R-th) reads them all back and writes the loss
+    int last = 0;
+    if (lane == 0) {
+      post_f64(&a.numer[r], ok ? sum : double(qnan));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // numerator acknowledged first
+      last = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.R - 1;
+    }
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      // lane l adds branches l, l + 64, ... in order, then a butterfly over
+      // the wave (both lanes of a pair add the same two values, so every lane
+      // ends with the same sum, in an order fixed by the branch indices)
+      double t = 0.0;
+      for (int b = lane; b < a.R; b += 64) t += peek_f64(&a.numer[b]);
+#pragma unroll
+      for (int w = 32; w >= 1; w >>= 1) t += __shfl_xor(t, w, 64);
+      if (lane == 0) {
+        a.loss_out[0] = 1.0 - t / a.count;
+        a.loss_out[1] = t;
+        a.loss_out[2] = a.count;
+      }
+    }
   }
 }
 
-__global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ bcount,
-                                  int32_t* __restrict__ branch_ok, int R) {
+__global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ done,
+                                  int32_t* __restrict__ bcount, int32_t* __restrict__ branch_ok, int R) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) *ticket = 0;
+  if (i == 0) {
+    *ticket = 0;
+    *done = 0;
+  }
   if (i < R) {
     bcount[size_t(i) * kCtrStride] = 0;
     branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
@@ -748,30 +782,6 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   for (int k = 1; k < kResLds; ++k) lds_block(k);
 }
 
-constexpr int kFinThreads = 256;
-
-__global__ __launch_bounds__(kFinThreads) void e2etv_finalize_kernel(const double* __restrict__ numer,
-                                                                     int R, double count,
-                                                                     double* __restrict__ loss_out) {
-  __shared__ double red[kFinThreads];
-  double s = 0.0;
-  for (int r = threadIdx.x; r < R; r += kFinThreads) s += numer[r];
-  red[threadIdx.x] = s;
-  __syncthreads();
-  for (int w = kFinThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double tot = red[0];
-    loss_out[0] = 1.0 - tot / count;
-    loss_out[1] = tot;
-    loss_out[2] = count;
-  }
-}
-
-
-
 template <bool BF16, bool VECTOR>
 hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s, int spin_limit) {
   const E2etvWs L = e2etv_ws_layout(d);
@@ -789,12 +799,15 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.segB = reinterpret_cast<float*>(a.ws + L.segB);
   f.bcount = reinterpret_cast<int32_t*>(a.ws + L.bcount);
   f.ticket = reinterpret_cast<int32_t*>(a.ws + L.ticket);
+  f.done = f.ticket + 32;  // the next 128-byte line of the ticket's block
+  f.R = R;
   f.numer = reinterpret_cast<double*>(a.ws + L.numer);
+  f.loss_out = a.loss_out;
   f.branch_ok = reinterpret_cast<int32_t*>(a.ws + L.branch_ok);
   f.alpha_out = a.alpha_out;
   f.prefix_out = a.prefix_out;
   f.grad = a.grad;
-  e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.bcount, f.branch_ok, R);
+  e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.done, f.bcount, f.branch_ok, R);
   const unsigned grid = unsigned(N);
   timing_mark(1, 0, s);
   if constexpr (BF16 && VECTOR) {
@@ -811,7 +824,6 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   else
     e2etv_fused_kernel<BF16, VECTOR, true, false><<<grid, kThreads, 0, s>>>(f);
   timing_mark(1, 1, s);
-  e2etv_finalize_kernel<<<1, kFinThreads, 0, s>>>(f.numer, R, f.count, a.loss_out);
   return hipGetLastError();
 }
 
@@ -823,7 +835,7 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   size_t off = 0;
   w.segB = off;      off = align_up(off + N * 2 * sizeof(float), 256);
   w.bcount = off;    off = align_up(off + size_t(d.R) * kCtrStride * sizeof(int32_t), 256);
-  w.ticket = off;    off = align_up(off + sizeof(int32_t), 256);
+  w.ticket = off;    off = align_up(off + 256, 256);  // ticket, and the done count 128 bytes on
   w.numer = off;     off = align_up(off + size_t(d.R) * sizeof(double), 256);
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
   w.total = off;
