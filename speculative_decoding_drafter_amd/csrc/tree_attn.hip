@@ -133,6 +133,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
     const size_t tB = size_t(t) * p.B;
     const int B = p.B, Wn = p.Wn;
     __shared__ int8_t s_par[kPlanLds];  // parent of every node of the trunk
+    __shared__ int8_t s_dep[kPlanLds];  // depth its position implies (-1: none in 0..63)
     __shared__ __attribute__((aligned(16))) int s_key[kSortLds + 4];  // anchor, then sort key (-1: malformed)
     __shared__ int s_bad[kSortLds];
     __shared__ int s_ord[kSortLds];
@@ -144,9 +145,14 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
         s_key[b] = p.anchors[tB + b];
         s_bad[b] = 0;
       }
+      // parents, positions and anchors are read in one pass (independent
+      // loads), so the walk below touches only LDS
+#pragma unroll 4
       for (int i = tid; i < nodes; i += 256) {
         const int pj = p.parent[tB * Wn + i];
         s_par[i] = int8_t((pj >= -1 && pj < 64) ? pj : -2);  // -2: invalid
+        const long long e = (long long)p.pos[tB * Wn + i] - p.anchors[tB + i / Wn] - 1;
+        s_dep[i] = int8_t((e >= 0 && e < 64) ? e : -1);
       }
       __syncthreads();
       // one thread per node: walk the parent chain (each step must go to an
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
           k = pk;
         }
         const int depth = __popcll(m) - 1;
-        if (p.pos[tB * Wn + i] != s_key[b] + 1 + depth) ok = false;
+        if (s_dep[i] != depth) ok = false;
         p.anc[tB * Wn + i] = m;
         if (!ok) s_bad[b] = 1;
       }
@@ -236,6 +242,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
     run[tid] = sum;
     __syncthreads();
     int32_t* ps = p.pstart + size_t(t) * (np + 1);
+    __shared__ int wsum[4];
     {
       // exclusive scan of the 256 run totals: within each wave by shuffles,
       // then across the four waves
@@ -246,7 +253,6 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
         const int y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
       }
-      __shared__ int wsum[4];
       if (lane == 63) wsum[w] = x;
       __syncthreads();
       int base = 0;
@@ -257,29 +263,28 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
       if (tid == 255) ps[np] = base + x;
     }
     __syncthreads();
-    int acc = run[tid];
-    for (int i = lo; i < hi; ++i) {
-      ps[i] = acc;
-      acc += tiles(i);
-    }
-    // units of the matrix-core kernel per (trunk, kv head): U = npacks *
-    // nsplit, one per pack plus the other U - npacks dealt to the packs in
-    // proportion to their key tiles (cumulatively, so they add up exactly)
-    __syncthreads();
+    // each thread's run of packs: tile offsets, and the matrix-core kernel's
+    // units per (trunk, kv head): U = npacks * nsplit, one per pack plus the
+    // other U - npacks dealt to the packs in proportion to their key tiles
+    // (cumulatively, so they add up exactly)
     {
+      const long long NT = (long long)wsum[0] + wsum[1] + wsum[2] + wsum[3];
       const int U = np * p.nsplit, extra = U - np;
-      const long long NT = ps[np];
       int32_t* us = p.ustart + size_t(t) * (np + 1);
       int32_t* um = p.umap + size_t(t) * U;
-      for (int i = tid; i <= np; i += 256) {
-        const long long e = NT > 0 ? (long long)extra * ps[i] / NT : 0;
-        us[i] = i == np ? U : i + int(e);
+      auto share = [&](long long tiles_before) {
+        return NT > 0 ? int((long long)extra * tiles_before / NT) : 0;
+      };
+      int acc = run[tid];
+      for (int i = lo; i < hi; ++i) {
+        const int ti = tiles(i);
+        ps[i] = acc;
+        const int e0 = share(acc), e1 = i + 1 == np ? extra : share(acc + ti);
+        us[i] = i + e0;
+        for (int u = i + e0; u < i + 1 + e1; ++u) um[u] = i;
+        acc += ti;
       }
-      for (int i = tid; i < np; i += 256) {
-        const long long e0 = NT > 0 ? (long long)extra * ps[i] / NT : 0;
-        const long long e1 = i + 1 == np ? extra : (NT > 0 ? (long long)extra * ps[i + 1] / NT : 0);
-        for (int u = i + int(e0); u < i + 1 + int(e1); ++u) um[u] = i;
-      }
+      if (tid == 255) us[np] = U;
     }
     int32_t* c = p.ctr + size_t(t) * p.Hkv * np;
     for (int i = tid; i < p.Hkv * np; i += 256) c[i] = 0;
