@@ -178,6 +178,25 @@ def test_log_sum_exp_reference_moves(gpu_ok, logits):
     _check_full(cpu, out)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", ["wide", "single"])
+def test_branch_width_extremes(gpu_ok, dtype, shape):
+    """The widest branch the call takes (64 nodes: one per lane of the wave
+    that scans the branch; a seeded random tree) and one-node branches, on
+    the resident (bf16) and streaming (fp32) kernels."""
+    if shape == "wide":
+        rng = np.random.default_rng(11)
+        par = tuple([-1] + [int(rng.integers(-1, j)) for j in range(1, 64)])
+        R = 3
+    else:
+        par, R = (-1,), 40
+    cfg = shrink_loss(WORKLOADS[2].loss, R=R, V=4096, parent=par, dtype=dtype)
+    inp = gen_loss(cfg, 12, device=DEV, cid=2)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)
+
+
 def test_malformed_parent_flags_branch(gpu_ok):
     cfg = shrink_loss(WORKLOADS[2].loss, R=4, V=4096)
     inp = gen_loss(cfg, 4, device=DEV, cid=2)
