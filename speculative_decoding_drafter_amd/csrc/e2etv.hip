@@ -10,7 +10,7 @@
 // One fused kernel, one workgroup per row (row n = branch r, node j):
 //   pass A   read the row: log-sum-exp of draft and target;
 //   pass B   alpha = sum min(q, p) and G = sum_{q<p} q;
-//   post     publish (alpha, G) and count the row into its branch;
+//   post     publish (alpha, G) in the row's slot;
 //   scan     once every row of the branch has posted, compute prefix
 //            products, suffix sums S and this row's coefficient
 //            c = grad_scale * dLoss/dalpha in fp64 (every row of a branch
@@ -25,7 +25,7 @@
 // atomic ticket, so a workgroup only waits for rows of its own branch that
 // were claimed just before or after it; the wait is bounded and a timeout
 // marks the branch malformed rather than hanging.  The exchange uses
-// device-scope relaxed atomic accesses (see post_f32).
+// device-scope relaxed atomic accesses (see the cross-workgroup exchange).
 // The branch that reports last sums the branch numerators in a fixed order
 // (loss), so no further kernel runs after the rows.
 // No floating-point atomics: results are bitwise reproducible.
@@ -39,8 +39,6 @@ namespace specopd {
 namespace {
 
 constexpr int kThreads = 1024;  // per workgroup (one row)
-constexpr int kCtrStride = 64;  // branch counters 256 B apart, so polls of different
-                                // branches do not all land on one memory channel
 constexpr int kU = 2;           // 16-byte vectors per tensor per thread per batch
 
 // One element's log2-probabilities.  The overlap pass and the gradient pass
@@ -188,37 +186,20 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float* red) {
 // Cross-workgroup exchange.  The XCDs' L2 caches are not coherent with each
 // other, and device-scope release/acquire would write back / invalidate a
 // whole L2 per use.  Instead every exchanged word is a device-scope relaxed
-// atomic access (individually coherent across the XCDs, no fence): a
-// workgroup posts its partials, waits until those stores are acknowledged,
-// and only then bumps the counter; a reader that sees the count reads the
-// partials the same way.
-__device__ __forceinline__ void post_f32(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float peek_f32(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// atomic access (individually coherent across the XCDs, no fence).  A row
+// posts its (alpha, G) as one 64-bit word whose top bit marks it posted (the
+// slots are cleared before the rows run; alpha >= 0 leaves its sign bit
+// free), so a reader that sees the mark has the values in the same access.
+// Numerators are posted and acknowledged before the branch is counted.
 __device__ __forceinline__ void post_f64(double* p, double v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ double peek_f64(const double* p) {
   return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void post_count(int32_t* ctr) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partials acknowledged first
-  __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Bounded wait until *ctr reaches want.  False on timeout.
-__device__ __forceinline__ bool wait_count(int32_t* ctr, int want, int spin_limit) {
-  int spins = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
-    if (++spins > spin_limit) return false;
-    if (spins < 32)  // back off after the first polls
-      __builtin_amdgcn_s_sleep(2);
-    else
-      __builtin_amdgcn_s_sleep(8);
-  }
-  return true;
+constexpr unsigned long long kPosted = 1ull << 63;
+__device__ __forceinline__ unsigned long long pack_slot(float al, float g) {
+  return kPosted | (static_cast<unsigned long long>(__float_as_uint(al)) << 32) | __float_as_uint(g);
 }
 
 struct FusedArgs {
@@ -229,8 +210,7 @@ struct FusedArgs {
   double count;
   float grad_scale;
   int spin_limit;
-  float* segB;      // [N][2] (alpha, G) of every row
-  int32_t* bcount;  // [R] rows of each branch that posted
+  unsigned long long* slot;  // [N] posted (alpha, G) of every row, 0 until posted
   int32_t* ticket;
   int32_t* done;    // branches that reported their numerator
   int R;
@@ -252,30 +232,39 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
 }
 
 // The first wave of a row's workgroup (all 64 lanes): publish the row's
-// (alpha, G), count it into its branch, and -- if the row needs the branch
-// (gradient rows, and the branch's first row, which reports the branch) --
-// wait for every row of the branch, then scan it in fp64: prefix products
-// P_k = alpha_k P_parent, suffix sums S_k = 1 + sum over children c of
-// alpha_c S_c, and this row's gradient coefficients s_val[0] (where q < p)
-// and s_val[1] (elsewhere).  The branch's rows are read one per lane in a
-// single round trip; the scan walks the nodes in index order (children come
-// after their parents) with every value held by its node's lane, so every
-// row of a branch does the same arithmetic in the same order.
+// (alpha, G) and -- if the row needs the branch (gradient rows, and the
+// branch's first row, which reports the branch) -- wait until every row of
+// the branch has posted (lane k polls node k's slot; bounded), then scan the
+// branch in fp64: prefix products P_k = alpha_k P_parent, suffix sums
+// S_k = 1 + sum over children c of alpha_c S_c, and this row's gradient
+// coefficients s_val[0] (where q < p) and s_val[1] (elsewhere).  The scan
+// walks the nodes in index order (children come after their parents) with
+// every value held by its node's lane, so every row of a branch does the
+// same arithmetic in the same order.
 __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j, float al, float g,
                                            bool need_scan, float* s_val) {
   const int lane = int(threadIdx.x) & 63;
   const float qnan = __builtin_nanf("");
-  int32_t* const ctr = &a.bcount[size_t(r) * kCtrStride];
-  if (lane == 0) {
-    post_f32(a.segB + size_t(n) * 2 + 0, al);
-    post_f32(a.segB + size_t(n) * 2 + 1, g);
-    post_count(ctr);
-  }
+  const unsigned long long mine = pack_slot(al, g);
+  if (lane == 0) __hip_atomic_store(a.slot + n, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!need_scan) return;
-  bool lok = true;
-  if (lane == 0) lok = wait_count(ctr, a.Wn, a.spin_limit);
-  // read after the wait (the loads follow the spin in program order)
   const int Wn = a.Wn;
+  unsigned long long* const bs = a.slot + size_t(r) * Wn;
+  // this row's own slot is known; lanes past the branch have nothing to wait for
+  unsigned long long v = lane == j ? mine : 0ull;
+  bool have = lane >= Wn || lane == j;
+  for (int spins = 0;;) {
+    if (!have) {
+      v = __hip_atomic_load(bs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      have = (v & kPosted) != 0;
+    }
+    if (__builtin_amdgcn_ballot_w64(!have) == 0 || ++spins > a.spin_limit) break;
+    if (spins < 32)  // back off after the first polls
+      __builtin_amdgcn_s_sleep(2);
+    else
+      __builtin_amdgcn_s_sleep(8);
+  }
+  bool lok = have;
   int pk = -1;
   double ak = 0.0;
   float gk = 0.f;
@@ -285,9 +274,8 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
       lok = false;
       pk = -1;
     }
-    const float* sb = a.segB + (size_t(r) * Wn + lane) * 2;
-    ak = double(peek_f32(sb));
-    gk = peek_f32(sb + 1);
+    ak = double(__uint_as_float(unsigned(v >> 32) & 0x7fffffffu));
+    gk = __uint_as_float(unsigned(v));
   }
   const bool ok = __builtin_amdgcn_ballot_w64(!lok) == 0;
   double P = 0.0, sum = 0.0;
@@ -345,16 +333,15 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
 }
 
 __global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ done,
-                                  int32_t* __restrict__ bcount, int32_t* __restrict__ branch_ok, int R) {
+                                  unsigned long long* __restrict__ slot, int N,
+                                  int32_t* __restrict__ branch_ok, int R) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) {
     *ticket = 0;
     *done = 0;
   }
-  if (i < R) {
-    bcount[size_t(i) * kCtrStride] = 0;
-    branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
-  }
+  if (i < N) slot[i] = 0;  // not posted
+  if (i < R) branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
 }
 
 // Elements of a streamed unit as fp32: a 16-byte vector, or one raw element.
@@ -796,8 +783,7 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.count = d.norm_count > 0 ? d.norm_count : double(N);
   f.grad_scale = d.grad_scale;
   f.spin_limit = spin_limit;
-  f.segB = reinterpret_cast<float*>(a.ws + L.segB);
-  f.bcount = reinterpret_cast<int32_t*>(a.ws + L.bcount);
+  f.slot = reinterpret_cast<unsigned long long*>(a.ws + L.slot);
   f.ticket = reinterpret_cast<int32_t*>(a.ws + L.ticket);
   f.done = f.ticket + 32;  // the next 128-byte line of the ticket's block
   f.R = R;
@@ -807,7 +793,7 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.alpha_out = a.alpha_out;
   f.prefix_out = a.prefix_out;
   f.grad = a.grad;
-  e2etv_zero_kernel<<<(R + 255) / 256, 256, 0, s>>>(f.ticket, f.done, f.bcount, f.branch_ok, R);
+  e2etv_zero_kernel<<<(N + 255) / 256, 256, 0, s>>>(f.ticket, f.done, f.slot, N, f.branch_ok, R);
   const unsigned grid = unsigned(N);
   timing_mark(1, 0, s);
   if constexpr (BF16 && VECTOR) {
@@ -833,8 +819,7 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   const size_t N = size_t(d.R) * size_t(d.Wn);
   E2etvWs w{};
   size_t off = 0;
-  w.segB = off;      off = align_up(off + N * 2 * sizeof(float), 256);
-  w.bcount = off;    off = align_up(off + size_t(d.R) * kCtrStride * sizeof(int32_t), 256);
+  w.slot = off;      off = align_up(off + N * sizeof(unsigned long long), 256);
   w.ticket = off;    off = align_up(off + 256, 256);  // ticket, and the done count 128 bytes on
   w.numer = off;     off = align_up(off + size_t(d.R) * sizeof(double), 256);
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);

@@ -131,13 +131,13 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
 
 // ---------------------------------------------------------------- E2E-TV
 // Workspace layout:
-//   segB       float  [N][2]  (alpha, G) of every row
-//   bcount     int32  [R]     rows of each branch that posted
-//   ticket     int32          next row to hand out, in order
+//   slot       u64    [N]     (alpha, G) of every row, top bit set once posted
+//   ticket     int32          next row to hand out, in order; 128 bytes on, the
+//                             count of branches that reported their numerator
 //   numer      double [R]     sum of prefix products of each branch
 //   branch_ok  int32  [R]
 struct E2etvWs {
-  size_t segB, bcount, ticket, numer, branch_ok, total;
+  size_t slot, ticket, numer, branch_ok, total;
 };
 E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d);
 
