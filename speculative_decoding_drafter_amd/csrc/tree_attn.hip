@@ -97,6 +97,7 @@ struct PrepParams {
 constexpr int kSortLds = 2048;  // branches per trunk planned and sorted in LDS
 constexpr int kPlanLds = 8192;  // nodes per trunk whose parents are staged in LDS
 constexpr int kRopeNodes = 4;   // nodes per rotary pass of a workgroup
+constexpr int kRopeBatch = 6;   // rotary units per thread whose loads are in flight together
 
 __device__ void plan_branch(const PrepParams& p, size_t tb) {
   const int a = p.anchors[tb];
@@ -155,27 +156,51 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
         s_dep[i] = int8_t((e >= 0 && e < 64) ? e : -1);
       }
       __syncthreads();
-      // one thread per node: walk the parent chain (each step must go to an
-      // earlier node, so the walk ends); the visited nodes are the node's
-      // ancestor mask, their count fixes the depth
-      for (int i = tid; i < nodes; i += 256) {
-        const int b = i / Wn, j = i - b * Wn;
-        uint64_t m = 0;
-        bool ok = true;
-        for (int k = j;;) {
-          m |= uint64_t(1) << k;
-          const int pk = s_par[b * Wn + k];
-          if (pk == -1) break;
-          if (pk < 0 || pk >= k) {
-            ok = false;
-            break;
-          }
-          k = pk;
+      // ancestor masks by pointer jumping: one lane per node, a branch's
+      // nodes in a group of gsz lanes (the power of two >= Wn); each round a
+      // node takes in the mask of the node its link points to and links on
+      // to that node's link, so after r rounds the mask holds the ancestors
+      // less than 2^r steps up (a parent must be an earlier node, so a
+      // node's depth is below Wn).  A node whose own parent is out of range
+      // marks its branch malformed and counts as a root.  The mask's size
+      // fixes the depth.
+      {
+        int gsz = 1, rounds = 0;
+        while (gsz < Wn) {
+          gsz <<= 1;
+          ++rounds;
         }
-        const int depth = __popcll(m) - 1;
-        if (s_dep[i] != depth) ok = false;
-        p.anc[tB * Wn + i] = m;
-        if (!ok) s_bad[b] = 1;
+        const int lane = tid & 63, wv = tid >> 6;
+        const int j = lane & (gsz - 1);
+        const int bpw = 64 / gsz;  // branches per wave and pass
+        for (int b0 = wv * bpw; b0 < B; b0 += 4 * bpw) {
+          const int b = b0 + lane / gsz;
+          const bool live = b < B && j < Wn;
+          int pj = live ? int(s_par[b * Wn + j]) : -1;
+          bool ok = true;
+          if (pj < -1 || pj >= j) {
+            ok = false;
+            pj = -1;
+          }
+          uint64_t m = live ? uint64_t(1) << j : 0;
+          int link = pj >= 0 ? lane - j + pj : -1;  // the parent's lane
+          for (int rd = 0; rd < rounds; ++rd) {
+            const int src = (link >= 0 ? link : lane) << 2;
+            const unsigned lo = __builtin_amdgcn_ds_bpermute(src, unsigned(m));
+            const unsigned hi = __builtin_amdgcn_ds_bpermute(src, unsigned(m >> 32));
+            const int nl = __builtin_amdgcn_ds_bpermute(src, link);
+            if (link >= 0) {
+              m |= (uint64_t(hi) << 32) | lo;
+              link = nl;
+            }
+          }
+          if (live) {
+            const int i = b * Wn + j;
+            if (s_dep[i] != __popcll(m) - 1) ok = false;
+            p.anc[tB * Wn + i] = m;
+            if (!ok) s_bad[b] = 1;
+          }
+        }
       }
       __syncthreads();
       for (int b = tid; b < B; b += 256) {
@@ -316,30 +341,50 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
       s_cs[idx] = make_float2(cs, sn);
     }
     __syncthreads();
-    for (int u = tid; u < nn * H * octs; u += 256) {
-      const int lnh = u / octs;
-      const int i0 = (u - lnh * octs) * 8;
-      const int ln = lnh / H, hd = lnh - ln * H;
-      const size_t node = n0 + ln;
-      const bool isq = hd < p.Hq;
-      const uint16_t* __restrict__ src =
-          isq ? p.q + (node * p.Hq + hd) * p.D : p.k + (node * p.Hkv + (hd - p.Hq)) * p.D;
-      uint16_t* __restrict__ dst =
-          isq ? p.qr + (node * p.Hq + hd) * p.D : p.kr + (node * p.Hkv + (hd - p.Hq)) * p.D;
-      const float mul = isq ? p.qmul : 1.0f;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(src + i0);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(src + i0 + half);
-      u32x4 ya, yb;
+    // kRopeBatch units per thread at a time: their loads are all issued
+    // before any of them is rotated, so a pass costs one memory round trip
+    // per batch rather than one per unit
+    const int units = nn * H * octs;
+    for (int u0 = tid; u0 < units; u0 += 256 * kRopeBatch) {
+      u32x4 a[kRopeBatch], b[kRopeBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float2 c0 = s_cs[ln * half + i0 + 2 * e], c1 = s_cs[ln * half + i0 + 2 * e + 1];
-        const float x10 = bf16_lo(a[e]), x11 = bf16_hi(a[e]);
-        const float x20 = bf16_lo(b[e]), x21 = bf16_hi(b[e]);
-        ya[e] = pack_bf16x2((x10 * c0.x - x20 * c0.y) * mul, (x11 * c1.x - x21 * c1.y) * mul);
-        yb[e] = pack_bf16x2((x20 * c0.x + x10 * c0.y) * mul, (x21 * c1.x + x11 * c1.y) * mul);
+      for (int r = 0; r < kRopeBatch; ++r) {
+        const int u = u0 + r * 256;
+        if (u < units) {
+          const int lnh = u / octs;
+          const int i0 = (u - lnh * octs) * 8;
+          const int ln = lnh / H, hd = lnh - ln * H;
+          const size_t node = n0 + ln;
+          const uint16_t* src =
+              hd < p.Hq ? p.q + (node * p.Hq + hd) * p.D : p.k + (node * p.Hkv + (hd - p.Hq)) * p.D;
+          a[r] = *reinterpret_cast<const u32x4*>(src + i0);
+          b[r] = *reinterpret_cast<const u32x4*>(src + i0 + half);
+        }
       }
-      *reinterpret_cast<u32x4*>(dst + i0) = ya;
-      *reinterpret_cast<u32x4*>(dst + i0 + half) = yb;
+#pragma unroll
+      for (int r = 0; r < kRopeBatch; ++r) {
+        const int u = u0 + r * 256;
+        if (u < units) {
+          const int lnh = u / octs;
+          const int i0 = (u - lnh * octs) * 8;
+          const int ln = lnh / H, hd = lnh - ln * H;
+          const size_t node = n0 + ln;
+          const bool isq = hd < p.Hq;
+          uint16_t* dst = isq ? p.qr + (node * p.Hq + hd) * p.D : p.kr + (node * p.Hkv + (hd - p.Hq)) * p.D;
+          const float mul = isq ? p.qmul : 1.0f;
+          u32x4 ya, yb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 c0 = s_cs[ln * half + i0 + 2 * e], c1 = s_cs[ln * half + i0 + 2 * e + 1];
+            const float x10 = bf16_lo(a[r][e]), x11 = bf16_hi(a[r][e]);
+            const float x20 = bf16_lo(b[r][e]), x21 = bf16_hi(b[r][e]);
+            ya[e] = pack_bf16x2((x10 * c0.x - x20 * c0.y) * mul, (x11 * c1.x - x21 * c1.y) * mul);
+            yb[e] = pack_bf16x2((x20 * c0.x + x10 * c0.y) * mul, (x21 * c1.x + x11 * c1.y) * mul);
+          }
+          *reinterpret_cast<u32x4*>(dst + i0) = ya;
+          *reinterpret_cast<u32x4*>(dst + i0 + half) = yb;
+        }
+      }
     }
   }
 }
