@@ -81,6 +81,7 @@ def test_reduced_workloads(gpu_ok, cid, R, V):
     135168,    # exactly the on-chip capacity: nothing streamed
     135176,    # one octet streamed
     139264,    # a streamed tail of 4096 elements
+    160008,    # a long streamed tail (24,840 elements)
 ])
 def test_resident_capacity_boundaries(gpu_ok, V):
     """Row lengths around the on-chip capacity of the resident loss kernel
@@ -285,3 +286,24 @@ def test_full_size_sampled_branches(gpu_ok, cid):
         check_grad_rows(out["grad"][r].float().cpu().numpy(), ref["grad"][0], ref["margin"][0],
                         _oracle_q(inp["draft"][r]), ref["dL_dalpha"][0], identical=ident[r],
                         what=f"grad branch {r}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes(gpu_ok, seed):
+    """Seeded random shapes: branches, random trees of 1..24 nodes,
+    vocabularies from 1 to 160,000 (aligned or not), bf16 or fp32 logits,
+    each recipe -- checked element by element against the oracle."""
+    rng = np.random.default_rng(2000 + seed)
+    Wn = int(rng.integers(1, 25))
+    par = tuple([-1] + [int(rng.integers(-1, j)) for j in range(1, Wn)])
+    V = int(rng.choice([1, 7, 64, 1000, 8200, 40001, 151936, 160000]))
+    cid = int(rng.choice([2, 3, 4]))
+    R = int(rng.integers(1, max(2, 64 // Wn)))
+    if V * R * Wn > 6_000_000:
+        R = max(1, 6_000_000 // (V * Wn))
+    cfg = shrink_loss(WORKLOADS[cid].loss, R=R, V=V, parent=par, dtype=str(rng.choice(["bf16", "f32"])))
+    print(f"random shape {seed}: R={R} Wn={Wn} V={V} cid={cid} {cfg.dtype}", flush=True)
+    inp = gen_loss(cfg, 30 + seed, device=DEV, cid=cid)
+    out = sd.e2etv(inp["draft"], inp["target"], inp["parent"])
+    torch.cuda.synchronize()
+    _check_full(inp, out)

@@ -181,3 +181,21 @@ def test_timing_hook_counts_trunk_launches(gpu_ok):
         sd.specopd_kernel_timing(False)
     assert n == cfg.T and ms > 0.0
     assert a_n == 0, "a prefill is not timed as a tree-attention call"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_shapes(gpu_ok, seed):
+    """Seeded random trunk shapes: trunks, lengths ragged against the tile,
+    1..8 query heads per kv head, D of 64, 128 or 256 -- every row and the
+    cache checked against the oracle."""
+    rng = np.random.default_rng(3000 + seed)
+    Hkv = int(rng.choice([1, 2, 4]))
+    cfg = shrink_attn(WORKLOADS[2].attn, T=int(rng.integers(1, 3)), L=int(rng.integers(1, 500)),
+                      Hq=Hkv * int(rng.choice([1, 2, 4, 8])), Hkv=Hkv, D=int(rng.choice([64, 128, 256])))
+    print(f"random shape {seed}: T={cfg.T} L={cfg.L} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D}", flush=True)
+    inp = gen_prefill(cfg, 40 + seed, device=DEV, cid=2)
+    out, ck, cv = _run(inp)
+    for t in range(cfg.T):
+        ref, _, _ = oracle.trunk_prefill(_np(inp["q"][t]), _np(inp["k"][t]), _np(inp["v"][t]))
+        check_attention(_np(out[t]), ref, what=f"trunk {t}")
+        _check_cache(ck, cv, inp, t)

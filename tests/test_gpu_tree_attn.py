@@ -195,3 +195,25 @@ def test_more_branches_than_the_staged_plan(gpu_ok):
     got = out.float().cpu().numpy()
     for (t, b) in picks:
         check_attention(got[t, b], ref[t, b], what=f"branch {b}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes(gpu_ok, seed):
+    """Seeded random shapes across the argument space: trunks, trunk length
+    (ragged against the 32-key tile), prompt length, branches, random trees of
+    1..12 nodes, 1..8 query heads per kv head, 1..4 kv heads, D of 64, 128 or
+    256, bf16 -- each checked element by element against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128, 256]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    Wn = int(rng.integers(1, 13))
+    L = int(rng.integers(1, 600))
+    parent, depth = _random_tree(rng, Wn)
+    cfg = shrink_attn(WORKLOADS[2].attn, T=int(rng.integers(1, 3)), L=L, P=int(rng.integers(0, L)),
+                      B=int(rng.integers(1, 17)), Hq=G * Hkv, Hkv=Hkv, D=D, parent=parent, depth=depth)
+    print(f"random shape {seed}: {cfg}", flush=True)
+    inp = gen_attn(cfg, 20 + seed, device=DEV, cid=2)
+    out, desc, ws = _run(inp)
+    assert sd.specopd_tree_attn_device_status(desc, ws) == 0
+    check_attention(out.float().cpu().numpy(), _ref(inp))
