@@ -288,7 +288,7 @@ def test_full_size_sampled_branches(gpu_ok, cid):
                         what=f"grad branch {r}")
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_shapes(gpu_ok, seed):
     """Seeded random shapes: branches, random trees of 1..24 nodes,
     vocabularies from 1 to 160,000 (aligned or not), bf16 or fp32 logits,
@@ -298,6 +298,8 @@ def test_random_shapes(gpu_ok, seed):
     par = tuple([-1] + [int(rng.integers(-1, j)) for j in range(1, Wn)])
     V = int(rng.choice([1, 7, 64, 1000, 8200, 40001, 151936, 160000]))
     cid = int(rng.choice([2, 3, 4]))
+    if cid == 4:
+        V = max(V, 2)  # the stress recipe's disjoint rows peak at two distinct tokens
     R = int(rng.integers(1, max(2, 64 // Wn)))
     if V * R * Wn > 6_000_000:
         R = max(1, 6_000_000 // (V * Wn))

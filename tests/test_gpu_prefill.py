@@ -183,7 +183,7 @@ def test_timing_hook_counts_trunk_launches(gpu_ok):
     assert a_n == 0, "a prefill is not timed as a tree-attention call"
 
 
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(8))
 def test_random_shapes(gpu_ok, seed):
     """Seeded random trunk shapes: trunks, lengths ragged against the tile,
     1..8 query heads per kv head, D of 64, 128 or 256 -- every row and the

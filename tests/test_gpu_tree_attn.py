@@ -197,7 +197,7 @@ def test_more_branches_than_the_staged_plan(gpu_ok):
         check_attention(got[t, b], ref[t, b], what=f"branch {b}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_shapes(gpu_ok, seed):
     """Seeded random shapes across the argument space: trunks, trunk length
     (ragged against the 32-key tile), prompt length, branches, random trees of
@@ -208,10 +208,11 @@ def test_random_shapes(gpu_ok, seed):
     Hkv = int(rng.choice([1, 2, 4]))
     G = int(rng.choice([1, 2, 4, 8]))
     Wn = int(rng.integers(1, 13))
-    L = int(rng.integers(1, 600))
+    B = int(rng.integers(1, 17))
+    L = int(rng.integers(B + 1, 600))  # B distinct anchors in [P, L - 1)
     parent, depth = _random_tree(rng, Wn)
-    cfg = shrink_attn(WORKLOADS[2].attn, T=int(rng.integers(1, 3)), L=L, P=int(rng.integers(0, L)),
-                      B=int(rng.integers(1, 17)), Hq=G * Hkv, Hkv=Hkv, D=D, parent=parent, depth=depth)
+    cfg = shrink_attn(WORKLOADS[2].attn, T=int(rng.integers(1, 3)), L=L, P=int(rng.integers(0, L - B)),
+                      B=B, Hq=G * Hkv, Hkv=Hkv, D=D, parent=parent, depth=depth)
     print(f"random shape {seed}: {cfg}", flush=True)
     inp = gen_attn(cfg, 20 + seed, device=DEV, cid=2)
     out, desc, ws = _run(inp)
