@@ -47,7 +47,7 @@ extern "C" {
 /* Same type as HIP's own stream handle. */
 typedef struct ihipStream_t* hipStream_t;
 
-#define SPECOPD_VERSION 1
+#define SPECOPD_VERSION 2
 
 typedef enum {
   SPECOPD_OK = 0,
@@ -189,6 +189,8 @@ typedef struct {
   double norm_count;           /* <= 0: R*Wn; else the global count (Eq. 18) */
   float grad_scale;            /* factor applied to the gradient (1 = dLoss) */
   uint32_t flags;              /* reserved, must be 0                        */
+  int32_t wait_polls;          /* bound on a row's polls for its branch; <= 0:
+                                  2^20 (see specopd_e2etv_fwd_bwd)           */
 } specopd_e2etv_desc;
 
 specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size_t* bytes);
@@ -222,6 +224,17 @@ specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size
  *
  * Rows whose parent map is malformed get NaN alpha/prefix/gradient and are
  * counted (specopd_e2etv_device_status); the loss is then NaN.
+ *
+ * Scheduling.  Each row is reduced by one workgroup, and a row's gradient
+ * needs the overlaps of every row of its branch, so a workgroup waits for
+ * the other rows of its branch after posting its own.  That wait is bounded
+ * by desc->wait_polls polls (each a few hundred nanoseconds): a row whose
+ * branch has not fully posted by then -- because its rows could not run at
+ * the same time, e.g. other kernels occupied the CUs -- hands its scan and
+ * gradient to a second kernel of the same call, which runs once every row
+ * has posted and re-reads that row.  Results are identical either way (the
+ * deferred count is reported by specopd_e2etv_device_status); only the time
+ * changes.  The wait never fails and never hangs.
  */
 specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc,
                                      const void* draft_logits, const void* target_logits,
@@ -231,10 +244,14 @@ specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc,
                                      hipStream_t stream);
 
 /* Synchronises `stream`; reports how many branches had a malformed parent map
- * in the last specopd_e2etv_fwd_bwd on this workspace. */
+ * in the last specopd_e2etv_fwd_bwd on this workspace (returning
+ * SPECOPD_ERR_DEVICE_VALIDATION if any did) and how many rows gave up their
+ * wait for their branch and were finished by the second kernel (not an
+ * error).  Either output pointer may be NULL. */
 specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
                                            const void* workspace, size_t workspace_bytes,
-                                           int32_t* bad_branches, hipStream_t stream);
+                                           int32_t* bad_branches, int32_t* deferred_rows,
+                                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing, for measurement harnesses.

@@ -45,7 +45,7 @@ class TreeAttnDesc(ctypes.Structure):
 class E2etvDesc(ctypes.Structure):
     _fields_ = [("R", c_int32), ("Wn", c_int32), ("V", c_int32), ("logits_dtype", c_int),
                 ("grad_dtype", c_int), ("norm_count", c_double), ("grad_scale", c_float),
-                ("flags", c_uint32)]
+                ("flags", c_uint32), ("wait_polls", c_int32)]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -72,7 +72,7 @@ def _load():
     lib.specopd_e2etv_workspace_size.argtypes = [POINTER(E2etvDesc), POINTER(c_size_t)]
     lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P, c_size_t, P]
     lib.specopd_e2etv_device_status.argtypes = [POINTER(E2etvDesc), P, c_size_t,
-                                                POINTER(c_int32), P]
+                                                POINTER(c_int32), POINTER(c_int32), P]
     lib.specopd_prefill_workspace_size.argtypes = [POINTER(PrefillDesc), POINTER(c_size_t)]
     lib.specopd_prefill_fwd.argtypes = [POINTER(PrefillDesc)] + [P] * 6 + [P, c_size_t, P]
     lib.specopd_kernel_timing.argtypes = [c_int]
@@ -136,10 +136,10 @@ def tree_attn_desc(T, L, B, Wn, Hq, Hkv, D, dtype, rope_base=10000.0, scale=0.0,
 
 
 def e2etv_desc(R, Wn, V, logits_dtype, grad_dtype=torch.float32, norm_count=0.0, grad_scale=1.0,
-               flags=0):
+               flags=0, wait_polls=0):
     ld = _DT.get(logits_dtype, logits_dtype) if not isinstance(logits_dtype, int) else logits_dtype
     gd = _DT.get(grad_dtype, grad_dtype) if not isinstance(grad_dtype, int) else grad_dtype
-    return E2etvDesc(R, Wn, V, ld, gd, norm_count, grad_scale, flags)
+    return E2etvDesc(R, Wn, V, ld, gd, norm_count, grad_scale, flags, wait_polls)
 
 
 def prefill_desc(T, L, Hq, Hkv, D, dtype, rope_base=10000.0, scale=0.0, flags=0):
@@ -221,14 +221,16 @@ def specopd_e2etv_fwd_bwd(desc, draft, target, parent, alpha_out, prefix_out, lo
         raise SpecopdError(st, "specopd_e2etv_fwd_bwd")
 
 
-def specopd_e2etv_device_status(desc, workspace, stream=None) -> int:
-    bad = c_int32(0)
+def specopd_e2etv_device_status(desc, workspace, stream=None, with_deferred=False):
+    """Malformed branches of the last call on this workspace (and, with
+    with_deferred, the rows that the follow-up kernel finished)."""
+    bad, deferred = c_int32(0), c_int32(0)
     st = LIB.specopd_e2etv_device_status(ctypes.byref(desc), _ptr(workspace),
                                          c_size_t(workspace.numel() * workspace.element_size()),
-                                         ctypes.byref(bad), _stream(stream))
+                                         ctypes.byref(bad), ctypes.byref(deferred), _stream(stream))
     if st not in (SPECOPD_OK, SPECOPD_ERR_DEVICE_VALIDATION):
         raise SpecopdError(st, "specopd_e2etv_device_status")
-    return bad.value
+    return (bad.value, deferred.value) if with_deferred else bad.value
 
 
 # ------------------------------------------------------------------ helpers
@@ -270,11 +272,12 @@ def prefill(q, k, v, rope_base=10000.0, scale=0.0, ws=None, outs=None):
 
 
 def e2etv(draft, target, parent, grad=True, grad_dtype=torch.float32, norm_count=0.0,
-          grad_scale=1.0, ws=None, outs=None):
+          grad_scale=1.0, ws=None, outs=None, wait_polls=0):
     """E2E-TV forward + gradient; returns dict of device tensors."""
     R, Wn, V = draft.shape
     dev = draft.device
-    desc = e2etv_desc(R, Wn, V, draft.dtype, grad_dtype, norm_count, grad_scale)
+    desc = e2etv_desc(R, Wn, V, draft.dtype, grad_dtype, norm_count, grad_scale,
+                      wait_polls=wait_polls)
     if ws is None:
         ws = workspace(specopd_e2etv_workspace_size(desc), dev)
     if outs is None:

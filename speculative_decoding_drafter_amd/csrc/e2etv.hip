@@ -23,9 +23,13 @@
 // pass with software-pipelined loads: the next batch of 16-byte vectors is in
 // flight while the current one is reduced.  Rows are taken in order from an
 // atomic ticket, so a workgroup only waits for rows of its own branch that
-// were claimed just before or after it; the wait is bounded and a timeout
-// marks the branch malformed rather than hanging.  The exchange uses
-// device-scope relaxed atomic accesses (see the cross-workgroup exchange).
+// were claimed just before or after it.  The wait is bounded: a row whose
+// siblings have not all posted by then (they could not be resident at the
+// same time, e.g. while other kernels hold the CUs) leaves its log-sum-exps
+// in the workspace and hands its scan and gradient to e2etv_rescue_kernel,
+// which runs after every row has posted; results are the same either way.
+// The exchange uses device-scope relaxed atomic accesses (see the
+// cross-workgroup exchange).
 // The branch that reports last sums the branch numerators in a fixed order
 // (loss), so no further kernel runs after the rows.
 // No floating-point atomics: results are bitwise reproducible.
@@ -220,6 +224,9 @@ struct FusedArgs {
   float* alpha_out;
   float* prefix_out;
   void* grad;
+  int32_t* ndefer;  // rows whose wait gave up
+  int32_t* defer;   // [N] those rows, in the order they gave up
+  float2* lse;      // [N] (-log2-sum-exp2) of draft and target of each deferred row
 };
 
 // Lane k of a wave holds node k of a branch (Wn <= 64).  Uniform-index
@@ -232,27 +239,31 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
 }
 
 // The first wave of a row's workgroup (all 64 lanes): publish the row's
-// (alpha, G) and -- if the row needs the branch (gradient rows, and the
-// branch's first row, which reports the branch) -- wait until every row of
-// the branch has posted (lane k polls node k's slot; bounded), then scan the
-// branch in fp64: prefix products P_k = alpha_k P_parent, suffix sums
-// S_k = 1 + sum over children c of alpha_c S_c, and this row's gradient
+// (alpha, G) (when `post`) and -- if the row needs the branch (gradient rows,
+// and the branch's first row, which reports the branch) -- wait until every
+// row of the branch has posted (lane k polls node k's slot; bounded), then
+// scan the branch in fp64: prefix products P_k = alpha_k P_parent, suffix
+// sums S_k = 1 + sum over children c of alpha_c S_c, and this row's gradient
 // coefficients s_val[0] (where q < p) and s_val[1] (elsewhere).  The scan
 // walks the nodes in index order (children come after their parents) with
 // every value held by its node's lane, so every row of a branch does the
-// same arithmetic in the same order.
-__device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j, float al, float g,
-                                           bool need_scan, float* s_val) {
+// same arithmetic in the same order, in whichever kernel it runs.
+// When the wait gives up and `can_defer`, the row records its log-sum-exps,
+// appends itself to the deferred list and sets s_val[2]; its scan and
+// gradient are then done by e2etv_rescue_kernel.
+__device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j,
+                                              unsigned long long mine, bool post, bool need_scan,
+                                              bool can_defer, float nlz, float nlt, float* s_val) {
   const int lane = int(threadIdx.x) & 63;
   const float qnan = __builtin_nanf("");
-  const unsigned long long mine = pack_slot(al, g);
-  if (lane == 0) __hip_atomic_store(a.slot + n, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (post && lane == 0) __hip_atomic_store(a.slot + n, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!need_scan) return;
   const int Wn = a.Wn;
   unsigned long long* const bs = a.slot + size_t(r) * Wn;
-  // this row's own slot is known; lanes past the branch have nothing to wait for
-  unsigned long long v = lane == j ? mine : 0ull;
-  bool have = lane >= Wn || lane == j;
+  // this row's own slot is known when it was just posted; lanes past the
+  // branch have nothing to wait for
+  unsigned long long v = (post && lane == j) ? mine : 0ull;
+  bool have = lane >= Wn || (post && lane == j);
   for (int spins = 0;;) {
     if (!have) {
       v = __hip_atomic_load(bs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -263,6 +274,15 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
       __builtin_amdgcn_s_sleep(2);
     else
       __builtin_amdgcn_s_sleep(8);
+  }
+  if (can_defer && __builtin_amdgcn_ballot_w64(!have) != 0) {
+    if (lane == 0) {
+      a.lse[n] = make_float2(nlz, nlt);
+      const int at = __hip_atomic_fetch_add(a.ndefer, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.defer[at] = n;
+      s_val[2] = 1.f;
+    }
+    return;
   }
   bool lok = have;
   int pk = -1;
@@ -333,12 +353,13 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
 }
 
 __global__ void e2etv_zero_kernel(int32_t* __restrict__ ticket, int32_t* __restrict__ done,
-                                  unsigned long long* __restrict__ slot, int N,
-                                  int32_t* __restrict__ branch_ok, int R) {
+                                  int32_t* __restrict__ ndefer, unsigned long long* __restrict__ slot,
+                                  int N, int32_t* __restrict__ branch_ok, int R) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i == 0) {
     *ticket = 0;
     *done = 0;
+    *ndefer = 0;
   }
   if (i < N) slot[i] = 0;  // not posted
   if (i < R) branch_ok[i] = 1;  // cleared by any workgroup of the branch that finds a problem
@@ -360,6 +381,66 @@ struct Unit {
   }
 };
 
+// Pass C of the streaming form: grad[u] = q_u * (c1 where q_u < p_u, else
+// c0) over one row, all kThreads threads of the workgroup.
+template <bool BF16, bool VECTOR, bool GBF16>
+__device__ __forceinline__ void stream_grad(const FusedArgs& a, size_t row, const void* zrow,
+                                            const void* trow, float nlz, float nlt, float c1,
+                                            float c0) {
+  using U = Unit<BF16, VECTOR>;
+  constexpr int NV = U::NV;
+  constexpr int ESZ = BF16 ? 2 : 4;
+  const int tid = threadIdx.x;
+  const int V = a.V;
+  const int units = V / NV;
+  const int e0 = units * NV;
+  auto load1 = [&](const void* rowp, int e) -> float {
+    if constexpr (BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(rowp)[e]);
+    else return reinterpret_cast<const float*>(rowp)[e];
+  };
+  auto gradv = [&](float z, float t) {
+    float lq, lp;
+    log2probs(z, t, nlz, nlt, lq, lp);
+    return fast_exp2(lq) * (lq < lp ? c1 : c0);
+  };
+  stream_pairs<VECTOR, true>(zrow, trow, 0, units, ESZ, [&](const auto& zw, const auto& tw, int u) {
+    float gv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) gv[i] = gradv(U::get(zw, i), U::get(tw, i));
+    if constexpr (VECTOR) {
+      if constexpr (GBF16) {
+        uint16_t* o = reinterpret_cast<uint16_t*>(a.grad) + row + size_t(u) * NV;
+        if constexpr (NV == 8) {
+          const u32x4 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]),
+                           pack_bf16x2(gv[4], gv[5]), pack_bf16x2(gv[6], gv[7])};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
+        } else {
+          const u32x2 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(o));
+        }
+      } else {
+        float* o = reinterpret_cast<float*>(a.grad) + row + size_t(u) * NV;
+#pragma unroll
+        for (int i = 0; i < NV; i += 4)
+          __builtin_nontemporal_store(f32x4{gv[i], gv[i + 1], gv[i + 2], gv[i + 3]},
+                                      reinterpret_cast<f32x4*>(o + i));
+      }
+    } else {
+      if constexpr (GBF16)
+        reinterpret_cast<uint16_t*>(a.grad)[row + u] = f32_to_bf16(gv[0]);
+      else
+        reinterpret_cast<float*>(a.grad)[row + u] = gv[0];
+    }
+  });
+  for (int e = e0 + tid; e < V; e += kThreads) {
+    const float gv = gradv(load1(zrow, e), load1(trow, e));
+    if constexpr (GBF16)
+      reinterpret_cast<uint16_t*>(a.grad)[row + e] = f32_to_bf16(gv);
+    else
+      reinterpret_cast<float*>(a.grad)[row + e] = gv;
+  }
+}
+
 template <bool BF16, bool VECTOR, bool GRAD, bool GBF16>
 __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a) {
   using U = Unit<BF16, VECTOR>;
@@ -370,8 +451,10 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   __shared__ float s_val[4];
 
   const int tid = threadIdx.x;
-  if (tid == 0)
+  if (tid == 0) {
     s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_val[2] = 0.f;
+  }
   __syncthreads();
   const int n = s_unit;
   const int r = n / a.Wn;
@@ -426,52 +509,39 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   block_sum2<kThreads>(al, g, red);
 
   // ---- post, wait for the branch, scan
-  if (tid < 64) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val);
+  if (tid < 64) post_and_scan(a, n, r, j, pack_slot(al, g), true, GRAD || j == 0, true, nlz, nlt, s_val);
   if constexpr (!GRAD) return;
   __syncthreads();
+  if (s_val[2] != 0.f) return;  // handed to the rescue kernel
 
   // ---- pass C: gradient
-  const float c1 = s_val[0], c0 = s_val[1];
-  auto gradv = [&](float z, float t) {
-    float lq, lp;
-    log2probs(z, t, nlz, nlt, lq, lp);
-    return fast_exp2(lq) * (lq < lp ? c1 : c0);
-  };
-  stream_pairs<VECTOR, true>(zrow, trow, 0, units, ESZ, [&](const auto& zw, const auto& tw, int u) {
-    float gv[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) gv[i] = gradv(U::get(zw, i), U::get(tw, i));
-    if constexpr (VECTOR) {
-      if constexpr (GBF16) {
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.grad) + row + size_t(u) * NV;
-        if constexpr (NV == 8) {
-          const u32x4 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]),
-                           pack_bf16x2(gv[4], gv[5]), pack_bf16x2(gv[6], gv[7])};
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(o));
-        } else {
-          const u32x2 w = {pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(o));
-        }
-      } else {
-        float* o = reinterpret_cast<float*>(a.grad) + row + size_t(u) * NV;
-#pragma unroll
-        for (int i = 0; i < NV; i += 4)
-          __builtin_nontemporal_store(f32x4{gv[i], gv[i + 1], gv[i + 2], gv[i + 3]},
-                                      reinterpret_cast<f32x4*>(o + i));
-      }
-    } else {
-      if constexpr (GBF16)
-        reinterpret_cast<uint16_t*>(a.grad)[row + u] = f32_to_bf16(gv[0]);
-      else
-        reinterpret_cast<float*>(a.grad)[row + u] = gv[0];
+  stream_grad<BF16, VECTOR, GBF16>(a, row, zrow, trow, nlz, nlt, s_val[0], s_val[1]);
+}
+
+// Rows whose wait for their branch gave up in the main kernel: every row has
+// posted by now (this kernel runs after it on the same stream), so the scan
+// finds every slot at once; the gradient is the streaming pass C with the
+// row's stored log-sum-exps, i.e. the same arithmetic the row would have done.
+template <bool BF16, bool VECTOR, bool GRAD, bool GBF16>
+__global__ __launch_bounds__(kThreads) void e2etv_rescue_kernel(const FusedArgs a) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  __shared__ float s_val[4];
+  const int cnt = *a.ndefer;
+  const int tid = threadIdx.x;
+  for (int i = blockIdx.x; i < cnt; i += gridDim.x) {
+    const int n = a.defer[i];
+    const int r = n / a.Wn;
+    const int j = n - r * a.Wn;
+    const float2 l = a.lse[n];
+    if (tid < 64) post_and_scan(a, n, r, j, 0ull, false, true, false, l.x, l.y, s_val);
+    if constexpr (GRAD) {
+      __syncthreads();
+      const size_t row = size_t(n) * size_t(a.V);
+      stream_grad<BF16, VECTOR, GBF16>(a, row, static_cast<const char*>(a.draft) + row * ESZ,
+                                       static_cast<const char*>(a.target) + row * ESZ, l.x, l.y,
+                                       s_val[0], s_val[1]);
+      __syncthreads();  // s_val is rewritten by the next row
     }
-  });
-  for (int e = e0 + tid; e < V; e += kThreads) {
-    const float gv = gradv(load1(zrow, e), load1(trow, e));
-    if constexpr (GBF16)
-      reinterpret_cast<uint16_t*>(a.grad)[row + e] = f32_to_bf16(gv);
-    else
-      reinterpret_cast<float*>(a.grad)[row + e] = gv;
   }
 }
 
@@ -566,8 +636,10 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   __shared__ float s_val[4];
 
   const int tid = threadIdx.x, wave = tid >> 6;
-  if (tid == 0)
+  if (tid == 0) {
     s_unit = __hip_atomic_fetch_add(a.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_val[2] = 0.f;
+  }
   __syncthreads();
   // uniform: the row's addresses and buffer resources stay in scalar registers
   const int n = __builtin_amdgcn_readfirstlane(s_unit);
@@ -691,9 +763,10 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   block_sum2<kResThreads>(al, g, red);
 
   // ---- post, wait for the branch, scan
-  if (tid < 64) post_and_scan(a, n, r, j, al, g, GRAD || j == 0, s_val);
+  if (tid < 64) post_and_scan(a, n, r, j, pack_slot(al, g), true, GRAD || j == 0, true, nlz, nlt, s_val);
   if constexpr (!GRAD) return;
   __syncthreads();
+  if (s_val[2] != 0.f) return;  // handed to the rescue kernel
 
   // ---- pass C: gradient, streamed quads first
   reopen(zr);
@@ -785,7 +858,8 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.spin_limit = spin_limit;
   f.slot = reinterpret_cast<unsigned long long*>(a.ws + L.slot);
   f.ticket = reinterpret_cast<int32_t*>(a.ws + L.ticket);
-  f.done = f.ticket + 32;  // the next 128-byte line of the ticket's block
+  f.done = reinterpret_cast<int32_t*>(a.ws + e2etv_done_offset(L));
+  f.ndefer = reinterpret_cast<int32_t*>(a.ws + e2etv_ndefer_offset(L));
   f.R = R;
   f.numer = reinterpret_cast<double*>(a.ws + L.numer);
   f.loss_out = a.loss_out;
@@ -793,8 +867,11 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.alpha_out = a.alpha_out;
   f.prefix_out = a.prefix_out;
   f.grad = a.grad;
-  e2etv_zero_kernel<<<(N + 255) / 256, 256, 0, s>>>(f.ticket, f.done, f.slot, N, f.branch_ok, R);
+  f.defer = reinterpret_cast<int32_t*>(a.ws + L.defer);
+  f.lse = reinterpret_cast<float2*>(a.ws + L.lse);
+  e2etv_zero_kernel<<<(N + 255) / 256, 256, 0, s>>>(f.ticket, f.done, f.ndefer, f.slot, N, f.branch_ok, R);
   const unsigned grid = unsigned(N);
+  const unsigned rgrid = unsigned(N < 256 ? N : 256);
   timing_mark(1, 0, s);
   if constexpr (BF16 && VECTOR) {
     if (!a.grad)
@@ -810,6 +887,15 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   else
     e2etv_fused_kernel<BF16, VECTOR, true, false><<<grid, kThreads, 0, s>>>(f);
   timing_mark(1, 1, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // rows whose wait gave up (normally none: the launch finds an empty list)
+  if (!a.grad)
+    e2etv_rescue_kernel<BF16, VECTOR, false, false><<<rgrid, kThreads, 0, s>>>(f);
+  else if (d.grad_dtype == SPECOPD_BF16)
+    e2etv_rescue_kernel<BF16, VECTOR, true, true><<<rgrid, kThreads, 0, s>>>(f);
+  else
+    e2etv_rescue_kernel<BF16, VECTOR, true, false><<<rgrid, kThreads, 0, s>>>(f);
   return hipGetLastError();
 }
 
@@ -820,7 +906,11 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   E2etvWs w{};
   size_t off = 0;
   w.slot = off;      off = align_up(off + N * sizeof(unsigned long long), 256);
-  w.ticket = off;    off = align_up(off + 256, 256);  // ticket, and the done count 128 bytes on
+  // ticket, then the count of reported branches and the count of deferred
+  // rows, each on a 128-byte line of its own
+  w.ticket = off;    off = align_up(off + 384, 256);
+  w.defer = off;     off = align_up(off + N * sizeof(int32_t), 256);
+  w.lse = off;       off = align_up(off + N * 2 * sizeof(float), 256);
   w.numer = off;     off = align_up(off + size_t(d.R) * sizeof(double), 256);
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
   w.total = off;
@@ -828,7 +918,7 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
 }
 
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s) {
-  const int spin_limit = a.spin_limit > 0 ? a.spin_limit : (1 << 20);
+  const int spin_limit = d.wait_polls > 0 ? d.wait_polls : (1 << 20);
   const size_t esz = d.logits_dtype == SPECOPD_BF16 ? 2 : 4;
   const bool vec = (size_t(d.V) * esz) % 16 == 0 &&
                    (reinterpret_cast<uintptr_t>(a.draft) % 16) == 0 &&

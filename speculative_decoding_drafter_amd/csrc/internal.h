@@ -133,13 +133,19 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
 // Workspace layout:
 //   slot       u64    [N]     (alpha, G) of every row, top bit set once posted
 //   ticket     int32          next row to hand out, in order; 128 bytes on, the
-//                             count of branches that reported their numerator
+//                             count of branches that reported their numerator;
+//                             256 bytes on, the count of deferred rows
+//   defer      int32  [N]     rows whose wait for their branch gave up
+//   lse        float2 [N]     their -log2-sum-exp2 of draft and target
 //   numer      double [R]     sum of prefix products of each branch
 //   branch_ok  int32  [R]
 struct E2etvWs {
-  size_t slot, ticket, numer, branch_ok, total;
+  size_t slot, ticket, defer, lse, numer, branch_ok, total;
 };
 E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d);
+// byte offsets of the count of reported branches and of deferred rows
+inline size_t e2etv_done_offset(const E2etvWs& w) { return w.ticket + 128; }
+inline size_t e2etv_ndefer_offset(const E2etvWs& w) { return w.ticket + 256; }
 
 
 struct E2etvArgs {
@@ -149,9 +155,9 @@ struct E2etvArgs {
   double* loss_out;
   void* grad;
   char* ws;
-  int spin_limit;  // bound on a workgroup's wait for its branch (<= 0: default)
 };
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s);
+
 
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`

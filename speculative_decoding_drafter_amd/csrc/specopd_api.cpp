@@ -2,7 +2,6 @@
 // HIP call), workspace sizing, dispatch to the kernel launchers, and the
 // device-status readback.  Nothing here throws across the ABI.
 #include <math.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -284,28 +283,30 @@ specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc, const void*
   a.draft = draft_logits; a.target = target_logits; a.parent = parent;
   a.alpha_out = alpha_out; a.prefix_out = prefix_out; a.loss_out = loss_out;
   a.grad = grad_draft; a.ws = static_cast<char*>(workspace);
-  // Test hook: a small bound on the in-kernel wait forces the timeout path
-  // (the affected branches are reported as malformed; nothing hangs).
-  if (const char* sl = getenv("SPECOPD_E2ETV_SPIN_LIMIT")) a.spin_limit = atoi(sl);
   hipError_t e = launch_e2etv(*desc, a, stream);
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
 }
 
 specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc, const void* workspace,
                                            size_t workspace_bytes, int32_t* bad_branches,
-                                           hipStream_t stream) {
+                                           int32_t* deferred_rows, hipStream_t stream) {
   specopd_status st = check_e2etv_desc(desc);
   if (st != SPECOPD_OK) return st;
   const E2etvWs L = e2etv_ws_layout(*desc);
   if (!workspace || workspace_bytes < L.total) return SPECOPD_ERR_WORKSPACE;
   std::vector<int32_t> ok(size_t(desc->R));
+  int32_t deferred = 0;
+  const char* ws = static_cast<const char*>(workspace);
   if (hipStreamSynchronize(stream) != hipSuccess) return SPECOPD_ERR_HIP;
-  if (hipMemcpy(ok.data(), static_cast<const char*>(workspace) + L.branch_ok,
-                ok.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(ok.data(), ws + L.branch_ok, ok.size() * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+          hipSuccess ||
+      hipMemcpy(&deferred, ws + e2etv_ndefer_offset(L), sizeof(int32_t), hipMemcpyDeviceToHost) !=
+          hipSuccess)
     return SPECOPD_ERR_HIP;
   int32_t bad = 0;
   for (int32_t x : ok) bad += (x == 0);
   if (bad_branches) *bad_branches = bad;
+  if (deferred_rows) *deferred_rows = deferred;
   return bad ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
 }
 

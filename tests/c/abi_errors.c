@@ -40,7 +40,7 @@ int main(void) {
                                1u << 30, NULL),
          SPECOPD_ERR_INVALID_ARGUMENT);
 
-  specopd_e2etv_desc ed = {4, 7, 151936, SPECOPD_BF16, SPECOPD_F32, 0.0, 1.0f, 0u};
+  specopd_e2etv_desc ed = {4, 7, 151936, SPECOPD_BF16, SPECOPD_F32, 0.0, 1.0f, 0u, 0};
   EXPECT(specopd_e2etv_workspace_size(&ed, &bytes), SPECOPD_OK);
   {
     char* f = (char*)fake; /* distinct, aligned stand-ins: no argument aliases another */

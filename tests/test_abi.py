@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.specopd_version() == 1
+    assert sd.specopd_version() == 2
     assert sd.status_string(0) == "ok"
     for s in (-1, -2, -3, -4, -5):
         assert sd.status_string(s) not in ("ok", "unknown status")
@@ -161,7 +161,7 @@ def test_status_readback_rejects_bad_workspace_before_gpu():
                                                   ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE
     e = _edesc()
     assert sd.LIB.specopd_e2etv_device_status(ctypes.byref(e), ctypes.c_void_p(FAKE), 1,
-                                              ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE
+                                              ctypes.byref(bad), None, None) == sd.SPECOPD_ERR_WORKSPACE
 
 
 def _pdesc(**kw):
