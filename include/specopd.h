@@ -253,6 +253,33 @@ specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
                                            int32_t* bad_branches, int32_t* deferred_rows,
                                            hipStream_t stream);
 
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same
+ * computation as specopd_e2etv_fwd_bwd, with the workspace taken from a
+ * static device array of SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library allocation); its first call on
+ * a GPU looks up that GPU's copy of the array.
+ *
+ *   Arguments are those of specopd_e2etv_fwd_bwd without the workspace.
+ *   Returns SPECOPD_ERR_WORKSPACE, before any HIP call, when the call needs
+ *   more than SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES of workspace
+ *   (specopd_e2etv_workspace_size), e.g. more than ~200,000 rows.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call clears what must start at zero itself): calls that
+ * overlap on one GPU -- on different streams, or from different threads --
+ * race and must not be issued.  Malformed branches show as NaN outputs; the
+ * device status of this call is not kept for specopd_e2etv_device_status.
+ */
+#define SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES (4u << 20)
+specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
+                                             const void* draft_logits, const void* target_logits,
+                                             const int32_t* parent, float* alpha_out,
+                                             float* prefix_out, double* loss_out, void* grad_draft,
+                                             hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing, for measurement harnesses.
  *

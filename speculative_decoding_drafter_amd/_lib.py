@@ -26,10 +26,13 @@ SPECOPD_ERR_DEVICE_VALIDATION = -5
 SPECOPD_F32 = 0
 SPECOPD_BF16 = 1
 
+E2ETV_NOALLOC_SCRATCH_BYTES = 4 << 20  # SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES
+
 # every symbol include/specopd.h declares
 EXPORTS = (
     "specopd_tree_attn_workspace_size", "specopd_tree_attn_fwd", "specopd_tree_attn_device_status",
     "specopd_e2etv_workspace_size", "specopd_e2etv_fwd_bwd", "specopd_e2etv_device_status",
+    "specopd_e2etv_fwd_bwd_noalloc",
     "specopd_prefill_workspace_size", "specopd_prefill_fwd",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
@@ -71,6 +74,7 @@ def _load():
                                                     POINTER(c_int32), P]
     lib.specopd_e2etv_workspace_size.argtypes = [POINTER(E2etvDesc), POINTER(c_size_t)]
     lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P, c_size_t, P]
+    lib.specopd_e2etv_fwd_bwd_noalloc.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P]
     lib.specopd_e2etv_device_status.argtypes = [POINTER(E2etvDesc), P, c_size_t,
                                                 POINTER(c_int32), POINTER(c_int32), P]
     lib.specopd_prefill_workspace_size.argtypes = [POINTER(PrefillDesc), POINTER(c_size_t)]
@@ -219,6 +223,17 @@ def specopd_e2etv_fwd_bwd(desc, draft, target, parent, alpha_out, prefix_out, lo
         return st
     if st != SPECOPD_OK:
         raise SpecopdError(st, "specopd_e2etv_fwd_bwd")
+
+
+def specopd_e2etv_fwd_bwd_noalloc(desc, draft, target, parent, alpha_out, prefix_out, loss_out, grad,
+                                  stream=None, raw_status=False):
+    st = LIB.specopd_e2etv_fwd_bwd_noalloc(
+        ctypes.byref(desc), _ptr(draft), _ptr(target), _ptr(parent), _ptr(alpha_out),
+        _ptr(prefix_out), _ptr(loss_out), _ptr(grad), _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_e2etv_fwd_bwd_noalloc")
 
 
 def specopd_e2etv_device_status(desc, workspace, stream=None, with_deferred=False):

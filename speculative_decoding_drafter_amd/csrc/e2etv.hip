@@ -33,6 +33,7 @@
 // The branch that reports last sums the branch numerators in a fixed order
 // (loss), so no further kernel runs after the rows.
 // No floating-point atomics: results are bitwise reproducible.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -915,6 +916,36 @@ E2etvWs e2etv_ws_layout(const specopd_e2etv_desc& d) {
   w.branch_ok = off; off = align_up(off + size_t(d.R) * sizeof(int32_t), 256);
   w.total = off;
   return w;
+}
+
+// ---------------------------------------------------------------- static scratch
+// The workspace of specopd_e2etv_fwd_bwd_noalloc: one array per GPU, held by
+// the library until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); the
+// device address of each GPU's copy is looked up once, with that GPU
+// current, and kept.
+static __device__ __align__(256) char scratch[kE2etvScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t e2etv_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s) {

@@ -158,6 +158,10 @@ struct E2etvArgs {
 };
 hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream_t s);
 
+// Static scratch of specopd_e2etv_fwd_bwd_noalloc (e2etv.hip): the device
+// address of the current GPU's copy, looked up on first use per GPU.
+constexpr size_t kE2etvScratchBytes = SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES;
+hipError_t e2etv_scratch(void** ptr);
 
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`

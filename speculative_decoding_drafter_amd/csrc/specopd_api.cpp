@@ -287,6 +287,32 @@ specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc, const void*
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
 }
 
+specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc, const void* draft_logits,
+                                             const void* target_logits, const int32_t* parent,
+                                             float* alpha_out, float* prefix_out, double* loss_out,
+                                             void* grad_draft, hipStream_t stream) {
+  specopd_status st = check_e2etv_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!draft_logits || !target_logits || !parent || !loss_out) return SPECOPD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {draft_logits, target_logits, parent, loss_out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if ((alpha_out && !aligned16(alpha_out)) || (prefix_out && !aligned16(prefix_out)) ||
+      (grad_draft && !aligned16(grad_draft)))
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (grad_draft && (grad_draft == draft_logits || grad_draft == target_logits))
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (e2etv_ws_layout(*desc).total > kE2etvScratchBytes) return SPECOPD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (e2etv_scratch(&ws) != hipSuccess) return SPECOPD_ERR_HIP;
+  E2etvArgs a{};
+  a.draft = draft_logits; a.target = target_logits; a.parent = parent;
+  a.alpha_out = alpha_out; a.prefix_out = prefix_out; a.loss_out = loss_out;
+  a.grad = grad_draft; a.ws = static_cast<char*>(ws);
+  hipError_t e = launch_e2etv(*desc, a, stream);
+  return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
 specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc, const void* workspace,
                                            size_t workspace_bytes, int32_t* bad_branches,
                                            int32_t* deferred_rows, hipStream_t stream) {

@@ -264,3 +264,25 @@ def test_header_is_plain_c_and_the_library_links_from_c(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr
+
+
+def test_noalloc_rejects_host_errors_before_the_gpu():
+    """The allocation-free E2E-TV call refuses, before any HIP call, a call
+    whose workspace would exceed its static scratch, and bad arguments."""
+    P = ctypes.c_void_p
+    big = _edesc(R=1_000_000, Wn=7, V=16)
+    n = ctypes.c_size_t(0)
+    assert sd.LIB.specopd_e2etv_workspace_size(ctypes.byref(big), ctypes.byref(n)) == 0
+    assert n.value > sd.E2ETV_NOALLOC_SCRATCH_BYTES
+
+    def call(desc, **over):
+        a = dict(draft=FAKE, target=FAKE + 16, parent=FAKE + 32, alpha=FAKE + 48, prefix=FAKE + 64,
+                 loss=FAKE + 80, grad=FAKE + 96)
+        a.update(over)
+        return sd.LIB.specopd_e2etv_fwd_bwd_noalloc(
+            ctypes.byref(desc), P(a["draft"]), P(a["target"]), P(a["parent"]), P(a["alpha"]),
+            P(a["prefix"]), P(a["loss"]), P(a["grad"]), P(None))
+    assert call(big) == sd.SPECOPD_ERR_WORKSPACE
+    assert call(_edesc(), draft=0) == sd.SPECOPD_ERR_INVALID_ARGUMENT
+    assert call(_edesc(), grad=FAKE) == sd.SPECOPD_ERR_INVALID_ARGUMENT  # grad aliases draft
+    assert call(_edesc(Wn=65)) == sd.SPECOPD_ERR_UNSUPPORTED
