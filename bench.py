@@ -7,15 +7,21 @@ over the scored rows (specopd_e2etv_fwd_bwd).  The timed steps replay the step
 captured once as a HIP graph (every kernel of both calls runs in every
 replay); --eager times plain calls, and the JSON line carries both.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--also 2,5]
 
-Prints one JSON line.  `value` is scored branch rows per second through the
-whole step.  `roofline` describes the kernel that takes most of the step,
-timed with HIP events on the stream it runs on; `roofline_attn` /
-`roofline_loss` give both parts.  `prefill` measures, separately, the trunk
-prefill that fills the cache (specopd_prefill_fwd) on the workload's trunks.
-`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
-workload (reported, not a target).
+Prints one JSON line for the workload (default: the batch of 8 trunks of
+8192 tokens, 128 branches of 16 nodes each, 32/8 heads of 128, and its
+16,384 x 151,936 bf16 logit rows -- the largest configuration on one GPU).
+`value` is scored branch rows per second through the whole step.  `roofline`
+describes the kernel that takes most of the step, timed with HIP events on
+the stream it runs on; `roofline_attn` / `roofline_loss` give both parts,
+with the HBM bytes and matrix-core / vector-ALU busy fractions of the
+rocprofv3 counter summaries under profiles/ while those match the kernel
+sources.  `other_workloads` repeats the measurement for the --also
+workloads.  `prefill` measures, separately, the trunk prefill that fills the
+cache (specopd_prefill_fwd) on the workload's trunks.  `cpu_baseline` times
+the fp64 CPU oracle on a bounded sample of the same workload, on one core and
+on every usable core (reported, not a target).
 """
 
 from __future__ import annotations
@@ -51,30 +57,6 @@ def loss_bytes(cfg, grad_bytes=4):
     gradient once, plus 12 bytes of per-row scalars."""
     s_in = 2 if cfg.dtype == "bf16" else 4
     return cfg.N * cfg.V * (2 * s_in + grad_bytes) + 12 * cfg.N
-
-
-def measured_traffic(kernel_tag, src_files):
-    """HBM bytes per launch of a kernel from the committed counter summary
-    (profiles/<kernel_tag>.txt), or None when the kernel source has changed
-    since the counters were taken (the summary records its sha256)."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", kernel_tag + ".txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in src_files:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if kv.get("source_sha256") != h.hexdigest():
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
 
 
 def time_graph(step, stream, steps):
@@ -142,11 +124,7 @@ def bench_prefill(sd, wl, seed, steps, warmup, dev, stream):
     fl = prefill_flops(ac)
     tf = fl / (kern_ms / 1e3) / 1e12
     peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
-    t_pf = measured_traffic(f"prefill_mfma_{wl.name}",
-                            ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
-                             "speculative_decoding_drafter_amd/csrc/device_common.h",
-                             "speculative_decoding_drafter_amd/csrc/internal.h",
-                             "speculative_decoding_drafter_amd/build.py"])
+    t_pf = _counter(profile_summary(f"prefill_mfma_{wl.name}", ATTN_SRC), "hbm_bytes_per_launch")
     return {
         "metric": "trunk prefill tokens/s", "value": ac.T * ac.L / (call_ms / 1e3),
         "unit": "tokens/s", "calls": n, "call_ms": call_ms,
@@ -160,78 +138,133 @@ def bench_prefill(sd, wl, seed, steps, warmup, dev, stream):
     }
 
 
-def cpu_baseline(wl, attn_inp_cpu, loss_inp_cpu, budget_s=12.0):
-    """The fp64 oracle as it stands, single BLAS thread, on a bounded sample:
-    whole branches (every node, every head) of attention and their loss rows,
-    in a seeded order, going round the branches again until budget_s of CPU
-    work.  Returns scored rows per second."""
-    import numpy as np
+_CPU = {}
+
+
+def _cpu_init():
     from threadpoolctl import threadpool_limits
+    import torch
+    torch.set_num_threads(1)
+    _CPU["lim"] = threadpool_limits(limits=1)
+
+
+def _cpu_branch(i):
+    """One whole branch of the sample through the oracle: tree attention of
+    every node and head, then its E2E-TV rows (forward and gradient)."""
     import oracle
-    rows = 0
-    t_total = 0.0
-    nb = 0
-    with threadpool_limits(limits=1):
-        cfg = wl.attn if wl.attn is not None else None
-        lc = wl.loss
-        R = lc.R
-        order = np.random.default_rng(0).permutation(R)
-        for i in range(1 << 30):
-            r = order[i % R]
-            t0 = time.perf_counter()
-            if cfg is not None:
-                t, b = divmod(int(r), cfg.B)
-                if t < cfg.T:
-                    c = attn_inp_cpu
-                    oracle.tree_attention(c["trunk_k"], c["trunk_v"], c["q"], c["k"], c["v"],
-                                          c["anchors"], c["parent"], c["pos"], branches=[(t, b)])
-            d = loss_inp_cpu
-            oracle.e2etv_branch(d["draft"][r], d["target"][r], d["parent"][r].numpy(), float(lc.N))
-            t_total += time.perf_counter() - t0
-            rows += lc.Wn
-            nb += 1
-            if t_total >= budget_s:
-                break
-    return rows / t_total, nb, t_total
+    d = _CPU
+    b = i % d["nb"]
+    if d["attn"] is not None:
+        tk, tv, q, k, v, anc, par, pos = d["attn"]
+        oracle.tree_attention_branch(tk, tv, q[b], k[b], v[b], anc[b], par[b], pos[b])
+    oracle.e2etv_branch(d["draft"][b], d["target"][b], d["lparent"][b], d["count"])
+    return b
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2, help="1..5 (default: the 8B-shaped layer)")
-    ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
-    ap.add_argument("--eager", action="store_true",
-                    help="time plain calls instead of replays of the step captured as a HIP graph")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="also run one plain device copy of MIB MiB (counter calibration)")
-    args = ap.parse_args()
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    if args.gpus != 1:
-        print(f"bench.py: the scoring path runs on one GPU; --gpus {args.gpus} is not supported "
-              "(trunks, and whole branches of the loss, would be the units sharded across GPUs; "
-              "only the loss numerators would then be summed across them).", file=sys.stderr)
-        sys.exit(2)
 
+def cpu_baseline(wl, seed, budget_s=16.0, max_workers=16):
+    """The fp64 oracle as it stands on a bounded sample of the workload: whole
+    branches (tree attention of every node and head against the full trunk,
+    then the branch's E2E-TV rows with the workload's global count), drawn
+    from the same configuration on the host.  Runs before anything touches
+    the GPU, in forked worker processes, each with one BLAS thread: first one
+    worker for about budget_s/2, then every usable core (at most max_workers)
+    for about as long.  Returns (rows/s on all cores, rows/s on one core,
+    workers, branches timed, seconds)."""
+    import multiprocessing as mp
+    import numpy as np
+    from synthetic import gen_attn, gen_loss, shrink_attn, shrink_loss
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    nb = min(wl.loss.R, 2 * workers)
+    lc = wl.loss
+    li = gen_loss(shrink_loss(lc, R=nb), seed, device="cpu", cid=wl.cid)
+    _CPU.update(nb=nb, draft=li["draft"], target=li["target"], lparent=li["parent"].numpy(),
+                count=float(lc.N), attn=None)
+    if wl.attn is not None:
+        ac = shrink_attn(wl.attn, T=1, B=min(wl.attn.B, nb))
+        ai = gen_attn(ac, seed, device="cpu", cid=wl.cid)
+        f64 = lambda x: x[0].double().numpy()
+        _CPU["attn"] = (f64(ai["trunk_k"]), f64(ai["trunk_v"]), f64(ai["q"]), f64(ai["k"]), f64(ai["v"]),
+                        ai["anchors"][0].numpy(), ai["parent"][0].numpy(), ai["pos"][0].numpy())
+        _CPU["nb"] = min(nb, ac.B)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(1, initializer=_cpu_init) as pool:
+        n1, t1 = 0, 0.0
+        t0 = time.perf_counter()
+        while t1 < budget_s / 2:
+            pool.apply(_cpu_branch, (n1,))
+            n1 += 1
+            t1 = time.perf_counter() - t0
+    per_branch = t1 / n1
+    k = max(1, int(round(budget_s / 2 / per_branch)))
+    with ctx.Pool(workers, initializer=_cpu_init) as pool:
+        pool.map(_cpu_init_probe, range(workers), chunksize=1)  # workers up before the clock starts
+        t0 = time.perf_counter()
+        pool.map(_cpu_branch, range(workers * k), chunksize=1)
+        tw = time.perf_counter() - t0
+    rows_w = workers * k * lc.Wn
+    return rows_w / tw, n1 * lc.Wn / t1, workers, n1 + workers * k, t1 + tw
+
+
+def _cpu_init_probe(i):
+    return i
+
+
+def profile_summary(tag, src_files):
+    """Key/value lines of profiles/<tag>.txt when the kernel sources it names
+    are unchanged since it was taken (its source_sha256), else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", tag + ".txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in src_files:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return kv if kv.get("source_sha256") == h.hexdigest() else None
+
+
+ATTN_SRC = ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
+            "speculative_decoding_drafter_amd/csrc/device_common.h",
+            "speculative_decoding_drafter_amd/csrc/internal.h",
+            "speculative_decoding_drafter_amd/build.py"]
+LOSS_SRC = ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
+            "speculative_decoding_drafter_amd/csrc/device_common.h",
+            "speculative_decoding_drafter_amd/csrc/internal.h",
+            "speculative_decoding_drafter_amd/build.py"]
+
+
+def _counter(kv, key):
+    try:
+        return float(kv[key]) if kv is not None and key in kv else None
+    except ValueError:
+        return None
+
+
+def measure(sd, wl, args, dev):
+    """One workload: W warm-up steps, K eager steps with per-call events, K
+    steps again with the library's kernel events, then K replays of the step
+    captured as a HIP graph (the timed value unless --eager)."""
     import numpy as np
     import torch
-
-    import speculative_decoding_drafter_amd as sd
-    from synthetic import WORKLOADS, gen_attn, gen_loss
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = "cuda:0"
-    wl = WORKLOADS[args.workload]
-    torch.manual_seed(args.seed)
+    from synthetic import gen_attn, gen_loss
 
     ai = gen_attn(wl.attn, args.seed, device=dev, cid=wl.cid) if wl.attn is not None else None
     li = gen_loss(wl.loss, args.seed, device=dev, cid=wl.cid)
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
     if ai is not None:
         ac = wl.attn
@@ -270,7 +303,7 @@ def main():
     torch.cuda.synchronize()
     if args.calibrate_copy > 0:
         # a plain copy of known size: hardware byte counters are read for it
-        # too, and the ratio converts the loss kernel's counters to bytes
+        # too, and the ratio converts the kernels' counters to bytes
         nbytes = args.calibrate_copy << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -304,13 +337,13 @@ def main():
     # a timed run only counts if every branch came out well formed
     if ai is not None and sd.specopd_tree_attn_device_status(adesc, aws) != 0:
         raise SystemExit("tree attention reported malformed branches")
-    if sd.specopd_e2etv_device_status(ldesc, lws) != 0:
-        raise SystemExit("E2E-TV reported malformed or timed-out branches")
+    bad, deferred = sd.specopd_e2etv_device_status(ldesc, lws, with_deferred=True)
+    if bad != 0:
+        raise SystemExit("E2E-TV reported malformed branches")
     eager_ms_step = t_start.elapsed_time(t_end) / args.steps
     # The timed steps: the whole step (every kernel of both calls) captured
     # once as a HIP graph and replayed, which removes the host launch gaps
-    # between its kernels; --eager times the plain calls instead (above, with
-    # per-call events).
+    # between its kernels; --eager times the plain calls instead.
     graph_ms_step = None
     graph_note = None
     if not args.eager:
@@ -322,18 +355,15 @@ def main():
     ms_step = graph_ms_step if graph_ms_step is not None else eager_ms_step
     attn_call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) if ai is not None else 0.0
     loss_call_ms = float(np.mean([(e[1] if ai is not None else e[0]).elapsed_time(e[2]) for e in evs])) \
-        if ai is not None else float(np.mean([t_start.elapsed_time(t_end) / args.steps]))
+        if ai is not None else eager_ms_step
     attn_ms = kern_ms[0] if kern_ms[0] else attn_call_ms
     loss_ms = kern_ms[1] if kern_ms[1] else loss_call_ms
 
     N = lc.N
-    rows_per_s = N / (ms_step / 1e3)
     res = {
-        "metric": METRIC, "value": rows_per_s, "unit": "rows/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if lc.dtype == "bf16" else "f32", "data": "synthetic",
+        "value": N / (ms_step / 1e3), "ms_per_step": ms_step,
         "graph": graph_ms_step is not None, "eager_ms_per_step": eager_ms_step,
+        "deferred_rows": deferred,
     }
     if graph_note:
         res["graph_note"] = graph_note
@@ -341,18 +371,15 @@ def main():
             "loss": {"R": lc.R, "Wn": lc.Wn, "V": lc.V, "logits": lc.dtype, "grad": "f32"}}
     lb = loss_bytes(lc)
     loss_gbs = lb / (loss_ms / 1e3) / 1e9
-    t_loss = measured_traffic(f"e2etv_resident_{wl.name}",
-                              ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
-                               "speculative_decoding_drafter_amd/csrc/device_common.h",
-                               "speculative_decoding_drafter_amd/csrc/internal.h",
-                               "speculative_decoding_drafter_amd/build.py"])
+    pl = profile_summary(f"e2etv_resident_{wl.name}", LOSS_SRC)
+    t_loss = _counter(pl, "hbm_bytes_per_launch")
     roof_loss = {"bound": "hbm", "achieved": loss_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": loss_gbs / HBM_PEAK_GBS,
                  "traffic": None if t_loss is None else t_loss / (loss_ms / 1e3) / 1e9,
                  "traffic_bytes_per_launch": t_loss,
+                 "valu_busy_pct": _counter(pl, "valu_busy_pct"),
                  "kernel": "e2etv_resident_kernel (specopd_e2etv_fwd_bwd)", "ms": loss_ms,
-                 "call_ms": loss_call_ms,
-                 "alg_bytes_per_launch": lb}
+                 "call_ms": loss_call_ms, "alg_bytes_per_launch": lb}
     roofs = {"loss": roof_loss}
     if ai is not None:
         ac = wl.attn
@@ -361,15 +388,13 @@ def main():
         fl = attn_flops(ac, ai["anchors"].cpu().numpy())
         tf = fl / (attn_ms / 1e3) / 1e12
         peak = BF16_PEAK_TFLOPS if ac.dtype == "bf16" else FP32_PEAK_TFLOPS
-        t_attn = measured_traffic(f"tree_attn_mfma_{wl.name}",
-                                  ["speculative_decoding_drafter_amd/csrc/tree_attn_mfma.hip",
-                                   "speculative_decoding_drafter_amd/csrc/device_common.h",
-                               "speculative_decoding_drafter_amd/csrc/internal.h",
-                               "speculative_decoding_drafter_amd/build.py"])
+        pa = profile_summary(f"tree_attn_mfma_{wl.name}", ATTN_SRC)
+        t_attn = _counter(pa, "hbm_bytes_per_launch")
         roofs["attn"] = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
                          "frac": tf / peak,
                          "traffic": None if t_attn is None else t_attn / (attn_ms / 1e3) / 1e9,
                          "traffic_unit": "GB/s", "traffic_bytes_per_launch": t_attn,
+                         "mfma_util_pct": _counter(pa, "mfma_util_pct"),
                          "kernel": "tree_attn_mfma_kernel (specopd_tree_attn_fwd)",
                          "ms": attn_ms, "call_ms": attn_call_ms, "alg_flops_per_launch": fl}
         res["attn_rows_per_s"] = ac.rows / (attn_call_ms / 1e3)
@@ -380,19 +405,81 @@ def main():
     res["roofline_loss"] = roofs["loss"]
     if "attn" in roofs:
         res["roofline_attn"] = roofs["attn"]
+    del ai, li, grad
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
-    if ai is not None and not args.no_prefill:
-        res["prefill"] = bench_prefill(sd, wl, args.seed, args.steps, args.warmup, dev, stream)
 
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="1..5 (default: the batch of 8 trunks, the largest single-GPU workload)")
+    ap.add_argument("--also", default="2,5",
+                    help="other workloads measured the same way and reported under other_workloads "
+                         "('' for none)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=16.0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
+    ap.add_argument("--eager", action="store_true",
+                    help="time plain calls instead of replays of the step captured as a HIP graph")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: the scoring path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(trunks, and whole branches of the loss, would be the units sharded across GPUs; "
+              "only the loss numerators would then be summed across them).", file=sys.stderr)
+        sys.exit(2)
+
+    from synthetic import WORKLOADS
+    wl = WORKLOADS[args.workload]
+    cpu = None
     if not args.no_cpu:
-        ai_c = {k: v.cpu() for k, v in ai.items()} if ai is not None else None
-        li_c = {k: v.cpu() for k, v in li.items()}
-        v_cpu, nb, secs = cpu_baseline(wl, ai_c, li_c, args.cpu_budget)
+        # before anything touches the GPU: the oracle's workers are forked
+        cpu = cpu_baseline(wl, args.seed, args.cpu_budget)
+
+    import torch
+    import speculative_decoding_drafter_amd as sd
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.manual_seed(args.seed)
+    m = measure(sd, wl, args, dev)
+    res = {
+        "metric": METRIC, "value": m.pop("value"), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": m.pop("ms_per_step"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.loss.dtype == "bf16" else "f32", "data": "synthetic",
+    }
+    res.update(m)
+    if wl.attn is not None and not args.no_prefill:
+        res["prefill"] = bench_prefill(sd, wl, args.seed, args.steps, args.warmup, dev,
+                                       torch.cuda.current_stream())
+    others = {}
+    for c in [int(x) for x in args.also.split(",") if x.strip()]:
+        if c == args.workload:
+            continue
+        o = measure(sd, WORKLOADS[c], args, dev)
+        keep = ("value", "ms_per_step", "eager_ms_per_step", "deferred_rows", "roofline_attn",
+                "roofline_loss")
+        others[o["config"]["workload"]] = {k: o[k] for k in keep if k in o}
+    if others:
+        res["other_workloads"] = others
+    if cpu is not None:
+        v_all, v_one, workers, nb, secs = cpu
         res["cpu_baseline"] = {
-            "value": v_cpu, "unit": "rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nb} whole branches of {lc.R}, seeded order, repeating ({nb * lc.Wn} scored "
-                      f"rows: tree attention over all heads + E2E-TV fwd/grad), fp64 numpy, "
-                      f"1 BLAS thread, {secs:.1f} s",
+            "value": v_all, "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "value_one_core": v_one, "cpu_model": cpu_model(),
+            "sample": f"{nb} whole branches of the {wl.name} configuration drawn on the host "
+                      f"(tree attention of every node and head against the full trunk + the "
+                      f"branch's E2E-TV forward/gradient rows), fp64 numpy, one BLAS thread per "
+                      f"worker; one worker, then {workers} forked workers, {secs:.1f} s in all",
         }
     print(json.dumps(res))
 
