@@ -75,8 +75,26 @@ typedef struct {
   specopd_dtype dtype; /* of trunk_k, trunk_v, q, k, v and out               */
   float rope_base;     /* rotary base; <= 0 means 10000                       */
   float scale;         /* score scale; <= 0 means 1/sqrt(D)                   */
-  uint32_t flags;      /* reserved, must be 0                                 */
+  uint32_t flags;      /* 0 or SPECOPD_TREE_BATCH_INVARIANT                   */
 } specopd_tree_attn_desc;
+
+/*
+ * Batch-invariant scoring (the deterministic mode behind the jaehun.me
+ * review's §3.2 "maintaining numerical consistency" and Table 4, where full
+ * recomputation, single and batched cached scoring and merged tree execution
+ * agree exactly): with this flag every output row is bitwise the same
+ * whatever else is in the call -- its pack partners, the number of branches
+ * or trunks, their order.  A row's keys are then always accumulated in one
+ * pass over the same 32-key tiles (its trunk keys 0..a_b at their absolute
+ * positions, then its own branch's nodes at fixed tile positions), never
+ * split into key ranges merged afterwards.  Without the flag, calls with too
+ * few (trunk, kv head, pack) units to fill the GPU split long packs into key
+ * ranges for speed, and a row's result can then differ in its last bits
+ * from the same row scored in another batch.  Calls that fill the GPU are
+ * scored the same way with or without the flag.  bf16 matrix-core path only
+ * (the fp32 path is batch-invariant always).
+ */
+#define SPECOPD_TREE_BATCH_INVARIANT 1u
 
 /* Bytes of device workspace specopd_tree_attn_fwd needs for `desc`. */
 specopd_status specopd_tree_attn_workspace_size(const specopd_tree_attn_desc* desc,

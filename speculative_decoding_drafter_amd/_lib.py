@@ -26,6 +26,8 @@ SPECOPD_ERR_DEVICE_VALIDATION = -5
 SPECOPD_F32 = 0
 SPECOPD_BF16 = 1
 
+SPECOPD_TREE_BATCH_INVARIANT = 1
+
 E2ETV_NOALLOC_SCRATCH_BYTES = 4 << 20  # SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES
 
 # every symbol include/specopd.h declares
@@ -256,12 +258,12 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def tree_attn(inp: dict, rope_base=10000.0, scale=0.0, ws=None, out=None):
+def tree_attn(inp: dict, rope_base=10000.0, scale=0.0, ws=None, out=None, flags=0):
     """Tree attention on generated inputs (dict of device tensors)."""
     q = inp["q"]
     T, B, Wn, Hq, D = q.shape
     L, Hkv = inp["trunk_k"].shape[1], inp["trunk_k"].shape[2]
-    desc = tree_attn_desc(T, L, B, Wn, Hq, Hkv, D, q.dtype, rope_base, scale)
+    desc = tree_attn_desc(T, L, B, Wn, Hq, Hkv, D, q.dtype, rope_base, scale, flags)
     if ws is None:
         ws = workspace(specopd_tree_attn_workspace_size(desc), q.device)
     if out is None:

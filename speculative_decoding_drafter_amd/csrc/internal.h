@@ -50,8 +50,8 @@ size_t mfma_slot_bytes(int D);
 // Key-range splits per pack: packs are split only when there are too few of
 // them to give every CU one workgroup (a workgroup fills a CU, and merging
 // split partials costs more than a second round of workgroups saves).
-inline int mfma_nsplit(long long units) {
-  if (units >= 256) return 1;
+inline int mfma_nsplit(long long units, bool batch_invariant = false) {
+  if (units >= 256 || batch_invariant) return 1;
   const long long s = (256 + units - 1) / units;
   return int(s < 16 ? s : 16);
 }
@@ -74,6 +74,9 @@ struct MfmaParams {
   uint16_t* out;                      // [T][B][Wn][Hq][D]
   int T, B, L, Wn, Hq, Hkv, G;
   int bpp;     // branches per pack
+  int spb;     // packs per branch (> 1 when a branch has more rows than a workgroup; bpp is 1 then)
+  int tstride; // tail keys per branch slot (Wn rounded up so each slot starts where a lone
+               // branch's would: a row's tail keys sit at the same tile positions in any pack)
   int npacks;  // packs per trunk
   int nsplit;  // key-range splits per pack
   int ugp;      // units per (trunk, kv head) group, padded to a multiple of ilv
@@ -82,6 +85,17 @@ struct MfmaParams {
   int ilv;      // XCD blocks a group's units are dealt across (1: none)
   int chunked;  // 1: consecutive units to one XCD; 0: units by block index
 };
+// Tail keys per branch slot of a tree call: the branch's Wn nodes from a
+// multiple of 16 (32, 64 for larger branches), so that in any pack a row's
+// own nodes occupy the same positions of a 32-key tile and of its 16-key
+// matrix-core steps as they would with the branch alone.
+inline int mfma_tail_stride(int Wn) { return Wn <= 16 ? 16 : Wn <= 32 ? 32 : 64; }
+// Key tiles of a pack whose longest anchor is `a` (-1: none well formed)
+// holding `nbr` branch slots of `tstride` keys, the last one Wn keys.
+__host__ __device__ inline int mfma_pack_tiles(int a, int nbr, int tstride, int Wn) {
+  return (a + 32) / 32 + ((nbr - 1) * tstride + Wn + 31) / 32;
+}
+
 // Grid of the matrix-core kernel from T, Hkv, npacks and nsplit.  With a
 // multiple of 8 (trunk, kv head) groups every XCD gets whole groups; with 1,
 // 2 or 4 groups each spans 8/groups XCDs, its packs dealt to them

@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void prefill_plan_kernel(const PrefillPlanPara
   auto tiles = [&](int pk) {
     const int b0 = pk * p.bpp, nbr = min(p.bpp, B - b0);
     const int amax = B - 1 - b0;
-    return (amax + 32) / 32 + (nbr + 31) / 32;
+    return mfma_pack_tiles(amax, nbr, 1, 1);
   };
   __shared__ int run[256];
   const int per = (np + 255) / 256;
@@ -337,6 +337,8 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
       p.out = static_cast<uint16_t*>(a.out) + (t0 + 1) * q_tok;
       p.T = 1; p.B = g.B; p.L = d.L; p.Wn = 1; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
       p.bpp = g.bpp;
+      p.spb = 1;
+      p.tstride = 1;  // one-node branches: each token's own key, packed densely
       p.npacks = g.np;
       p.nsplit = g.nsplit;
       mfma_grid(p);

@@ -23,7 +23,7 @@ specopd_status check_tree_desc(const specopd_tree_attn_desc* d) {
   if (d->Hq % d->Hkv != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->D != 64 && d->D != 128 && d->D != 256) return SPECOPD_ERR_UNSUPPORTED;
   if (d->dtype != SPECOPD_F32 && d->dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
-  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if ((d->flags & ~SPECOPD_TREE_BATCH_INVARIANT) != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (!(isfinite(d->rope_base) && isfinite(d->scale))) return SPECOPD_ERR_INVALID_ARGUMENT;
   // element counts must stay within what the kernels index with 32/64-bit math
   const double nodes = double(d->T) * d->B * d->Wn;

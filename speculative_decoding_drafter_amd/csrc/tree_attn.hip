@@ -89,7 +89,7 @@ struct PrepParams {
   uint64_t* anc;
   int32_t *branch_ok, *order, *pstart, *ustart, *umap, *ctr;
   uint16_t *qr, *kr;
-  int T, B, L, Wn, Hq, Hkv, D, bpp, npacks, nsplit;
+  int T, B, L, Wn, Hq, Hkv, D, bpp, spb, tstride, npacks, nsplit;
   double log2_base;
   float qmul;
 };
@@ -244,9 +244,10 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
       __syncthreads();
     }
     // key tiles of pack pk: trunk tiles up to its longest anchor, then tail
-    // tiles holding the pack's branch nodes
+    // tiles holding the pack's branch nodes (a branch split over spb packs
+    // gives each of them its trunk and its nodes)
     auto tiles = [&](int pk) {
-      const int b0 = pk * p.bpp;
+      const int b0 = (pk / p.spb) * p.bpp;
       const int nbr = min(p.bpp, B - b0);
       int a;
       if (staged) {
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
         const int bl = p.order[tB + b0];
         a = p.branch_ok[tB + bl] ? p.anchors[tB + bl] : -1;
       }
-      return (a + 32) / 32 + (nbr * Wn + 31) / 32;
+      return mfma_pack_tiles(a, nbr, p.tstride, Wn);
     };
     // exclusive prefix sums of the packs' tiles: per-thread runs, then a scan
     // of the 256 run totals
@@ -478,25 +479,41 @@ __global__ __launch_bounds__(256) void tree_attn_generic_kernel(
 
 // ---------------------------------------------------------------- launch
 
-// Matrix-core plan: branches per pack and packs per trunk; false when the
-// inputs are fp32 or a single branch's rows exceed one workgroup.
-static bool mfma_plan(const specopd_tree_attn_desc& d, int* bpp, int* npacks) {
+// Matrix-core plan: branches per pack, packs per branch and packs per trunk;
+// false for fp32 inputs.  A pack fills one workgroup with the rows (node x
+// query head of a kv group) of whole branches; a branch with more rows than
+// a workgroup holds is split over several packs, each scoring a slice of its
+// rows against all of its keys.
+struct MfmaPlan {
+  int bpp, spb, npacks, nsplit;
+};
+static bool mfma_plan(const specopd_tree_attn_desc& d, MfmaPlan* pl) {
   if (d.dtype != SPECOPD_BF16) return false;
-  const int rows_per_branch = d.Wn * (d.Hq / d.Hkv);
-  const int b = mfma_rows_per_wg(d.D) / rows_per_branch;
-  if (b < 1) return false;
   // per-trunk element offsets are formed in 32 bits
   const double lim = 2147483647.0;
   if (double(d.L) * d.Hkv * d.D > lim || double(d.B) * d.Wn * d.Hq * d.D > lim) return false;
-  *bpp = b;
-  *npacks = (d.B + b - 1) / b;
+  const int rows_per_branch = d.Wn * (d.Hq / d.Hkv);
+  const int rpw = mfma_rows_per_wg(d.D);
+  if (rows_per_branch <= rpw) {
+    pl->bpp = rpw / rows_per_branch;
+    pl->spb = 1;
+    pl->npacks = (d.B + pl->bpp - 1) / pl->bpp;
+  } else {
+    pl->bpp = 1;
+    pl->spb = (rows_per_branch + rpw - 1) / rpw;
+    if (double(d.B) * pl->spb > lim) return false;
+    pl->npacks = d.B * pl->spb;
+  }
+  pl->nsplit = mfma_nsplit((long long)d.T * d.Hkv * pl->npacks,
+                           (d.flags & SPECOPD_TREE_BATCH_INVARIANT) != 0);
   return true;
 }
 
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   const size_t TB = size_t(d.T) * d.B, nodes = TB * d.Wn;
-  int bpp = 0, np = 0;
-  const bool mf = mfma_plan(d, &bpp, &np);
+  MfmaPlan pl{};
+  const bool mf = mfma_plan(d, &pl);
+  const int np = mf ? pl.npacks : 0;
   TreeAttnWs w{};
   size_t off = 0;
   w.anc = off;        off = align_up(off + nodes * sizeof(uint64_t), 256);
@@ -507,7 +524,7 @@ TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   w.rot = off;        off = align_up(off + nodes * (size_t(d.Hq) + d.Hkv) * d.D * esz, 256);
   w.pstart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
   const long long units = mf ? (long long)d.T * d.Hkv * np : 0;
-  const int nsplit = mf ? mfma_nsplit(units) : 1;
+  const int nsplit = mf ? pl.nsplit : 1;
   w.ustart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
   w.umap = off;       off = align_up(off + (mf ? size_t(d.T) * np * nsplit * sizeof(int32_t) : 0), 256);
   w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
@@ -560,8 +577,8 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
   const int TB = d.T * d.B;
   const int nodes = TB * d.Wn;
   hipError_t e;
-  int bpp = 0, np = 0;
-  if (mfma_plan(d, &bpp, &np)) {
+  MfmaPlan pl{};
+  if (mfma_plan(d, &pl)) {
     uint16_t* qr = reinterpret_cast<uint16_t*>(a.ws + L.rot);
     uint16_t* kr = qr + size_t(nodes) * d.Hq * d.D;
     PrepParams pp{};
@@ -572,11 +589,11 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     pp.pstart = reinterpret_cast<int32_t*>(a.ws + L.pstart);
     pp.ustart = reinterpret_cast<int32_t*>(a.ws + L.ustart);
     pp.umap = reinterpret_cast<int32_t*>(a.ws + L.umap);
-    pp.nsplit = mfma_nsplit((long long)d.T * d.Hkv * np);
+    pp.nsplit = pl.nsplit;
     pp.ctr = reinterpret_cast<int32_t*>(a.ws + L.ctr);
     pp.qr = qr; pp.kr = kr;
     pp.T = d.T; pp.B = d.B; pp.L = d.L; pp.Wn = d.Wn; pp.Hq = d.Hq; pp.Hkv = d.Hkv; pp.D = d.D;
-    pp.bpp = bpp; pp.npacks = np;
+    pp.bpp = pl.bpp; pp.spb = pl.spb; pp.tstride = mfma_tail_stride(d.Wn); pp.npacks = pl.npacks;
     pp.log2_base = log2(double(a.rope_base));
     pp.qmul = a.scale * kLog2e;
     const unsigned rope_blocks = unsigned(std::min<size_t>((size_t(nodes) + kRopeNodes - 1) / kRopeNodes, 16384));
@@ -600,8 +617,10 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.slot_bytes = mfma_slot_bytes(d.D);
     p.out = static_cast<uint16_t*>(a.out);
     p.T = d.T; p.B = d.B; p.L = d.L; p.Wn = d.Wn; p.Hq = d.Hq; p.Hkv = d.Hkv; p.G = d.Hq / d.Hkv;
-    p.bpp = bpp;
-    p.npacks = np;
+    p.bpp = pl.bpp;
+    p.spb = pl.spb;
+    p.tstride = pp.tstride;
+    p.npacks = pl.npacks;
     p.nsplit = pp.nsplit;
     mfma_grid(p);
     timing_mark(a.timing_kind, 0, s);

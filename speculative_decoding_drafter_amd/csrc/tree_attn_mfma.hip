@@ -98,10 +98,10 @@ struct Geo {
 };
 
 // Visible tail keys of a row within tail tile [tau0, tau0 + 32): the row's own
-// branch occupies tail keys slot*Wn .. slot*Wn + Wn - 1 and it sees the nodes
+// branch occupies tail keys slot*ts .. slot*ts + Wn - 1 and it sees the nodes
 // set in its ancestor mask.  Bit q of the result = tail key tau0 + q.
-__device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int Wn, int tau0) {
-  const int base = slot * Wn - tau0;  // tile position of the row's node 0
+__device__ __forceinline__ uint32_t tail_window(uint64_t anc, int slot, int ts, int tau0) {
+  const int base = slot * ts - tau0;  // tile position of the row's node 0
   if (anc == 0 || base >= KT || base <= -64) return 0u;
   const uint64_t w = base >= 0 ? (anc << base) : (anc >> (-base));
   return uint32_t(w);
@@ -191,7 +191,7 @@ __device__ __forceinline__ void dma_whole(int v, int kvrow, int wave, char* lb,
 // private memory.
 template <int D>
 __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk, int kvrow, int Wn,
-                                         int wave, const uint16_t* tk, const uint16_t* tv,
+                                         int ts, int wave, const uint16_t* tk, const uint16_t* tv,
                                          const uint16_t* bk, const uint16_t* bv,
                                          const int32_t* pord, char* lb,
                                          const int (&dcode)[Geo<D>::JPW],
@@ -214,8 +214,9 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
     } else {
       int tau = (v - ntrunk) * KT + key;
       if (tau >= nt_total) tau = 0;
-      const int sl = tau / Wn;
-      const int node = tau - sl * Wn;
+      const int sl = tau / ts;
+      int node = tau - sl * ts;
+      if (node >= Wn) node = 0;  // a slot's padding: a valid key that every row masks
       // branch of a tail slot from global memory: an LDS read here would make
       // the compiler wait for every load in flight before later LDS reads
       const int off = (pord[sl] * Wn + node) * kvrow + c * 8;
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   const int rows_per_branch = p.Wn * p.G;
   // scalars the helper lambdas use, copied so that no lambda takes the
   // address of the kernel argument block (that would move it to scratch)
-  const int Lk = p.L, Wn = p.Wn;
+  const int Lk = p.L, Wn = p.Wn, ts = p.tstride;
   char* const part = p.part;
   const size_t slot_bytes = p.slot_bytes;
 
@@ -418,9 +419,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     // per-branch metadata has arrived
     const size_t tB = size_t(t) * p.B;
     const int32_t* ord = p.order + tB;
-    const int b0 = pk * p.bpp;
+    // sorted branches [b0, b0 + nbr) in slots of ts tail keys; with a branch
+    // split over spb packs, this pack's rows start at row ro of the branch
+    const int b0 = (pk / p.spb) * p.bpp;
     const int nbr = min(p.bpp, p.B - b0);
-    const int nt_total = nbr * p.Wn;
+    const int ro = (pk % p.spb) * mfma_rows_per_wg(D);
+    const int nt_total = (nbr - 1) * ts + Wn;
     const int ntrunk = nvt - (nt_total + KT - 1) / KT;
 
     // per-segment bases (uniform); per-lane offsets below stay in 32 bits
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 
     // ---- tile loads: global -> LDS buffer b
 #define DMA_TILE(v, b) \
-  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
+  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
     const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
     const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
 
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       const uint16_t* qb = p.qr + (tB * p.Wn * p.Hq + size_t(g) * p.G) * D;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int rho = (wave * NB + nb) * 32 + r32;
+        const int rho = (wave * NB + nb) * 32 + r32 + ro;
         const int slot = rho / rows_per_branch;
         const int within = rho - slot * rows_per_branch;
         const int j = within / p.G;
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         const int tau0 = (v - ntrunk) * KT;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          const uint32_t vis = tail_window(rmask[nb], rslot[nb], Wn, tau0) >> (4 * h);
+          const uint32_t vis = tail_window(rmask[nb], rslot[nb], ts, tau0) >> (4 * h);
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (!((vis >> (8 * (i >> 2) + (i & 3))) & 1u)) S[nb][i] = kNegInf;
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float lt = lsum[nb] + __shfl_xor(lsum[nb], 32, 64);
-        const int rho = (wave * NB + nb) * 32 + r32;
+        const int rho = (wave * NB + nb) * 32 + r32 + ro;
         const int slot = rho / rows_per_branch;
         if (slot >= nbr) continue;
         const int within = rho - slot * rows_per_branch;

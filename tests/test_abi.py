@@ -66,7 +66,7 @@ def _tcall(desc, ws_bytes=1 << 30, **over):
     ("L", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("B", -3, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("dtype", 7, sd.SPECOPD_ERR_INVALID_ARGUMENT),
-    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),     # only SPECOPD_TREE_BATCH_INVARIANT is defined
     ("rope_base", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
 ])
 def test_tree_desc_errors(field, value, code):

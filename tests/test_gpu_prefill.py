@@ -122,8 +122,11 @@ def test_full_size_sampled_rows(gpu_ok, cid):
 
 
 def test_r_c1_cb_t_consistency(gpu_ok):
-    """Branches whose nodes are the reference's own next W tokens: the tree
-    call on the prefill's cache must reproduce the prefill's rows."""
+    """Branches whose nodes are the reference's own next W tokens, scored on
+    the prefill's cache one at a time (C1), as separate sequences in one call
+    (CB) and under one trunk (T), in batch-invariant mode: C1, CB and T agree
+    bitwise, and match the prefill's own rows (R) and the oracle to the
+    attention tolerance (the prefill sums a row's keys in other tiles)."""
     cfg = shrink_attn(WORKLOADS[2].attn, L=600)
     W = 8
     inp = gen_prefill(cfg, 7, device=DEV, cid=2)
@@ -140,7 +143,8 @@ def test_r_c1_cb_t_consistency(gpu_ok):
 
     def tree(trunk_k, trunk_v, q, k, v, anc, par, pos):
         o, desc, ws = sd.tree_attn(dict(trunk_k=trunk_k, trunk_v=trunk_v, q=q, k=k, v=v,
-                                        anchors=anc, parent=par, pos=pos))
+                                        anchors=anc, parent=par, pos=pos),
+                                   flags=sd.SPECOPD_TREE_BATCH_INVARIANT)
         torch.cuda.synchronize()
         assert sd.specopd_tree_attn_device_status(desc, ws) == 0
         return o
@@ -156,6 +160,9 @@ def test_r_c1_cb_t_consistency(gpu_ok):
               q[:, None], k[:, None], v[:, None], anc[:, None], par[:, None], pos[:, None])[:, 0]
     # T: one call, all branches under one trunk (the merged tree)
     T = tree(ck, cv, q[None], k[None], v[None], anc[None], par[None], pos[None])[0]
+    # batch-invariant scoring: the three cached forms agree bit for bit
+    assert torch.equal(C1, CB), "C1 != CB"
+    assert torch.equal(CB, T), "CB != T"
     ref, _, _ = oracle.trunk_prefill(_np(inp["q"][0]), _np(inp["k"][0]), _np(inp["v"][0]))
     Rn = _np(R[0])
     for b, a in enumerate(anchors):

@@ -153,12 +153,19 @@ def test_sixty_four_node_trees(gpu_ok):
     check_attention(out.float().cpu().numpy(), _ref(inp))
 
 
-def test_rows_beyond_one_workgroup_take_the_vector_path(gpu_ok):
-    """A branch of 64 nodes with 8 query heads per kv head has 512 rows, more
-    than one matrix-core workgroup holds: the bf16 inputs take the vector
-    path, which must agree just the same."""
-    parent, depth = _random_tree(np.random.default_rng(12), 64)
-    cfg = shrink_attn(WORKLOADS[2].attn, L=200, P=50, B=2, Hq=8, Hkv=1, parent=parent, depth=depth)
+@pytest.mark.parametrize("Wn,G,D,L", [
+    (64, 8, 128, 200),    # 512 rows per branch: two packs of 256 rows each
+    (40, 8, 128, 300),    # 320 rows: a full pack and a part-filled one
+    (16, 16, 256, 333),   # D = 256 (128 rows per workgroup): two packs per branch
+    (64, 6, 256, 150),    # 384 rows at D = 256: three packs
+])
+def test_branches_beyond_one_workgroup(gpu_ok, Wn, G, D, L):
+    """A branch with more rows (node x query head of a kv group) than one
+    matrix-core workgroup holds is split over several packs, each scoring a
+    slice of its rows against all of its keys."""
+    parent, depth = _random_tree(np.random.default_rng(12 + Wn), Wn)
+    cfg = shrink_attn(WORKLOADS[2].attn, L=L, P=50, B=3, Hq=G * 2, Hkv=2, D=D, parent=parent,
+                      depth=depth)
     inp = gen_attn(cfg, 10, device=DEV, cid=2)
     out, desc, ws = _run(inp)
     assert sd.specopd_tree_attn_device_status(desc, ws) == 0
