@@ -138,6 +138,29 @@ specopd_status specopd_tree_attn_fwd(const specopd_tree_attn_desc* desc,
                                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Which attention row scores which branch token (jaehun.me review §3.2(a) and
+ * Fig. 3; rustineverything.app summary §2.2): a row's output predicts the
+ * token after it, so the target distribution of branch token j comes from
+ * the row of its parent node, and for a token attached to the anchor from
+ * the anchor's trunk row; siblings share their parent's row, and a leaf's
+ * own row scores nothing.  Score rows are numbered as one matrix: the trunk
+ * rows first, then the branch rows,
+ *     trunk row s of trunk t       ->  t*L + s
+ *     branch row (t, b, j)         ->  T*L + (t*B + b)*Wn + j
+ * (the rows of specopd_prefill_fwd's `out` followed by those of
+ * specopd_tree_attn_fwd's `out`).  Writes, for every node,
+ *   rows  [T][B][Wn] int32   the index of the score row of that token, or
+ *                            -1 when the branch is malformed (anchor outside
+ *                            the trunk, a parent that does not precede its
+ *                            child)
+ * Only T, L, B and Wn of `desc` are used (the rest is validated as for
+ * specopd_tree_attn_fwd).  `rows` can be passed to specopd_e2etv_fwd_bwd as
+ * its target_row, with target_rows = T*L + T*B*Wn.  No workspace.
+ */
+specopd_status specopd_score_rows(const specopd_tree_attn_desc* desc, const int32_t* anchors,
+                                  const int32_t* parent, int32_t* rows, hipStream_t stream);
+
+/*
  * Reads back (synchronising `stream`) how many branches the last
  * specopd_tree_attn_fwd on this workspace found malformed.  Returns
  * SPECOPD_ERR_DEVICE_VALIDATION if that count is non-zero.  `bad_branches`
@@ -209,6 +232,8 @@ typedef struct {
   uint32_t flags;              /* reserved, must be 0                        */
   int32_t wait_polls;          /* bound on a row's polls for its branch; <= 0:
                                   2^20 (see specopd_e2etv_fwd_bwd)           */
+  int32_t target_rows;         /* rows of target_logits when target_row is
+                                  given (ignored otherwise)                  */
 } specopd_e2etv_desc;
 
 specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size_t* bytes);
@@ -230,7 +255,15 @@ specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size
  *     S_n = 1 + sum over children c of n of alpha_c * S_c.
  * At an exact tie q_u == p_u the indicator is 0.
  *
- *   draft_logits, target_logits [R][Wn][V]  (logits_dtype); -inf allowed
+ *   draft_logits [R][Wn][V]     (logits_dtype); -inf allowed
+ *   target_logits               (logits_dtype): [R][Wn][V], row n the target
+ *                               distribution of node n; or, with target_row,
+ *                               [target_rows][V] score rows that nodes share
+ *   target_row   [R][Wn] int32  NULL, or the row of target_logits scoring
+ *                               each node (e.g. from specopd_score_rows:
+ *                               siblings share their parent's row); a row
+ *                               outside [0, target_rows) makes its branch
+ *                               malformed
  *   parent       [R][Wn] int32  -1 = attached to the anchor, else < j
  *   alpha_out    [R][Wn] float  overlaps, or NULL
  *   prefix_out   [R][Wn] float  prefix products, or NULL
@@ -240,8 +273,10 @@ specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size
  *   grad_draft   [R][Wn][V]     (grad_dtype), or NULL for forward only
  *   workspace    >= specopd_e2etv_workspace_size bytes, 16-byte aligned
  *
- * Rows whose parent map is malformed get NaN alpha/prefix/gradient and are
- * counted (specopd_e2etv_device_status); the loss is then NaN.
+ * Branches with a malformed parent map, a target row outside the target
+ * matrix, or an undefined overlap (NaN logits, a row that is -inf
+ * everywhere) get NaN alpha/prefix/gradient and are counted
+ * (specopd_e2etv_device_status); the loss is then NaN.
  *
  * Scheduling.  Each row is reduced by one workgroup, and a row's gradient
  * needs the overlaps of every row of its branch, so a workgroup waits for
@@ -256,7 +291,8 @@ specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size
  */
 specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc,
                                      const void* draft_logits, const void* target_logits,
-                                     const int32_t* parent, float* alpha_out,
+                                     const int32_t* target_row, const int32_t* parent,
+                                     float* alpha_out,
                                      float* prefix_out, double* loss_out, void* grad_draft,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
@@ -294,7 +330,8 @@ specopd_status specopd_e2etv_device_status(const specopd_e2etv_desc* desc,
 #define SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES (4u << 20)
 specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
                                              const void* draft_logits, const void* target_logits,
-                                             const int32_t* parent, float* alpha_out,
+                                             const int32_t* target_row, const int32_t* parent,
+                                             float* alpha_out,
                                              float* prefix_out, double* loss_out, void* grad_draft,
                                              hipStream_t stream);
 

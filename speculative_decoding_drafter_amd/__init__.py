@@ -11,6 +11,6 @@ from ._lib import (  # noqa: F401
     tree_attn_desc, e2etv_desc, specopd_tree_attn_workspace_size, specopd_tree_attn_fwd,
     specopd_tree_attn_device_status, specopd_e2etv_workspace_size, specopd_e2etv_fwd_bwd,
     specopd_e2etv_device_status, specopd_e2etv_fwd_bwd_noalloc, E2ETV_NOALLOC_SCRATCH_BYTES,
-    specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn,
+    specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn, specopd_score_rows, score_rows,
     e2etv, PrefillDesc, prefill_desc, specopd_prefill_workspace_size, specopd_prefill_fwd, prefill,
 )

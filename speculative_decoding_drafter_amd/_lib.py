@@ -33,6 +33,7 @@ E2ETV_NOALLOC_SCRATCH_BYTES = 4 << 20  # SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES
 # every symbol include/specopd.h declares
 EXPORTS = (
     "specopd_tree_attn_workspace_size", "specopd_tree_attn_fwd", "specopd_tree_attn_device_status",
+    "specopd_score_rows",
     "specopd_e2etv_workspace_size", "specopd_e2etv_fwd_bwd", "specopd_e2etv_device_status",
     "specopd_e2etv_fwd_bwd_noalloc",
     "specopd_prefill_workspace_size", "specopd_prefill_fwd",
@@ -50,7 +51,7 @@ class TreeAttnDesc(ctypes.Structure):
 class E2etvDesc(ctypes.Structure):
     _fields_ = [("R", c_int32), ("Wn", c_int32), ("V", c_int32), ("logits_dtype", c_int),
                 ("grad_dtype", c_int), ("norm_count", c_double), ("grad_scale", c_float),
-                ("flags", c_uint32), ("wait_polls", c_int32)]
+                ("flags", c_uint32), ("wait_polls", c_int32), ("target_rows", c_int32)]
 
 
 class PrefillDesc(ctypes.Structure):
@@ -75,8 +76,9 @@ def _load():
     lib.specopd_tree_attn_device_status.argtypes = [POINTER(TreeAttnDesc), P, c_size_t,
                                                     POINTER(c_int32), P]
     lib.specopd_e2etv_workspace_size.argtypes = [POINTER(E2etvDesc), POINTER(c_size_t)]
-    lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P, c_size_t, P]
-    lib.specopd_e2etv_fwd_bwd_noalloc.argtypes = [POINTER(E2etvDesc)] + [P] * 7 + [P]
+    lib.specopd_e2etv_fwd_bwd.argtypes = [POINTER(E2etvDesc)] + [P] * 8 + [P, c_size_t, P]
+    lib.specopd_e2etv_fwd_bwd_noalloc.argtypes = [POINTER(E2etvDesc)] + [P] * 8 + [P]
+    lib.specopd_score_rows.argtypes = [POINTER(TreeAttnDesc), P, P, P, P]
     lib.specopd_e2etv_device_status.argtypes = [POINTER(E2etvDesc), P, c_size_t,
                                                 POINTER(c_int32), POINTER(c_int32), P]
     lib.specopd_prefill_workspace_size.argtypes = [POINTER(PrefillDesc), POINTER(c_size_t)]
@@ -142,10 +144,10 @@ def tree_attn_desc(T, L, B, Wn, Hq, Hkv, D, dtype, rope_base=10000.0, scale=0.0,
 
 
 def e2etv_desc(R, Wn, V, logits_dtype, grad_dtype=torch.float32, norm_count=0.0, grad_scale=1.0,
-               flags=0, wait_polls=0):
+               flags=0, wait_polls=0, target_rows=0):
     ld = _DT.get(logits_dtype, logits_dtype) if not isinstance(logits_dtype, int) else logits_dtype
     gd = _DT.get(grad_dtype, grad_dtype) if not isinstance(grad_dtype, int) else grad_dtype
-    return E2etvDesc(R, Wn, V, ld, gd, norm_count, grad_scale, flags, wait_polls)
+    return E2etvDesc(R, Wn, V, ld, gd, norm_count, grad_scale, flags, wait_polls, target_rows)
 
 
 def prefill_desc(T, L, Hq, Hkv, D, dtype, rope_base=10000.0, scale=0.0, flags=0):
@@ -204,6 +206,16 @@ def specopd_tree_attn_fwd(desc, trunk_k, trunk_v, q, k, v, anchors, parent, pos,
     return out
 
 
+def specopd_score_rows(desc, anchors, parent, rows, stream=None, raw_status=False):
+    st = LIB.specopd_score_rows(ctypes.byref(desc), _ptr(anchors), _ptr(parent), _ptr(rows),
+                                _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_score_rows")
+    return rows
+
+
 def specopd_tree_attn_device_status(desc, workspace, stream=None) -> int:
     bad = c_int32(0)
     st = LIB.specopd_tree_attn_device_status(ctypes.byref(desc), _ptr(workspace),
@@ -215,9 +227,9 @@ def specopd_tree_attn_device_status(desc, workspace, stream=None) -> int:
 
 
 def specopd_e2etv_fwd_bwd(desc, draft, target, parent, alpha_out, prefix_out, loss_out, grad,
-                          workspace, stream=None, raw_status=False):
+                          workspace, stream=None, raw_status=False, target_row=None):
     st = LIB.specopd_e2etv_fwd_bwd(
-        ctypes.byref(desc), _ptr(draft), _ptr(target), _ptr(parent), _ptr(alpha_out),
+        ctypes.byref(desc), _ptr(draft), _ptr(target), _ptr(target_row), _ptr(parent), _ptr(alpha_out),
         _ptr(prefix_out), _ptr(loss_out), _ptr(grad), _ptr(workspace),
         c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
         _stream(stream))
@@ -228,9 +240,9 @@ def specopd_e2etv_fwd_bwd(desc, draft, target, parent, alpha_out, prefix_out, lo
 
 
 def specopd_e2etv_fwd_bwd_noalloc(desc, draft, target, parent, alpha_out, prefix_out, loss_out, grad,
-                                  stream=None, raw_status=False):
+                                  stream=None, raw_status=False, target_row=None):
     st = LIB.specopd_e2etv_fwd_bwd_noalloc(
-        ctypes.byref(desc), _ptr(draft), _ptr(target), _ptr(parent), _ptr(alpha_out),
+        ctypes.byref(desc), _ptr(draft), _ptr(target), _ptr(target_row), _ptr(parent), _ptr(alpha_out),
         _ptr(prefix_out), _ptr(loss_out), _ptr(grad), _stream(stream))
     if raw_status:
         return st
@@ -256,6 +268,16 @@ def specopd_e2etv_device_status(desc, workspace, stream=None, with_deferred=Fals
 def workspace(nbytes: int, device) -> torch.Tensor:
     """A 256-byte aligned uint8 device buffer of at least nbytes."""
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def score_rows(anchors, parent, L):
+    """Score row of every branch node ([T][B][Wn] int32) for anchors [T][B]
+    and parent [T][B][Wn] on a trunk of length L (specopd_score_rows)."""
+    T, B, Wn = parent.shape
+    desc = tree_attn_desc(T, L, B, Wn, 1, 1, 64, SPECOPD_BF16)
+    rows = torch.empty((T, B, Wn), dtype=torch.int32, device=parent.device)
+    specopd_score_rows(desc, anchors, parent, rows)
+    return rows
 
 
 def tree_attn(inp: dict, rope_base=10000.0, scale=0.0, ws=None, out=None, flags=0):
@@ -289,12 +311,15 @@ def prefill(q, k, v, rope_base=10000.0, scale=0.0, ws=None, outs=None):
 
 
 def e2etv(draft, target, parent, grad=True, grad_dtype=torch.float32, norm_count=0.0,
-          grad_scale=1.0, ws=None, outs=None, wait_polls=0):
-    """E2E-TV forward + gradient; returns dict of device tensors."""
+          grad_scale=1.0, ws=None, outs=None, wait_polls=0, target_row=None):
+    """E2E-TV forward + gradient; returns dict of device tensors.  With
+    target_row ([R][Wn] int32), target is a matrix of score rows [rows][V]
+    and node n's target distribution is row target_row[n] of it."""
     R, Wn, V = draft.shape
     dev = draft.device
     desc = e2etv_desc(R, Wn, V, draft.dtype, grad_dtype, norm_count, grad_scale,
-                      wait_polls=wait_polls)
+                      wait_polls=wait_polls,
+                      target_rows=target.numel() // V if target_row is not None else 0)
     if ws is None:
         ws = workspace(specopd_e2etv_workspace_size(desc), dev)
     if outs is None:
@@ -305,7 +330,7 @@ def e2etv(draft, target, parent, grad=True, grad_dtype=torch.float32, norm_count
             "grad": torch.empty((R, Wn, V), dtype=grad_dtype, device=dev) if grad else None,
         }
     specopd_e2etv_fwd_bwd(desc, draft, target, parent, outs["alpha"], outs["prefix"], outs["loss"],
-                          outs["grad"], ws)
+                          outs["grad"], ws, target_row=target_row)
     outs["desc"] = desc
     outs["ws"] = ws
     return outs

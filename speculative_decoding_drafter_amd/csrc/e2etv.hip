@@ -210,6 +210,8 @@ __device__ __forceinline__ unsigned long long pack_slot(float al, float g) {
 struct FusedArgs {
   const void* draft;
   const void* target;
+  const int32_t* target_row;  // NULL: node n's target is row n
+  int target_rows;
   const int32_t* parent;
   int Wn, V;
   double count;
@@ -229,6 +231,20 @@ struct FusedArgs {
   int32_t* defer;   // [N] those rows, in the order they gave up
   float2* lse;      // [N] (-log2-sum-exp2) of draft and target of each deferred row
 };
+
+// The target-logit row of node n: row n, or the row target_row names.  An
+// index outside the target matrix reads row 0 and marks the branch
+// malformed (the row posts NaN, so its whole branch comes out NaN).
+__device__ __forceinline__ size_t target_row_of(const FusedArgs& a, int n, bool& ok) {
+  ok = true;
+  if (!a.target_row) return size_t(n);
+  const int tr = a.target_row[n];
+  if (tr < 0 || tr >= a.target_rows) {
+    ok = false;
+    return 0;
+  }
+  return size_t(tr);
+}
 
 // Lane k of a wave holds node k of a branch (Wn <= 64).  Uniform-index
 // reads of another lane's value.
@@ -297,6 +313,7 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
     }
     ak = double(__uint_as_float(unsigned(v >> 32) & 0x7fffffffu));
     gk = __uint_as_float(unsigned(v));
+    if (!(ak == ak)) lok = false;  // undefined overlap (bad target row, NaN logits)
   }
   const bool ok = __builtin_amdgcn_ballot_w64(!lok) == 0;
   double P = 0.0, sum = 0.0;
@@ -462,8 +479,10 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   const int j = n - r * a.Wn;
   const int V = a.V;
   const size_t row = size_t(n) * size_t(V);
+  bool tok;
+  const size_t trw = target_row_of(a, n, tok) * size_t(V);
   const void* zrow = static_cast<const char*>(a.draft) + row * ESZ;
-  const void* trow = static_cast<const char*>(a.target) + row * ESZ;
+  const void* trow = static_cast<const char*>(a.target) + trw * ESZ;
   const int units = V / NV;  // whole units; a vector row's ragged tail is done element-wise
   const int e0 = units * NV;
   auto load1 = [&](const void* rowp, int e) -> float {
@@ -508,6 +527,10 @@ __global__ __launch_bounds__(kThreads) void e2etv_fused_kernel(const FusedArgs a
   });
   for (int e = e0 + tid; e < V; e += kThreads) overlap(load1(zrow, e), load1(trow, e));
   block_sum2<kThreads>(al, g, red);
+  if (!tok) {
+    al = __builtin_nanf("");
+    if (tid == 0) a.branch_ok[r] = 0;
+  }
 
   // ---- post, wait for the branch, scan
   if (tid < 64) post_and_scan(a, n, r, j, pack_slot(al, g), true, GRAD || j == 0, true, nlz, nlt, s_val);
@@ -538,8 +561,10 @@ __global__ __launch_bounds__(kThreads) void e2etv_rescue_kernel(const FusedArgs 
     if constexpr (GRAD) {
       __syncthreads();
       const size_t row = size_t(n) * size_t(a.V);
+      bool tok;
+      const size_t trw = target_row_of(a, n, tok) * size_t(a.V);
       stream_grad<BF16, VECTOR, GBF16>(a, row, static_cast<const char*>(a.draft) + row * ESZ,
-                                       static_cast<const char*>(a.target) + row * ESZ, l.x, l.y,
+                                       static_cast<const char*>(a.target) + trw * ESZ, l.x, l.y,
                                        s_val[0], s_val[1]);
       __syncthreads();  // s_val is rewritten by the next row
     }
@@ -648,8 +673,10 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   const int j = n - r * a.Wn;
   const int V = a.V;
   const size_t row = size_t(n) * size_t(V);
+  bool tok;
+  const size_t trw = target_row_of(a, n, tok) * size_t(V);
   const uint16_t* zrow = static_cast<const uint16_t*>(a.draft) + row;
-  const uint16_t* trow = static_cast<const uint16_t*>(a.target) + row;
+  const uint16_t* trow = static_cast<const uint16_t*>(a.target) + trw;
   const __amdgpu_buffer_rsrc_t zres = buf_rsrc(zrow, V * 2), tres = buf_rsrc(trow, V * 2);
   const int sbeg = min(V, kResElems);  // first streamed element (a multiple of 4)
 
@@ -762,6 +789,10 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   for (int k = 0; k < kResLds; ++k)
     if (kResRegElems + k * 4096 + tid * 8 < V) overlap8(lds8(k, 0), lds8(k, 1));
   block_sum2<kResThreads>(al, g, red);
+  if (!tok) {
+    al = __builtin_nanf("");
+    if (tid == 0) a.branch_ok[r] = 0;
+  }
 
   // ---- post, wait for the branch, scan
   if (tid < 64) post_and_scan(a, n, r, j, pack_slot(al, g), true, GRAD || j == 0, true, nlz, nlt, s_val);
@@ -851,6 +882,8 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   FusedArgs f{};
   f.draft = a.draft;
   f.target = a.target;
+  f.target_row = a.target_row;
+  f.target_rows = d.target_rows;
   f.parent = a.parent;
   f.Wn = Wn;
   f.V = d.V;

@@ -35,6 +35,9 @@ struct TreeAttnArgs {
   int timing_kind;  // call kind the attention kernel is timed as (timing_mark)
 };
 hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs& a, hipStream_t s);
+// Score row of every branch node (specopd_score_rows).
+hipError_t launch_score_rows(const specopd_tree_attn_desc& d, const int32_t* anchors,
+                             const int32_t* parent, int32_t* rows, hipStream_t s);
 
 // Matrix-core path (tree_attn_mfma.hip).  bf16 tensors are passed as uint16_t.
 // Four waves per workgroup, one per SIMD, so that a wave may hold 512
@@ -164,6 +167,7 @@ inline size_t e2etv_ndefer_offset(const E2etvWs& w) { return w.ticket + 256; }
 
 struct E2etvArgs {
   const void *draft, *target;
+  const int32_t* target_row;
   const int32_t* parent;
   float *alpha_out, *prefix_out;
   double* loss_out;

@@ -61,6 +61,25 @@ specopd_status check_e2etv_desc(const specopd_e2etv_desc* d) {
   return SPECOPD_OK;
 }
 
+// Pointer checks shared by the two E2E-TV calls (after the descriptor's).
+specopd_status check_e2etv_call(const specopd_e2etv_desc* d, const void* draft, const void* target,
+                                const int32_t* target_row, const int32_t* parent,
+                                const float* alpha, const float* prefix, const double* loss,
+                                const void* grad) {
+  specopd_status st = check_e2etv_desc(d);
+  if (st != SPECOPD_OK) return st;
+  if (!draft || !target || !parent || !loss) return SPECOPD_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {draft, target, parent, loss};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if ((alpha && !aligned16(alpha)) || (prefix && !aligned16(prefix)) || (grad && !aligned16(grad)) ||
+      (target_row && !aligned16(target_row)))
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (target_row && d->target_rows < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (grad && (grad == draft || grad == target)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  return SPECOPD_OK;
+}
+
 }  // namespace
 
 // ---- kernel timing
@@ -234,6 +253,19 @@ specopd_status specopd_prefill_fwd(const specopd_prefill_desc* desc, const void*
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
 }
 
+specopd_status specopd_score_rows(const specopd_tree_attn_desc* desc, const int32_t* anchors,
+                                  const int32_t* parent, int32_t* rows, hipStream_t stream) {
+  specopd_status st = check_tree_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!anchors || !parent || !rows) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(anchors) || !aligned16(parent) || !aligned16(rows)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  // every score row index must fit an int32
+  if (double(desc->T) * desc->L + double(desc->T) * desc->B * desc->Wn > 2147483647.0)
+    return SPECOPD_ERR_UNSUPPORTED;
+  return launch_score_rows(*desc, anchors, parent, rows, stream) == hipSuccess ? SPECOPD_OK
+                                                                                 : SPECOPD_ERR_HIP;
+}
+
 specopd_status specopd_tree_attn_device_status(const specopd_tree_attn_desc* desc,
                                                const void* workspace, size_t workspace_bytes,
                                                int32_t* bad_branches, hipStream_t stream) {
@@ -262,25 +294,17 @@ specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size
 }
 
 specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc, const void* draft_logits,
-                                     const void* target_logits, const int32_t* parent,
-                                     float* alpha_out, float* prefix_out, double* loss_out,
-                                     void* grad_draft, void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
-  specopd_status st = check_e2etv_desc(desc);
+                                     const void* target_logits, const int32_t* target_row,
+                                     const int32_t* parent, float* alpha_out, float* prefix_out,
+                                     double* loss_out, void* grad_draft, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  specopd_status st = check_e2etv_call(desc, draft_logits, target_logits, target_row, parent,
+                                       alpha_out, prefix_out, loss_out, grad_draft);
   if (st != SPECOPD_OK) return st;
-  if (!draft_logits || !target_logits || !parent || !loss_out) return SPECOPD_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {draft_logits, target_logits, parent, loss_out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
-  if ((alpha_out && !aligned16(alpha_out)) || (prefix_out && !aligned16(prefix_out)) ||
-      (grad_draft && !aligned16(grad_draft)))
-    return SPECOPD_ERR_INVALID_ARGUMENT;
-  if (grad_draft && (grad_draft == draft_logits || grad_draft == target_logits))
-    return SPECOPD_ERR_INVALID_ARGUMENT;
   const size_t need = e2etv_ws_layout(*desc).total;
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
   E2etvArgs a{};
-  a.draft = draft_logits; a.target = target_logits; a.parent = parent;
+  a.draft = draft_logits; a.target = target_logits; a.target_row = target_row; a.parent = parent;
   a.alpha_out = alpha_out; a.prefix_out = prefix_out; a.loss_out = loss_out;
   a.grad = grad_draft; a.ws = static_cast<char*>(workspace);
   hipError_t e = launch_e2etv(*desc, a, stream);
@@ -288,25 +312,18 @@ specopd_status specopd_e2etv_fwd_bwd(const specopd_e2etv_desc* desc, const void*
 }
 
 specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc, const void* draft_logits,
-                                             const void* target_logits, const int32_t* parent,
-                                             float* alpha_out, float* prefix_out, double* loss_out,
-                                             void* grad_draft, hipStream_t stream) {
-  specopd_status st = check_e2etv_desc(desc);
+                                             const void* target_logits, const int32_t* target_row,
+                                             const int32_t* parent, float* alpha_out,
+                                             float* prefix_out, double* loss_out, void* grad_draft,
+                                             hipStream_t stream) {
+  specopd_status st = check_e2etv_call(desc, draft_logits, target_logits, target_row, parent,
+                                       alpha_out, prefix_out, loss_out, grad_draft);
   if (st != SPECOPD_OK) return st;
-  if (!draft_logits || !target_logits || !parent || !loss_out) return SPECOPD_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {draft_logits, target_logits, parent, loss_out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
-  if ((alpha_out && !aligned16(alpha_out)) || (prefix_out && !aligned16(prefix_out)) ||
-      (grad_draft && !aligned16(grad_draft)))
-    return SPECOPD_ERR_INVALID_ARGUMENT;
-  if (grad_draft && (grad_draft == draft_logits || grad_draft == target_logits))
-    return SPECOPD_ERR_INVALID_ARGUMENT;
   if (e2etv_ws_layout(*desc).total > kE2etvScratchBytes) return SPECOPD_ERR_WORKSPACE;
   void* ws = nullptr;
   if (e2etv_scratch(&ws) != hipSuccess) return SPECOPD_ERR_HIP;
   E2etvArgs a{};
-  a.draft = draft_logits; a.target = target_logits; a.parent = parent;
+  a.draft = draft_logits; a.target = target_logits; a.target_row = target_row; a.parent = parent;
   a.alpha_out = alpha_out; a.prefix_out = prefix_out; a.loss_out = loss_out;
   a.grad = grad_draft; a.ws = static_cast<char*>(ws);
   hipError_t e = launch_e2etv(*desc, a, stream);

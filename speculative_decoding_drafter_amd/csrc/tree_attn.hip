@@ -48,6 +48,41 @@ __global__ void tree_plan_kernel(const int32_t* __restrict__ anchors,
   branch_ok[tb] = ok ? 1 : 0;
 }
 
+// ---------------------------------------------------------------- score rows
+
+// One thread per node: the score row of branch token j is its parent's row,
+// or the anchor's trunk row for a token attached to the anchor (jaehun.me
+// review §3.2(a), Fig. 3).  Rows: trunk rows t*L + s first, then branch rows
+// T*L + (t*B + b)*Wn + j.  A malformed branch gets -1 for every node.
+__global__ void score_rows_kernel(const int32_t* __restrict__ anchors,
+                                  const int32_t* __restrict__ parent, int T, int L, int B, int Wn,
+                                  int32_t* __restrict__ rows) {
+  const long long n = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long nodes = (long long)T * B * Wn;
+  if (n >= nodes) return;
+  const long long tb = n / Wn;
+  const int j = int(n - tb * Wn);
+  const int t = int(tb / B);
+  const int a = anchors[tb];
+  bool ok = a >= 0 && a < L;
+  const int32_t* par = parent + tb * Wn;
+  for (int k = 0; k < Wn; ++k) {
+    const int pk = par[k];
+    ok = ok && pk >= -1 && pk < k;
+  }
+  const int p = par[j];
+  long long r = p < 0 ? (long long)t * L + a : (long long)T * L + tb * Wn + p;
+  rows[n] = ok ? int32_t(r) : -1;
+}
+
+hipError_t launch_score_rows(const specopd_tree_attn_desc& d, const int32_t* anchors,
+                             const int32_t* parent, int32_t* rows, hipStream_t s) {
+  const long long nodes = (long long)d.T * d.B * d.Wn;
+  score_rows_kernel<<<unsigned((nodes + 255) / 256), 256, 0, s>>>(anchors, parent, d.T, d.L, d.B,
+                                                                 d.Wn, rows);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- rotary
 
 // Rotates every branch query and key at its node's semantic position.  One

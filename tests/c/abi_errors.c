@@ -40,13 +40,17 @@ int main(void) {
                                1u << 30, NULL),
          SPECOPD_ERR_INVALID_ARGUMENT);
 
-  specopd_e2etv_desc ed = {4, 7, 151936, SPECOPD_BF16, SPECOPD_F32, 0.0, 1.0f, 0u, 0};
+  specopd_e2etv_desc ed = {4, 7, 151936, SPECOPD_BF16, SPECOPD_F32, 0.0, 1.0f, 0u, 0, 0};
   EXPECT(specopd_e2etv_workspace_size(&ed, &bytes), SPECOPD_OK);
   {
     char* f = (char*)fake; /* distinct, aligned stand-ins: no argument aliases another */
-    EXPECT(specopd_e2etv_fwd_bwd(&ed, f, f + 16, (const int32_t*)(f + 32), NULL, NULL,
+    EXPECT(specopd_e2etv_fwd_bwd(&ed, f, f + 16, NULL, (const int32_t*)(f + 32), NULL, NULL,
                                  (double*)(f + 48), f + 64, NULL, 0, NULL),
            SPECOPD_ERR_WORKSPACE);
+    /* a target-row index without a row count */
+    EXPECT(specopd_e2etv_fwd_bwd(&ed, f, f + 16, (const int32_t*)(f + 96), (const int32_t*)(f + 32),
+                                 NULL, NULL, (double*)(f + 48), f + 64, f + 128, 1u << 30, NULL),
+           SPECOPD_ERR_INVALID_ARGUMENT);
   }
   ed.Wn = 65;
   EXPECT(specopd_e2etv_workspace_size(&ed, &bytes), SPECOPD_ERR_UNSUPPORTED);

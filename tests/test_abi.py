@@ -114,7 +114,8 @@ def _ecall(desc, ws_bytes=1 << 30, **over):
     args.update(over)
     P = ctypes.c_void_p
     return sd.LIB.specopd_e2etv_fwd_bwd(
-        ctypes.byref(desc), P(args["draft"]), P(args["target"]), P(args["parent"]),
+        ctypes.byref(desc), P(args["draft"]), P(args["target"]), P(args.get("target_row")),
+        P(args["parent"]),
         P(args["alpha"]), P(args["prefix"]), P(args["loss"]), P(args["grad"]), P(args["ws"]),
         ctypes.c_size_t(ws_bytes), P(None))
 
@@ -280,7 +281,7 @@ def test_noalloc_rejects_host_errors_before_the_gpu():
                  loss=FAKE + 80, grad=FAKE + 96)
         a.update(over)
         return sd.LIB.specopd_e2etv_fwd_bwd_noalloc(
-            ctypes.byref(desc), P(a["draft"]), P(a["target"]), P(a["parent"]), P(a["alpha"]),
+            ctypes.byref(desc), P(a["draft"]), P(a["target"]), P(None), P(a["parent"]), P(a["alpha"]),
             P(a["prefix"]), P(a["loss"]), P(a["grad"]), P(None))
     assert call(big) == sd.SPECOPD_ERR_WORKSPACE
     assert call(_edesc(), draft=0) == sd.SPECOPD_ERR_INVALID_ARGUMENT
