@@ -17,11 +17,20 @@ Tolerances:
 
 Gradient ties.  The gradient contains the indicator [q_u < p_u].  The GPU
 decides it in fp32 from log2-probabilities, the oracle in fp64; where
-|log p_u - log q_u| is within the fp32 error of that comparison (TIE_TAU) the
-two may legitimately differ, and each differing element moves grad[u] by
-|c| q_u and G by q_u, i.e. every element of the row by |c| q_u q_v.  The
-envelope adds exactly that much for every element u of an ambiguous set T:
+|log p_u - log q_u| is within the fp32 error of that comparison the two may
+legitimately differ.  That error bound (tie_tau) is per element: the kernel
+forms lq = z log2(e) - lse2(z) and lp likewise with one fused multiply-add
+each, so each carries at most half an fp32 ulp of its own magnitude plus the
+error of its log-sum-exp (a relative error of the fp32 sum of exponentials,
+taken as 1e-6 in log2 units); four ulps of the larger magnitude plus 2e-6,
+converted to natural-log units, bounds the difference of the two -- about
+7e-6 for typical rows (|lq| ~ 17 in log2 units), 2e-5 for the largest
+logits here.  Each differing element moves grad[u] by |c| q_u and G by q_u,
+i.e. every element of the row by |c| q_u q_v.  The envelope adds exactly
+that much for every element u of an ambiguous set T:
     |c| * (q_u * sum_{v in T} q_v + [u in T] q_u).
+Rows where that allowance exceeds a tenth of the row's gradient norm are
+reported (printed with their allowance), not hidden.
 Such ties are not rare with bf16 logits: when one token dominates each
 distribution, log p - log q of every other token is a bf16-grid difference
 minus a log-sum-exp difference that itself sits within ~1e-9 of a grid
@@ -42,7 +51,18 @@ ALPHA_ATOL = 1e-5
 GRAD_ATOL = 1e-5
 GRAD_REL_L2 = 1e-3
 GRAD_REL_L2_BF16 = 5e-3
-TIE_TAU = 1e-4
+LN2 = 0.6931471805599453
+LOG2E = 1.4426950408889634
+
+
+def tie_tau(lq, lp):
+    """Per-element bound (natural-log units) on the error of the kernel's
+    fp32 comparison of log2-probabilities; lq, lp natural-log probabilities
+    (fp64, from the oracle)."""
+    mag = np.maximum(np.abs(np.nan_to_num(lq, neginf=0.0)), np.abs(np.nan_to_num(lp, neginf=0.0)))
+    ulp = np.spacing(np.float32(1.0)).astype(np.float64) * np.exp2(np.floor(np.log2(
+        np.maximum(mag * LOG2E, 1e-30))))
+    return LN2 * (4.0 * ulp + 2e-6)
 
 
 def rel_l2(a, b):
@@ -82,21 +102,32 @@ def check_grad_rows(gpu, ref_grad, ref_margin, ref_q, coef, identical=None, bf16
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite"
     n = gpu.shape[0]
     resid = np.zeros_like(gpu)
+    loose = []
     for i in range(n):
         if identical is not None and identical[i]:
             assert np.all(gpu[i] == 0.0), f"{what}: row {i} (target == draft) not exactly zero"
             continue
-        tie = np.abs(np.nan_to_num(ref_margin[i], nan=0.0)) <= TIE_TAU
+        with np.errstate(divide="ignore"):
+            lq = np.log(ref_q[i])
+        margin = np.nan_to_num(ref_margin[i], nan=0.0)
+        tie = np.abs(margin) <= tie_tau(lq, lq + margin)
         env = np.zeros(gpu.shape[1])
         if tie.any():
             qt = float(ref_q[i][tie].sum())
             env = abs(coef[i]) * (ref_q[i] * qt + np.where(tie, ref_q[i], 0.0))
+            gn = float(np.linalg.norm(ref_grad[i]))
+            en = float(np.linalg.norm(env))
+            if gn > 0 and en > 0.1 * gn:
+                loose.append((i, int(tie.sum()), en / gn))
         atol = GRAD_ATOL if not bf16 else GRAD_ATOL + np.abs(ref_grad[i]) * 2.0 ** -8
         err = np.abs(gpu[i] - ref_grad[i])
         resid[i] = np.maximum(err - env, 0.0)
         bad = err > atol + env
         assert not bad.any(), (f"{what}: row {i}: {bad.sum()} elements out of tolerance, "
                                f"max err {err.max():.3e}")
+    if loose:
+        print(f"{what}: {len(loose)} of {n} rows have a tie allowance above 10% of their gradient "
+              f"norm (row, tied elements, allowance/norm): {loose[:8]}", flush=True)
     keep = np.ones(n, bool) if identical is None else ~np.asarray(identical, bool)
     if keep.any():
         den = np.linalg.norm(ref_grad[keep])

@@ -106,20 +106,29 @@ def test_malformed_trees_are_flagged(gpu_ok):
 
 
 @pytest.mark.parametrize("cid", [2, 3, 5])
-def test_full_size_sampled_branches(gpu_ok, cid):
+def test_full_size_branches(gpu_ok, cid):
+    """The full workloads in the launch configuration the benchmark times:
+    every branch of the 8B layer; 32 branches of the 8-trunk workload, four
+    per trunk (its longest and shortest anchors among them); 16 branches of
+    the long-context workload -- each element by element against the
+    oracle."""
     cfg = WORKLOADS[cid].attn
     inp = gen_attn(cfg, 0, device=DEV, cid=cid)
     out, desc, ws = _run(inp)
     assert sd.specopd_tree_attn_device_status(desc, ws) == 0
     rng = np.random.default_rng(cid)
     anch = inp["anchors"].cpu().numpy()
-    picks = set()
-    for _ in range(4):
-        picks.add((int(rng.integers(cfg.T)), int(rng.integers(cfg.B))))
-    # the longest and the shortest branch of trunk 0
-    picks.add((0, int(anch[0].argmax())))
-    picks.add((0, int(anch[0].argmin())))
-    picks = sorted(picks)
+    if cid == 2:
+        picks = [(0, b) for b in range(cfg.B)]
+    else:
+        per = 4 if cid == 3 else 16
+        picks = set()
+        for t in range(cfg.T):
+            picks.add((t, int(anch[t].argmax())))
+            picks.add((t, int(anch[t].argmin())))
+            for b in rng.choice(cfg.B, size=per - 2, replace=False):
+                picks.add((t, int(b)))
+        picks = sorted(picks)
     ref = _ref(inp, branches=picks)
     got = out.float().cpu().numpy()
     for (t, b) in picks:
