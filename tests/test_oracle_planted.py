@@ -1,0 +1,110 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case takes one oracle function's own source, makes one plausible
+mistake in it (a sign, an index, a dropped term, a widened or transposed
+mask, a wrong constant), swaps the mutant in for the duration of the test,
+and runs the pins that should notice: at least one must fail with an
+assertion.  This shows the pins are not restatements of the code they pin."""
+
+import importlib
+import inspect
+import textwrap
+
+import pytest
+
+import oracle
+import test_oracle_e2etv as te
+import test_oracle_prefill as tp
+import test_oracle_tree_attention as tt
+
+# (oracle module, function, text in its source, replacement, pins)
+CASES = {
+    "overlap takes the max": (
+        "oracle.e2etv", "overlap", "np.minimum(np.exp(lq), np.exp(lp))",
+        "np.maximum(np.exp(lq), np.exp(lp))",
+        [te.test_eq13_worked_example, te.test_appC2_first_overlap]),
+    "prefix product reads the parent's overlap": (
+        "oracle.e2etv", "prefix_products", "(1.0 if p < 0 else P[r, p])",
+        "(1.0 if p < 0 else alpha[r, p])",
+        [lambda: te.test_constant_alpha_chain_closed_form(0.7, 7)]),
+    "suffix sum drops the child's overlap": (
+        "oracle.e2etv", "suffix_sums", "S[r, p] += alpha[r, j] * S[r, j]", "S[r, p] += S[r, j]",
+        [te.test_division_free_equals_descendant_sum]),
+    "log-sum-exp drops its shift": (
+        "oracle.e2etv", "logsumexp", "return m + np.log(", "return np.log(",
+        [te.test_eq13_worked_example]),
+    "gradient indicator reversed": (
+        "oracle.e2etv", "e2etv", "ind = (lq < lp).astype(np.float64)",
+        "ind = (lq > lp).astype(np.float64)", [te.test_gradient_finite_difference]),
+    "gradient adds G instead of subtracting": (
+        "oracle.e2etv", "e2etv", "q * (ind - Gf[r0:r1, None])", "q * (ind + Gf[r0:r1, None])",
+        [te.test_gradient_finite_difference, te.test_grad_scale_and_row_sums]),
+    "gradient drops the parent's prefix product": (
+        "oracle.e2etv", "e2etv", "c = -grad_scale * Ppar * S / count", "c = -grad_scale * S / count",
+        [te.test_gradient_finite_difference, te.test_division_free_equals_descendant_sum]),
+    "loss divides by the wrong count": (
+        "oracle.e2etv", "e2etv", '"loss": 1.0 - numer / count', '"loss": 1.0 - numer / (count + 1.0)',
+        [lambda: te.test_constant_alpha_chain_closed_form(0.3, 2)]),
+    "rotation sign flipped": (
+        "oracle.rope", "rope", "x1 * c - x2 * s", "x1 * c + x2 * s",
+        [tt.test_rope_pair_is_complex_rotation, tt.test_rope_hand_values]),
+    "rotation frequencies halved": (
+        "oracle.rope", "rope_angles", "-2.0 * i / D", "-1.0 * i / D",
+        [tt.test_rope_pair_is_complex_rotation, tt.test_rope_hand_values]),
+    "anchor token masked": (
+        "oracle.tree_attention", "branch_mask", "m[j, : int(anchor) + 1] = True",
+        "m[j, : int(anchor)] = True", [tt.test_fig3_toy_tree]),
+    "every earlier node visible (siblings leak)": (
+        "oracle.tree_attention", "branch_mask", "for k in walk_ancestors(parent, j):",
+        "for k in range(j + 1):", [tt.test_each_row_is_plain_attention_over_its_history]),
+    "scores scaled by 1/D": (
+        "oracle.tree_attention", "tree_attention_branch", "scale = 1.0 / np.sqrt(D)", "scale = 1.0 / D",
+        [tt.test_each_row_is_plain_attention_over_its_history]),
+    "query heads dealt to kv heads round robin": (
+        "oracle.tree_attention", "tree_attention_branch", "for h in range(g * G, (g + 1) * G):",
+        "for h in range(g, Hq, Hkv):", [tt.test_gqa_head_mapping]),
+    "prefill sees one token ahead": (
+        "oracle.prefill", "trunk_prefill", "np.arange(L)[None, :] <= todo[:, None]",
+        "np.arange(L)[None, :] <= todo[:, None] + 1",
+        [lambda: tp.test_prefill_is_library_causal_attention(0, 37, 4, 2, 16)]),
+    "prefill kv head transposed": (
+        "oracle.prefill", "trunk_prefill", "g = h // G", "g = h % Hkv",
+        [lambda: tp.test_prefill_is_library_causal_attention(0, 37, 4, 2, 16)]),
+    "score row of the node itself": (
+        "oracle.rows", "score_row_source", 'else ("node", p)', 'else ("node", int(j))',
+        [tt.test_fig3_toy_tree]),
+}
+
+
+def _mutant(mod, name, old, new):
+    src = textwrap.dedent(inspect.getsource(getattr(mod, name)))
+    assert src.count(old) == 1, f"{name}: the planted text must occur once"
+    ns = dict(vars(mod))
+    exec(compile(src.replace(old, new), f"<planted {name}>", "exec"), ns)
+    return ns[name]
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_planted_mistake_is_caught(case, monkeypatch):
+    modname, name, old, new, pins = CASES[case]
+    mod = importlib.import_module(modname)
+    orig = getattr(mod, name)
+    bad = _mutant(mod, name, old, new)
+    monkeypatch.setattr(mod, name, bad)
+    if getattr(oracle, name, None) is orig:
+        monkeypatch.setattr(oracle, name, bad)
+    caught = []
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError as e:
+            caught.append(str(e)[:80])
+    assert caught, f"no pin caught: {case}"
+
+
+def test_unplanted_pins_pass():
+    """The same pins pass on the oracle as written (so a catch above is the
+    planted mistake's doing)."""
+    for case in CASES.values():
+        for pin in case[4]:
+            pin()
