@@ -20,9 +20,10 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 //   rot        rotated branch queries and keys
 //   pstart     int32  [T][npacks+1]  first key tile of each pack (prefix sums)
 //   ctr        int32  [T][Hkv][npacks]  splits of a pack that finished
+//   qctr       u64    [8]        unit-queue counters of the matrix-core kernel
 //   part       partial results, one slot per (pack, split) when packs are split
 struct TreeAttnWs {
-  size_t anc, branch_ok, order, rot, pstart, ustart, umap, ctr, part, total;
+  size_t anc, branch_ok, order, rot, pstart, ustart, umap, ctr, qctr, part, total;
 };
 TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d);
 
@@ -72,6 +73,7 @@ struct MfmaParams {
   const int32_t* ustart;              // [T][npacks+1] first unit of each pack (per kv head)
   const int32_t* umap;                // [T][npacks*nsplit] pack of each unit
   int32_t* ctr;                       // [T][Hkv][npacks], zero on entry
+  unsigned long long* qctr;           // [8] unit-queue counters, zero on entry
   char* part;                         // nunits slots of slot_bytes (nsplit > 1)
   size_t slot_bytes;
   uint16_t* out;                      // [T][B][Wn][Hq][D]
@@ -130,10 +132,11 @@ hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s, bool
 //   branch_ok, order, anc, pstart, ustart, umap: the tree kernel's plan of the
 //              L-1 one-node branches (the same for every trunk)
 //   ctr        int32  [T][Hkv][npacks]
+//   qctr       u64    [T][8]    unit-queue counters of each trunk's launch
 //   part       split partials (one trunk's launch at a time)
 // fp32 path: anchors, parent (-1), pos (b+1), then the tree workspace.
 struct PrefillWs {
-  size_t anchors, qr, branch_ok, order, anc, pstart, ustart, umap, ctr, part;
+  size_t anchors, qr, branch_ok, order, anc, pstart, ustart, umap, ctr, qctr, part;
   size_t parent, pos, tree, total;
 };
 PrefillWs prefill_ws_layout(const specopd_prefill_desc& d);

@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void prefill_rope_kernel(const PrefillRopePara
 
 struct PrefillPlanParams {
   int32_t *anchors, *parent, *pos, *branch_ok, *order, *pstart, *ustart, *umap, *ctr;
+  unsigned long long* qctr;
   uint64_t* anc;
   int T, B, Hkv, bpp, npacks, nsplit;
 };
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(256) void prefill_plan_kernel(const PrefillPlanPara
     for (int u = i + int(e0); u < i + 1 + int(e1); ++u) p.umap[u] = i;
   }
   for (int i = tid; i < p.T * p.Hkv * np; i += 256) p.ctr[i] = 0;
+  for (int i = tid; i < p.T * 8; i += 256) p.qctr[i] = 0;
 }
 
 // Matrix-core geometry of the one-node-branch problem of a trunk.
@@ -265,6 +267,7 @@ PrefillWs prefill_ws_layout(const specopd_prefill_desc& d) {
     w.ustart = off;    off = align_up(off + size_t(g.np + 1) * sizeof(int32_t), 256);
     w.umap = off;      off = align_up(off + size_t(g.np) * g.nsplit * sizeof(int32_t), 256);
     w.ctr = off;       off = align_up(off + size_t(d.T) * d.Hkv * g.np * sizeof(int32_t), 256);
+    w.qctr = off;      off = align_up(off + size_t(d.T) * 8 * sizeof(unsigned long long), 256);
     const size_t units = size_t(d.Hkv) * g.np;
     w.part = off;      off = align_up(off + (g.nsplit > 1 ? units * g.nsplit * mfma_slot_bytes(d.D) : 0), 256);
   } else if (B > 0) {
@@ -306,6 +309,7 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
     pp.ustart = reinterpret_cast<int32_t*>(a.ws + L.ustart);
     pp.umap = reinterpret_cast<int32_t*>(a.ws + L.umap);
     pp.ctr = reinterpret_cast<int32_t*>(a.ws + L.ctr);
+    pp.qctr = reinterpret_cast<unsigned long long*>(a.ws + L.qctr);
     pp.bpp = g.bpp; pp.npacks = g.np; pp.nsplit = g.nsplit;
   } else {
     pp.parent = reinterpret_cast<int32_t*>(a.ws + L.parent);
@@ -332,6 +336,7 @@ hipError_t launch_prefill(const specopd_prefill_desc& d, const PrefillArgs& a, h
       p.ustart = pp.ustart;
       p.umap = pp.umap;
       p.ctr = pp.ctr + size_t(t) * d.Hkv * g.np;
+      p.qctr = pp.qctr + size_t(t) * 8;
       p.part = a.ws + L.part;  // launches on one stream run in turn
       p.slot_bytes = mfma_slot_bytes(d.D);
       p.out = static_cast<uint16_t*>(a.out) + (t0 + 1) * q_tok;

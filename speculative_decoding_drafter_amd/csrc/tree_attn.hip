@@ -123,6 +123,7 @@ struct PrepParams {
   const uint16_t *q, *k;
   uint64_t* anc;
   int32_t *branch_ok, *order, *pstart, *ustart, *umap, *ctr;
+  unsigned long long* qctr;
   uint16_t *qr, *kr;
   int T, B, L, Wn, Hq, Hkv, D, bpp, spb, tstride, npacks, nsplit;
   double log2_base;
@@ -349,6 +350,7 @@ __global__ __launch_bounds__(256) void tree_prep_kernel(const PrepParams p) {
     }
     int32_t* c = p.ctr + size_t(t) * p.Hkv * np;
     for (int i = tid; i < p.Hkv * np; i += 256) c[i] = 0;
+    if (t == 0 && tid < 8) p.qctr[tid] = 0;
     return;
   }
   // rotary: kRopeNodes nodes per workgroup pass.  Frequencies are tabulated
@@ -563,6 +565,7 @@ TreeAttnWs tree_attn_ws_layout(const specopd_tree_attn_desc& d) {
   w.ustart = off;     off = align_up(off + (mf ? size_t(d.T) * (np + 1) * sizeof(int32_t) : 0), 256);
   w.umap = off;       off = align_up(off + (mf ? size_t(d.T) * np * nsplit * sizeof(int32_t) : 0), 256);
   w.ctr = off;        off = align_up(off + (mf ? size_t(d.T) * d.Hkv * np * sizeof(int32_t) : 0), 256);
+  w.qctr = off;       off = align_up(off + (mf ? 8 * sizeof(unsigned long long) : 0), 256);
   w.part = off;       off = align_up(off + (nsplit > 1 ? size_t(units) * nsplit * mfma_slot_bytes(d.D) : 0), 256);
   w.total = off;
   return w;
@@ -626,6 +629,7 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     pp.umap = reinterpret_cast<int32_t*>(a.ws + L.umap);
     pp.nsplit = pl.nsplit;
     pp.ctr = reinterpret_cast<int32_t*>(a.ws + L.ctr);
+    pp.qctr = reinterpret_cast<unsigned long long*>(a.ws + L.qctr);
     pp.qr = qr; pp.kr = kr;
     pp.T = d.T; pp.B = d.B; pp.L = d.L; pp.Wn = d.Wn; pp.Hq = d.Hq; pp.Hkv = d.Hkv; pp.D = d.D;
     pp.bpp = pl.bpp; pp.spb = pl.spb; pp.tstride = mfma_tail_stride(d.Wn); pp.npacks = pl.npacks;
@@ -648,6 +652,7 @@ hipError_t launch_tree_attn(const specopd_tree_attn_desc& d, const TreeAttnArgs&
     p.ustart = pp.ustart;
     p.umap = pp.umap;
     p.ctr = pp.ctr;
+    p.qctr = pp.qctr;
     p.part = a.ws + L.part;
     p.slot_bytes = mfma_slot_bytes(d.D);
     p.out = static_cast<uint16_t*>(a.out);

@@ -343,6 +343,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   // scopes and then waits for every global-to-LDS load before any LDS read.
   __shared__ __attribute__((aligned(1024))) char smem[Gm::NBUF * Gm::BUFB + 16];
   int* const s_last = reinterpret_cast<int*>(smem + Gm::NBUF * Gm::BUFB);
+  int* const s_unit = s_last + 1;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
@@ -351,14 +352,43 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 
   // Work unit u = (t * Hkv + g) * ugp + j, j < npacks * nsplit the j-th split
   // of the (trunk, kv head) group in pack order; ugp >= that count pads the
-  // group to a multiple of ilv.  In chunked mode units are dealt to the XCDs
+  // group to a multiple of ilv.  In chunked mode units are queued to the XCDs
   // in consecutive blocks (workgroups go to the 8 XCDs round robin), so the
   // packs of one kv head run side by side on one XCD and stream the same
   // trunk rows through its L2; when a group spans `ilv` XCD blocks, its packs
   // are dealt to those blocks alternately, so that each XCD gets a like share
-  // of long and short packs.  Otherwise units follow the block index.
-  const int ub = p.chunked ? (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : int(blockIdx.x);
-  if (ub >= p.nunits) return;
+  // of long and short packs.  The workgroups are persistent (one per CU): each
+  // takes the front unit of its XCD's queue (packs come longest first) until
+  // that queue is empty, then the back units -- the shortest left -- of the
+  // other XCDs' queues, so XCDs whose trunks hold less work help the others
+  // finish.  A queue's counter keeps the front count in its low half and the
+  // back count in its high half: one atomic add both claims an entry and
+  // tells whether it was still free, so every entry is taken exactly once.
+  // Otherwise (no XCD structure) units are claimed in order from one queue.
+  const int nq = p.nwg >> 3;  // entries per XCD queue
+  for (;;) {
+  __syncthreads();  // every wave is done with the previous unit and its claim
+  if (tid == 0) {
+    int u = -1;
+    if (p.chunked) {
+      const int x = blockIdx.x & 7;
+      for (int k = 0; k < 8 && u < 0; ++k) {
+        const int y = (x + k) & 7;
+        const unsigned long long old = __hip_atomic_fetch_add(
+            p.qctr + y, k == 0 ? 1ull : (1ull << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const long long f = (long long)(old & 0xffffffffull), bk = (long long)(old >> 32);
+        if (f + bk < nq) u = y * nq + int(k == 0 ? f : nq - 1 - bk);
+      }
+    } else {
+      const int v = int(__hip_atomic_fetch_add(p.qctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      u = v < p.nwg ? v : -1;
+    }
+    *s_unit = u;
+  }
+  __syncthreads();
+  const int ub = *s_unit;
+  if (ub < 0) break;             // every queue is empty
+  if (ub >= p.nunits) continue;  // padding
   const int np = p.npacks;
   const int ug = np * p.nsplit;            // units per (trunk, kv head)
   const int tg = ub / p.ugp;
@@ -367,7 +397,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     const int c = p.ugp / p.ilv;
     jj = (jj % c) * p.ilv + jj / c;
   }
-  if (jj >= ug) return;  // padding
+  if (jj >= ug) continue;  // padding
   const int g = tg % p.Hkv, t = tg / p.Hkv;
   // the pack of this unit and its splits: packs get units in proportion to
   // their key tiles (at least one each), so splits are of similar length
@@ -383,7 +413,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   auto split_begin = [=](int r2) __attribute__((always_inline)) { return int((long long)r2 * nvt / S); };
   const int v0 = split_begin(rsp);
   const int n = split_begin(rsp + 1) - v0;
-  if (n == 0) return;  // pack shorter than its split count
+  if (n == 0) continue;  // pack shorter than its split count
 
   const int rows_per_branch = p.Wn * p.G;
   // scalars the helper lambdas use, copied so that no lambda takes the
@@ -758,6 +788,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       }
     }
   }
+  }  // next unit
 }
 
 }  // namespace
@@ -767,8 +798,25 @@ size_t mfma_slot_bytes(int D) {
   return align_up(size_t(nw) * nb * (D / 32) * 8 * 64 * 4 + size_t(nw) * nb * 128 * 4, 256);
 }
 
+// Compute units of the current device (cached per device): the persistent
+// matrix-core kernel runs one workgroup per CU.
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_tree_attn_mfma(int D, const MfmaParams& p, hipStream_t s, bool prefill) {
-  const dim3 grid(p.nwg), block(mfma_waves(D) * 64);
+  // one workgroup per CU (a multiple of 8, so every XCD runs workgroups of
+  // its own queue), or fewer when there are fewer queue entries
+  const int cus = device_cus() / 8 * 8;
+  const dim3 grid(unsigned(p.nwg < cus ? p.nwg : (cus > 0 ? cus : 8))), block(mfma_waves(D) * 64);
   switch (D) {
     case 64:
       if (prefill) tree_attn_mfma_kernel<64, true><<<grid, block, 0, s>>>(p);
