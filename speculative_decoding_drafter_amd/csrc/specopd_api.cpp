@@ -30,6 +30,9 @@ specopd_status check_tree_desc(const specopd_tree_attn_desc* d) {
   if (double(d->T) * d->B > 2147483647.0 || nodes * d->Hq > 2147483647.0 ||
       double(d->T) * d->L * d->Hkv * d->D > 9.0e15)
     return SPECOPD_ERR_UNSUPPORTED;
+  // the matrix-core kernel addresses one trunk's K (and V) with 32-bit offsets
+  if (d->dtype == SPECOPD_BF16 && double(d->L) * d->Hkv * d->D * 2.0 > 4294967295.0)
+    return SPECOPD_ERR_UNSUPPORTED;
   return SPECOPD_OK;
 }
 
@@ -43,6 +46,8 @@ specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
   if (!(isfinite(d->rope_base) && isfinite(d->scale))) return SPECOPD_ERR_INVALID_ARGUMENT;
   // one trunk is one tree call of L-1 one-node branches: the same index limits
   if (double(d->L) * d->Hq > 2147483647.0 || double(d->T) * d->L * (d->Hq + d->Hkv) * d->D > 9.0e15)
+    return SPECOPD_ERR_UNSUPPORTED;
+  if (d->dtype == SPECOPD_BF16 && double(d->L) * d->Hkv * d->D * 2.0 > 4294967295.0)
     return SPECOPD_ERR_UNSUPPORTED;
   return SPECOPD_OK;
 }

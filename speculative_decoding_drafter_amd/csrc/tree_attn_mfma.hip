@@ -84,7 +84,10 @@ struct Geo {
   static constexpr int VROW = 2 * D + 32;        // LDS bytes per V row (two pad chunks)
   static constexpr int SK = KROW / 16, SV = VROW / 16;
   static constexpr int KBYTES = KT * KROW;
-  static constexpr int NJ = (KBYTES + KT * VROW + 1023) / 1024;  // 1 KB writes a tile needs
+  // the V rows start on a 1 KB boundary, so each wave-wide 1 KB write of a
+  // tile is all K or all V (one source tensor per load instruction)
+  static constexpr int VBASE = (KBYTES + 1023) / 1024 * 1024;
+  static constexpr int NJ = (VBASE + KT * VROW + 1023) / 1024;  // 1 KB writes a tile needs
   static constexpr int JPW = (NJ + NW - 1) / NW; // wave writes per tile (every wave the same)
   static constexpr int BUFB = JPW * NW * 1024;   // bytes of one staged K+V tile, with slack
   // staged tiles: up to six where they fit in LDS, at least four.  With
@@ -172,17 +175,27 @@ __device__ __forceinline__ void tile_scores(const char* kl,
   }
 }
 
-// Loads whole trunk tile v (every key < L) into LDS buffer lb: one add per
-// load from this lane's tile-0 source.
+// Load q of this wave for a whole trunk tile (every key < L) of the current
+// (trunk, kv head): a buffer load from the trunk's K or V (uniform per load:
+// its 1 KB of the tile is all K or all V) at this lane's fixed offset into
+// the tile plus the tile's offset as a scalar, straight into LDS buffer lb.
 template <int D>
-__device__ __forceinline__ void dma_whole(int v, int kvrow, int wave, char* lb,
-                                          const uint16_t* const* qsrc) {
+__device__ __forceinline__ void dma_whole_q(int q, int v, int kvrow, int wave, char* lb,
+                                            const uint16_t* kbase, const uint16_t* vbase, int tbytes,
+                                            int toffq) {
   using Gm = Geo<D>;
-  const size_t step = size_t(v) * KT * kvrow;
+  const int w = wave + Gm::NW * q;
+  const int so = int(uint32_t(v) * uint32_t(KT * 2) * uint32_t(kvrow));  // < 4 GiB (host check)
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w * 1024 >= Gm::VBASE ? vbase : kbase), (short)0, tbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lb + w * 1024), 16,
+                                           toffq, so, 0, 0);
+}
+template <int D>
+__device__ __forceinline__ void dma_whole(int v, int kvrow, int wave, char* lb, const uint16_t* kbase,
+                                          const uint16_t* vbase, int tbytes, const int (&toff)[Geo<D>::JPW]) {
 #pragma unroll
-  for (int q = 0; q < Gm::JPW; ++q)
-    __builtin_amdgcn_global_load_lds(qsrc[q] + step, (__attribute__((address_space(3))) void*)(
-                                                         lb + (wave + Gm::NW * q) * 1024), 16, 0, 0);
+  for (int q = 0; q < Geo<D>::JPW; ++q) dma_whole_q<D>(q, v, kvrow, wave, lb, kbase, vbase, tbytes, toff[q]);
 }
 
 // Loads key tile v (trunk tile, or tail tile of branch nodes) of the current
@@ -195,11 +208,12 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
                                          const uint16_t* bk, const uint16_t* bv,
                                          const int32_t* pord, char* lb,
                                          const int (&dcode)[Geo<D>::JPW],
-                                         const uint16_t* const* qsrc) {
+                                         const uint16_t* kbase, const uint16_t* vbase, int tbytes,
+                                         const int (&toff)[Geo<D>::JPW]) {
   using Gm = Geo<D>;
   const bool trunk = v < ntrunk;
   if (trunk && (v + 1) * KT <= Lk) {
-    dma_whole<D>(v, kvrow, wave, lb, qsrc);
+    dma_whole<D>(v, kvrow, wave, lb, kbase, vbase, tbytes, toff);
     return;
   }
 #pragma unroll
@@ -258,14 +272,29 @@ __device__ __forceinline__ void load_k(const char* kl, bf16x8 (&kop)[D / 16]) {
 // probabilities.  When knext is given, the K operands of the tile after next
 // are read into kop during the V products.  sched_barrier(0) keeps the
 // compiler from regrouping the steps.
-template <int D, bool KNEXT>
+// A whole trunk tile's loads (dma_whole_q) that tile_compute issues among its
+// score products.  With tbytes = 0 (no tile left to load) every lane is out
+// of the buffer's range and the loads fetch nothing: the step stays free of
+// branches, which would let the compiler move the exponentials out of the
+// score products.
+template <int D>
+struct TileLoads {
+  int v, kvrow, wave;
+  char* lb;
+  const uint16_t *kbase, *vbase;
+  int tbytes;
+  int toff[Geo<D>::JPW];
+};
+
+template <int D, bool KNEXT, bool MX, bool DMA>
 __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* knext,
                                              lds_cchar* __restrict__ vl,
                                              const bf16x8 (&qop)[Geo<D>::NB][D / 16],
                                              const f32x16 (&cinit)[Geo<D>::NB],
                                              const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
                                              float (&lsum)[Geo<D>::NB],
-                                             f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG]) {
+                                             f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG],
+                                             const TileLoads<D>& dma, float (&mx)[Geo<D>::NB]) {
   using Gm = Geo<D>;
   constexpr int NB = Gm::NB, KS = D / 16, OREG = Gm::OREG;
   constexpr int NPAIR = NB * 8;                    // pairs of probabilities per lane
@@ -305,6 +334,14 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
     }
 #pragma unroll
     for (int q = s2 * EARLY / KS; q < (s2 + 1) * EARLY / KS; ++q) pair(q);
+    // this wave's loads of a later tile, spread over the k-steps (the CU's
+    // vector memory path takes a wave-wide 16-byte load into LDS every 16
+    // cycles; issued in one burst by every wave they would queue and hold
+    // the waves at the issue)
+#pragma unroll
+    for (int q = s2 * Gm::JPW / KS; q < (s2 + 1) * Gm::JPW / KS; ++q)
+      if constexpr (DMA)
+        dma_whole_q<D>(q, dma.v, dma.kvrow, dma.wave, dma.lb, dma.kbase, dma.vbase, dma.tbytes, dma.toff[q]);
     __builtin_amdgcn_sched_barrier(0);
   }
   // V products by (row block, key half); the late pairs go between the first
@@ -321,6 +358,17 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
         if (sl < NPV / 2) {
 #pragma unroll
           for (int q = EARLY + sl * LATE / (NPV / 2); q < EARLY + (sl + 1) * LATE / (NPV / 2); ++q) pair(q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // the maxima of the next tile's scores (for the reference check) over
+      // the second half of the V products
+      if constexpr (MX) {
+        if (sl >= NPV / 2) {
+          constexpr int NE = NB * 16, H = NPV / 2;
+#pragma unroll
+          for (int k = (sl - H) * NE / H; k < (sl - H + 1) * NE / H; ++k)
+            mx[k >> 4] = (k & 15) == 0 ? Snext[k >> 4][0] : fmaxf(mx[k >> 4], Snext[k >> 4][k & 15]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -345,10 +393,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   int* const s_last = reinterpret_cast<int*>(smem + Gm::NBUF * Gm::BUFB);
   int* const s_unit = s_last + 1;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
   const int gi = lane >> 4, rq = lane & 15;
-  const int nwg = gridDim.x;
 
   // Work unit u = (t * Hkv + g) * ugp + j, j < npacks * nsplit the j-th split
   // of the (trunk, kv head) group in pack order; ugp >= that count pads the
@@ -423,21 +470,22 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   const size_t slot_bytes = p.slot_bytes;
 
   // This lane's 16-byte slot in each of its wave's tile loads: key row,
-  // chunk, K or V.  Pad chunks and the slack after the V rows load chunk 0 of
-  // a valid row.
+  // chunk, K or V.  Pad chunks, the gap before the V rows and the slack after
+  // them load chunk 0 of a valid row (of K or V, as the rest of the load).
   int dcode[Gm::JPW];
 #pragma unroll
   for (int q = 0; q < Gm::JPW; ++q) {
-    const int pos = (wave + Gm::NW * q) * 64 + lane;
-    int key = 0, c = 0, isv = 0;
+    const int w = wave + Gm::NW * q;
+    const int pos = w * 64 + lane;
+    int key = 0, c = 0;
+    const int isv = w * 1024 >= Gm::VBASE;
     if (pos < KT * Gm::SK) {
       key = pos / Gm::SK;
       c = pos - key * Gm::SK;
-    } else if (pos < KT * (Gm::SK + Gm::SV)) {
-      const int pv = pos - KT * Gm::SK;
+    } else if (isv && pos < Gm::VBASE / 16 + KT * Gm::SV) {
+      const int pv = pos - Gm::VBASE / 16;
       key = pv / Gm::SV;
       c = pv - key * Gm::SV;
-      isv = 1;
     }
     if (c >= Gm::CH) c = 0;
     dcode[q] = key | (c << 5) | (isv << 12);
@@ -463,19 +511,26 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     const uint16_t* bk = p.kr + (tB * p.Wn * p.Hkv + g) * D;
     const uint16_t* bv = p.v + (tB * p.Wn * p.Hkv + g) * D;
     const int kvrow = p.Hkv * D;  // elements between consecutive keys
-    // this lane's source of each of its tile loads for trunk tile 0
-    const uint16_t* qsrc[Gm::JPW];
+    // whole trunk tiles: buffer resources over trunk t's K and V (under 4 GiB
+    // each, checked on the host) and this lane's byte offset in each of its
+    // tile loads for trunk tile 0
+    const size_t tbase = size_t(t) * p.L * p.Hkv * D;
+    const int tbytes = int(uint32_t(size_t(p.L) * kvrow * 2));
+    const uint16_t* const kbase = p.trunk_k + tbase;
+    const uint16_t* const vbase = p.trunk_v + tbase;
+    int toff[Gm::JPW];
 #pragma unroll
     for (int q = 0; q < Gm::JPW; ++q) {
       const int code = dcode[q];
-      qsrc[q] = (((code >> 12) & 1) ? tv : tk) + (code & 31) * kvrow + ((code >> 5) & 127) * 8;
+      toff[q] = ((code & 31) * kvrow + ((code >> 5) & 127) * 8 + g * D) * 2;
     }
 
     // ---- tile loads: global -> LDS buffer b
 #define DMA_TILE(v, b) \
-  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, qsrc)
+  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, \
+              kbase, vbase, tbytes, toff)
     const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
-    const int voff = Gm::KBYTES + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
+    const int voff = Gm::VBASE + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
 
     // ---- staging.  Tile j of this range goes to LDS buffer j % NBUF and is
     // loaded AH = NBUF - 1 tiles ahead of the tile being accumulated, in
@@ -566,17 +621,11 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       }
     };
     // move the reference maximum of rows that need it (rare)
-    auto settle = [&](f32x16 (&S)[NB]) __attribute__((always_inline)) {
+    // (mx: the maxima of each row block's scores in this lane)
+    auto settle_mx = [&](f32x16 (&S)[NB], const float (&mx)[NB]) __attribute__((always_inline)) {
       bool any = false;
-      float mx[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float m = S[nb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
-        mx[nb] = m;
-        any |= m > lim[nb];
-      }
+      for (int nb = 0; nb < NB; ++nb) any |= mx[nb] > lim[nb];
       if (__any(any)) {
         // keeps this rare path a branch: without a side effect the compiler
         // would fold it into the common path as unconditional multiplies
@@ -600,6 +649,17 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
         }
       }
     };
+    auto settle = [&](f32x16 (&S)[NB]) __attribute__((always_inline)) {
+      float mx[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float m = S[nb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
+        mx[nb] = m;
+      }
+      settle_mx(S, mx);
+    };
 
     wait_tiles<Gm::JPW>(inflight(NEED - 1));  // tiles 0 .. NEED-1 have landed
     lds_barrier();
@@ -619,10 +679,22 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     int nfast = min(nomask - v0 - 1, n - 1);
     if (v0 + n > nwhole) nfast = min(nfast, nwhole - v0 - AH);
     auto fast = [&](int i, const f32x16 (&Sc)[NB], f32x16 (&Sn)[NB]) __attribute__((always_inline)) {
-      if (i + AH < n) dma_whole<D>(v0 + i + AH, kvrow, wave, buf(i + AH), qsrc);
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
-      tile_compute<D, EK>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum, oacc);
-      settle(Sn);
+      TileLoads<D> tl;
+      const bool on = i + AH < n;
+      tl.v = on ? v0 + i + AH : v0;
+      tl.kvrow = kvrow;
+      tl.wave = wave;
+      tl.lb = buf(i + AH);
+      tl.kbase = kbase;
+      tl.vbase = vbase;
+      tl.tbytes = on ? tbytes : 0;
+#pragma unroll
+      for (int q = 0; q < Gm::JPW; ++q) tl.toff[q] = toff[q];
+      float mx[NB];
+      tile_compute<D, EK, true, true>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum,
+                                      oacc, tl, mx);
+      settle_mx(Sn, mx);
       wait_tiles<Gm::JPW>(inflight(i + NEED));
       lds_barrier();
     };
@@ -637,7 +709,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     for (; i < n; ++i) {
       if (i + AH < n) DMA_TILE(v0 + i + AH, (i + AH) % NBUF);
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
-      tile_compute<D, EK>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sa, Sb, lsum, oacc);
+      float mxu[NB];
+      TileLoads<D> tl{};
+      tile_compute<D, EK, false, false>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sa, Sb, lsum,
+                                        oacc, tl, mxu);
       if (i + 1 < n) {
         mask(v0 + i + 1, Sb);
         settle(Sb);

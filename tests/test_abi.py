@@ -68,6 +68,7 @@ def _tcall(desc, ws_bytes=1 << 30, **over):
     ("dtype", 7, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),     # only SPECOPD_TREE_BATCH_INVARIANT is defined
     ("rope_base", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 20_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # one trunk's bf16 K beyond 4 GiB
 ])
 def test_tree_desc_errors(field, value, code):
     d = _tdesc()
@@ -191,6 +192,7 @@ def _pcall(desc, ws_bytes=1 << 30, **over):
     ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("scale", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("L", 300_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # L * Hq beyond 32-bit row indexing
+    ("L", 20_000_000, sd.SPECOPD_ERR_UNSUPPORTED),   # one trunk's bf16 K beyond 4 GiB
 ])
 def test_prefill_desc_errors(field, value, code):
     d = _pdesc()
