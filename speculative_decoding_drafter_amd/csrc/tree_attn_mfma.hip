@@ -373,7 +373,7 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
         }
       }
     }
-    if (KNEXT && g == NB * 2 - 2) load_k<D>(knext, kop);
+    if (KNEXT && g == 0) load_k<D>(knext, kop);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) lsum[nb] = acc[nb];
@@ -678,6 +678,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     const int nwhole = min(ntrunk, Lk / KT);
     int nfast = min(nomask - v0 - 1, n - 1);
     if (v0 + n > nwhole) nfast = min(nfast, nwhole - v0 - AH);
+    if (n < AH) nfast = 0;  // the fixed wait below counts on AH tiles in flight from the start
     auto fast = [&](int i, const f32x16 (&Sc)[NB], f32x16 (&Sn)[NB]) __attribute__((always_inline)) {
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
       TileLoads<D> tl;
@@ -695,7 +696,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       tile_compute<D, EK, true, true>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum,
                                       oacc, tl, mx);
       settle_mx(Sn, mx);
-      wait_tiles<Gm::JPW>(inflight(i + NEED));
+      // every fast iteration issues JPW loads (zero-record ones at the end),
+      // so exactly INFL tiles' loads follow those of tile i + NEED
+      wait_vm<INFL * Gm::JPW>();
       lds_barrier();
     };
     int i = 0;
