@@ -263,15 +263,18 @@ __device__ __forceinline__ void load_k(const char* kl, bf16x8 (&kop)[D / 16]) {
 // The matrix-core work of one steady-state tile, in an explicit order (one
 // wave per SIMD, so the wave's own instruction stream has to keep the matrix
 // core busy while the vector unit forms the probabilities).  The exponentials
-// of the current tile are spread over the matrix products: most of them
-// between the k-steps of the next tile's score product (K operands kop,
-// already in registers), together with the reads of the current tile's V
-// operands; with two row blocks, the last quarter (the probabilities of the
-// second block's upper 16 keys) between the first V products, which are
-// ordered by (row block, key half) so that each waits only for its own
-// probabilities.  When knext is given, the K operands of the tile after next
-// are read into kop during the V products.  sched_barrier(0) keeps the
-// compiler from regrouping the steps.
+// of the current tile are spread over the matrix products: between the
+// k-steps of the next tile's score product (K operands kop, already in
+// registers), together with the reads of the current tile's V operands and
+// this wave's loads of a later tile; with two row blocks, the second block's
+// half between the first V products, which are ordered by (row block, key
+// half) so that each waits only for its own probabilities.  The second half
+// of the V products covers the maxima of the next tile's scores.  When
+// knext is given, the K operands of the tile after next are read into kop
+// at the start of the V products.  sched_barrier(0) keeps the compiler from
+// regrouping the steps.  The row sums (v_dot2) are left where instruction
+// selection puts them, after the last product: between the products each
+// one stalls the matrix pipe (measured ~16 cycles apiece).
 // A whole trunk tile's loads (dma_whole_q) that tile_compute issues among its
 // score products.  With tbytes = 0 (no tile left to load) every lane is out
 // of the buffer's range and the loads fetch nothing: the step stays free of
@@ -298,7 +301,10 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
   using Gm = Geo<D>;
   constexpr int NB = Gm::NB, KS = D / 16, OREG = Gm::OREG;
   constexpr int NPAIR = NB * 8;                    // pairs of probabilities per lane
-  constexpr int LATE = NB == 2 ? 4 : 0;            // pairs formed during the V products
+  // pairs formed during the V products: half of them with two row blocks
+  // (the score products' exponentials otherwise saturate the vector unit;
+  // measured 1,687 -> 1,611 cycles per tile from 4 to 8 of 16, flat to 10)
+  constexpr int LATE = NB == 2 ? 8 : 0;
   constexpr int EARLY = NPAIR - LATE;              // pairs formed during the score product
   constexpr int NVO = OREG * 2;                    // V operands (two transposed reads each)
   constexpr int VPS = (NVO + KS - 1) / KS;         // V operands per k-step
