@@ -405,12 +405,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 
   // Work unit u = (t * Hkv + g) * ugp + j, j < npacks * nsplit the j-th split
   // of the (trunk, kv head) group in pack order; ugp >= that count pads the
-  // group to a multiple of ilv.  In chunked mode units are queued to the XCDs
-  // in consecutive blocks (workgroups go to the 8 XCDs round robin), so the
-  // packs of one kv head run side by side on one XCD and stream the same
-  // trunk rows through its L2; when a group spans `ilv` XCD blocks, its packs
-  // are dealt to those blocks alternately, so that each XCD gets a like share
-  // of long and short packs.  The workgroups are persistent (one per CU): each
+  // group to a multiple of ilv.  In chunked mode the groups are queued to the
+  // XCDs in consecutive blocks (workgroups go to the 8 XCDs round robin), so
+  // the packs of a kv head run on one XCD and stream its trunk rows through
+  // that XCD's L2; when a group spans `ilv` XCD blocks, its packs are dealt
+  // to those blocks alternately, so that each XCD gets a like share of long
+  // and short packs.  The workgroups are persistent (one per CU): each
   // takes the front unit of its XCD's queue (packs come longest first) until
   // that queue is empty, then the back units -- the shortest left -- of the
   // other XCDs' queues, so XCDs whose trunks hold less work help the others
@@ -444,9 +444,24 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   if (ub >= p.nunits) continue;  // padding
   const int np = p.npacks;
   const int ug = np * p.nsplit;            // units per (trunk, kv head)
-  const int tg = ub / p.ugp;
-  int jj = ub - tg * p.ugp;
-  if (p.ilv > 1) {
+  // Queue entry -> (group, unit of the group).  A queue holding whole groups
+  // deals them by unit rank (every group's longest pack first, its shortest
+  // last), so the units claimed at the end of the kernel are the shortest
+  // ones of every group, not one group's packs of all lengths; likewise the
+  // single queue of the unchunked mode.
+  int tg, jj;
+  if (!p.chunked) {
+    const int ng = p.T * p.Hkv;
+    tg = ub % ng;
+    jj = ub / ng;
+  } else if (p.ilv == 1) {
+    const int gpx = (p.T * p.Hkv) >> 3;  // groups per XCD queue
+    const int y = ub / nq, e = ub - y * nq;
+    tg = y * gpx + e % gpx;
+    jj = e / gpx;
+  } else {
+    tg = ub / p.ugp;
+    jj = ub - tg * p.ugp;
     const int c = p.ugp / p.ilv;
     jj = (jj % c) * p.ilv + jj / c;
   }
