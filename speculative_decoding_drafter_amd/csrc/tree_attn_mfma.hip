@@ -43,14 +43,15 @@
 // Pipeline per wave (four waves, one per SIMD, each owning 64 rows for head
 // sizes up to 128, so that every K and V operand read from LDS feeds two
 // products): the score product of tile i + 1 is issued step by step together
-// with the exponentials of tile i and the LDS reads of tile i's V operands;
-// the products with V of tile i follow, during which the K operands of tile
-// i + 2 are read.  Tiles go from global memory straight into LDS
-// (global_load_lds: each lane of a wave-wide load writes 16 bytes at base +
-// 16 * lane), through six LDS buffers (four for head size 256), one barrier
-// per tile.  Lanes whose 16 bytes land on a row's pad chunk load a harmless
-// in-bounds chunk that is never read.  Tiles that need no mask for any row
-// of the wave run through a branch-free copy of the step.
+// with the exponentials of tile i, the LDS reads of tile i's V operands and
+// the wave's loads of a later tile; the products with V of tile i follow,
+// at whose start the K operands of tile i + 2 are read.  Tiles go from
+// global memory straight into LDS (each lane of a wave-wide load writes 16
+// bytes at base + 16 * lane), through six LDS buffers (four for head size
+// 256), one barrier per tile.  Lanes whose 16 bytes land on a row's pad
+// chunk load a harmless in-bounds chunk that is never read.  Tiles that need
+// no mask for any row of the wave run through a branch-free copy of the
+// step.
 //
 // Softmax is online in log2 units.  The score product starts from -m (m the
 // row's reference maximum), so scores arrive already shifted; the reference
