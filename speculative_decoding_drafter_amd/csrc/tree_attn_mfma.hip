@@ -203,11 +203,17 @@ __device__ __forceinline__ void dma_whole(int v, int kvrow, int wave, char* lb, 
 // pack into LDS buffer b: this wave's share of the wave-wide 1 KB writes.
 // A plain function rather than a lambda: a lambda's closure here stays in
 // private memory.
-template <int D>
+// With FROM_LDS the branch of a tail slot comes from the pack's branch table
+// in LDS (s_ord, written in the unit's prologue and published by its first
+// barrier), read in inline assembly that waits for LDS only: a load from
+// global memory there waits for every tile load in flight, and so would an
+// LDS read the compiler sees (it cannot tell the table from the tiles being
+// loaded).  The prologue's own tile loads take the global path.
+template <int D, bool FROM_LDS>
 __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk, int kvrow, int Wn,
                                          int ts, int wave, const uint16_t* tk, const uint16_t* tv,
                                          const uint16_t* bk, const uint16_t* bv,
-                                         const int32_t* pord, char* lb,
+                                         const int32_t* pord, const int* s_ord, char* lb,
                                          const int (&dcode)[Geo<D>::JPW],
                                          const uint16_t* kbase, const uint16_t* vbase, int tbytes,
                                          const int (&toff)[Geo<D>::JPW]) {
@@ -232,9 +238,14 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
       const int sl = tau / ts;
       int node = tau - sl * ts;
       if (node >= Wn) node = 0;  // a slot's padding: a valid key that every row masks
-      // branch of a tail slot from global memory: an LDS read here would make
-      // the compiler wait for every load in flight before later LDS reads
-      const int off = (pord[sl] * Wn + node) * kvrow + c * 8;
+      int br;
+      if constexpr (FROM_LDS) {
+        const __attribute__((address_space(3))) int* lp = (const __attribute__((address_space(3))) int*)(s_ord) + sl;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(br) : "v"(lp) : "memory");
+      } else {
+        br = pord[sl];
+      }
+      const int off = (br * Wn + node) * kvrow + c * 8;
       src = (isv ? bv : bk) + off;
     }
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(
@@ -396,9 +407,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
   // The kernel's only LDS object (tile buffers, then one flag word): with a
   // second __shared__ variable the compiler tags LDS accesses with alias
   // scopes and then waits for every global-to-LDS load before any LDS read.
-  __shared__ __attribute__((aligned(1024))) char smem[Gm::NBUF * Gm::BUFB + 16];
+  __shared__ __attribute__((aligned(1024))) char smem[Gm::NBUF * Gm::BUFB + 16 + 1024];
   int* const s_last = reinterpret_cast<int*>(smem + Gm::NBUF * Gm::BUFB);
   int* const s_unit = s_last + 1;
+  int* const s_ord = s_last + 4;  // the current pack's branches (at most 256)
 
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
@@ -548,9 +560,10 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     }
 
     // ---- tile loads: global -> LDS buffer b
-#define DMA_TILE(v, b) \
-  dma_tile<D>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, smem + (b) * Gm::BUFB, dcode, \
-              kbase, vbase, tbytes, toff)
+#define DMA_TILE_(v, b, LDS)                                                                                 \
+  dma_tile<D, LDS>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, s_ord,            \
+                   smem + (b) * Gm::BUFB, dcode, kbase, vbase, tbytes, toff)
+#define DMA_TILE(v, b) DMA_TILE_(v, b, true)
     const int koff = r32 * Gm::KROW + 16 * h;  // this lane's K read in a tile
     const int voff = Gm::VBASE + (4 * (gi >> 1) + (rq >> 2)) * Gm::VROW + 32 * (gi & 1) + 8 * (rq & 3);
 
@@ -567,9 +580,14 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     // tiles issued beyond tile `last`, capped at INFL
     auto inflight = [&](int last) __attribute__((always_inline)) { return max(0, min(INFL, n - 1 - last)); };
 
+    // the pack's branch table for the tail loads of the loop (loaded before
+    // the first tiles, so that waiting for it does not wait for them)
+    static_assert(mfma_waves(D) * 64 >= 256, "one thread per table entry");
+    const int ordv = tid < nbr ? ord[b0 + tid] : 0;
 #pragma unroll
     for (int q = 0; q < AH; ++q)
-      if (q < n) DMA_TILE(v0 + q, q);
+      if (q < n) DMA_TILE_(v0 + q, q, false);
+    if (tid < nbr) s_ord[tid] = ordv;
     // ---- this lane's rows: metadata and the Q^T operand
     int ra[NB], rslot[NB], rbr[NB];  // anchor, pack slot and branch of each row block's row
     bool rok[NB];                     // the row's branch is well formed
@@ -749,6 +767,7 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     }
 
 #undef DMA_TILE
+#undef DMA_TILE_
 
     // ---- finish the pack (or this split of it)
     const int nseg = min(S, nvt);  // non-empty splits of the pack
