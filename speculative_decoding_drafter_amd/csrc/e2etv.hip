@@ -636,6 +636,20 @@ template <int AUX>
 __device__ __forceinline__ u32x2_t buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
   return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
 }
+// The same loads with the whole byte offset in the per-lane offset, which the
+// buffer's range check covers (the scalar offset is not checked): past the
+// row they return zeros without a memory access.  Issued unconditionally, so
+// that the loads of a pass stay in one straight block; loads under per-unit
+// conditions split it into blocks across which the compiler's wait
+// bookkeeping loses count and waits for every load in flight at the first use.
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16c(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ u32x2_t buf_load8c(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
+}
 
 // Gradient of elements [e, e + 4) of a row, e = 4 * (quad), through a buffer
 // resource over the row's gradient: 16 bytes (fp32) or 8 bytes (bf16) per lane.
@@ -649,6 +663,18 @@ __device__ __forceinline__ void store_grad4(__amdgpu_buffer_rsrc_t r, int e, con
   } else {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{gv[0], gv[1], gv[2], gv[3]}), r,
                                            vo, so, kNT);
+  }
+}
+
+// Calls f(integral_constant<k>) for k = 0 .. N-1, each after waiting until at
+// most 2 (N - 1 - k) of this wave's vector-memory loads are in flight (the
+// two loads of each later LDS block).
+template <int N, int K = 0, typename F>
+__device__ __forceinline__ void lds_blocks_in_order(F&& f) {
+  if constexpr (K < N) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (N - 1 - K)) : "memory");
+    f(std::integral_constant<int, K>{});
+    lds_blocks_in_order<N, K + 1>(f);
   }
 }
 
@@ -686,27 +712,27 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   // loads, 4: quads), kStreamBatch loads per thread at a time, the next
   // batch in flight while the current one is used.  Every access below is
   // guarded by the row length (the buffer range check is a second line only)
-  auto stream = [&](auto wtag, auto&& f) {
+  auto stream = [&](auto wtag, auto&& f, int s0) {
     constexpr int W = decltype(wtag)::value;
     using VT = typename std::conditional<W == 8, u32x4, u32x2_t>::type;
     constexpr int SB = W == 8 ? kStreamBatch / 2 : kStreamBatch, STEP = kResThreads * W, BSTEP = STEP * SB;
-    if (sbeg + tid * W >= V) return;
+    if (s0 + tid * W >= V) return;
     VT zc[SB], tc[SB], zn[SB], tn[SB];
     auto load = [&](VT(&z)[SB], VT(&t)[SB], int e0) {
 #pragma unroll
-      for (int i = 0; i < SB; ++i)
-        if (e0 + i * STEP + tid * W < V) {
-          if constexpr (W == 8) {
-            z[i] = buf_load16<0>(zres, tid * 16, (e0 + i * STEP) * 2);
-            t[i] = buf_load16<0>(tres, tid * 16, (e0 + i * STEP) * 2);
-          } else {
-            z[i] = buf_load8<0>(zres, tid * 8, (e0 + i * STEP) * 2);
-            t[i] = buf_load8<0>(tres, tid * 8, (e0 + i * STEP) * 2);
-          }
+      for (int i = 0; i < SB; ++i) {
+        const int off = (e0 + i * STEP + tid * W) * 2;  // past the row: zeros, no access
+        if constexpr (W == 8) {
+          z[i] = buf_load16c<0>(zres, off);
+          t[i] = buf_load16c<0>(tres, off);
+        } else {
+          z[i] = buf_load8c<0>(zres, off);
+          t[i] = buf_load8c<0>(tres, off);
         }
+      }
     };
-    load(zc, tc, sbeg);
-    for (int e0 = sbeg; e0 < V; e0 += BSTEP) {
+    load(zc, tc, s0);
+    for (int e0 = s0; e0 < V; e0 += BSTEP) {
       load(zn, tn, e0 + BSTEP);
 #pragma unroll
       for (int i = 0; i < SB; ++i) {
@@ -723,23 +749,33 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
   using W8 = std::integral_constant<int, 8>;
   using W4 = std::integral_constant<int, 4>;
 
-  // ---- pass A: load the resident elements, then stream the rest; log-sum-exps
+  // ---- pass A: load the resident elements and the first streamed batch,
+  // then the rest of the stream; log-sum-exps.  Loads go out in the order
+  // register units, first streamed batch, LDS blocks, so that each LDS block
+  // can be waited for on its own (the loads after it are the later blocks
+  // only) and summed while the later ones arrive.
+  // (every load is issued; units past the row read zeros and are not used)
   u32x4 zr[kResUnits], tr[kResUnits];
 #pragma unroll
-  for (int k = 0; k < kResUnits; ++k)
-    if (reg_e(k) < V) {
-      zr[k] = buf_load16<kNT>(zres, tid * 16, k * kResThreads * 16);
-      tr[k] = buf_load16<kNT>(tres, tid * 16, k * kResThreads * 16);
-    }
+  for (int k = 0; k < kResUnits; ++k) {
+    zr[k] = buf_load16c<kNT>(zres, reg_e(k) * 2);
+    tr[k] = buf_load16c<kNT>(tres, reg_e(k) * 2);
+  }
+  constexpr int SB0 = kStreamBatch / 2, STEP0 = kResThreads * 8;  // the stream's first batch (16-byte units)
+  u32x4 zs[SB0], ts[SB0];
 #pragma unroll
-  for (int k = 0; k < kResLds; ++k)
-    if (kResRegElems + k * 4096 + tid * 8 < V) {
-      // straight into LDS; each lane's 16 bytes land at the wave's base + 16 * lane
-      uint16_t* zb = s_row + (2 * k) * 4096 + wave * 512;
-      const int so = (kResRegElems + k * 4096) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zres, (lds_void*)zb, 16, tid * 16, so, 0, kNT);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (lds_void*)(zb + 4096), 16, tid * 16, so, 0, kNT);
-    }
+  for (int i = 0; i < SB0; ++i) {
+    zs[i] = buf_load16c<0>(zres, (sbeg + i * STEP0 + tid * 8) * 2);
+    ts[i] = buf_load16c<0>(tres, (sbeg + i * STEP0 + tid * 8) * 2);
+  }
+#pragma unroll
+  for (int k = 0; k < kResLds; ++k) {
+    // straight into LDS; each lane's 16 bytes land at the wave's base + 16 * lane
+    uint16_t* zb = s_row + (2 * k) * 4096 + wave * 512;
+    const int off = (kResRegElems + k * 4096 + tid * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(zres, (lds_void*)zb, 16, off, 0, 0, kNT);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(tres, (lds_void*)(zb + 4096), 16, off, 0, 0, kNT);
+  }
   float mz = kNegInf, sz = 0.f, mt = kNegInf, st = 0.f;
   auto lse8 = [&](const u32x4& zw, const u32x4& tw) {
     float z[8], t[8];
@@ -751,15 +787,20 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
 #pragma unroll
   for (int k = 0; k < kResUnits; ++k)
     if (reg_e(k) < V) lse8(zr[k], tr[k]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS blocks have landed
   // each thread reads back the 16 bytes its own lane loaded
   auto lds8 = [&](int k, int x) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(s_row + (2 * k + x) * 4096 + tid * 8);
   };
-#pragma unroll 1
-  for (int k = 0; k < kResLds; ++k)
+  // block k is in once at most the 2 (kResLds - 1 - k) loads of the later
+  // blocks are in flight
+  lds_blocks_in_order<kResLds>([&](auto kc) {
+    constexpr int k = decltype(kc)::value;
     if (kResRegElems + k * 4096 + tid * 8 < V) lse8(lds8(k, 0), lds8(k, 1));
-  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { lse8(zw, tw); });
+  });
+#pragma unroll
+  for (int i = 0; i < SB0; ++i)
+    if (sbeg + i * STEP0 + tid * 8 < V) lse8(zs[i], ts[i]);
+  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { lse8(zw, tw); }, sbeg + SB0 * STEP0);
   block_lse2<kResThreads>(mz, sz, mt, st, red);
   const float nlz = -(mz * kLog2e + log2f(sz));
   const float nlt = -(mt * kLog2e + log2f(st));
@@ -781,7 +822,7 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
       g += (lq < lp) ? e : 0.f;
     }
   };
-  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { overlap8(zw, tw); });
+  stream(W8{}, [&](const u32x4& zw, const u32x4& tw, int) { overlap8(zw, tw); }, sbeg);
 #pragma unroll
   for (int k = 0; k < kResUnits; ++k)
     if (reg_e(k) < V) overlap8(zr[k], tr[k]);
@@ -818,7 +859,7 @@ __global__ __launch_bounds__(kResThreads, 1) void e2etv_resident_kernel(const Fu
     }
     store_grad4<GBF16>(gres, e, gv);
   };
-  stream(W4{}, grad4);
+  stream(W4{}, grad4, sbeg);
   // LDS blocks, read as quads here (any wave's block: every wave's loads
   // completed before the barriers of pass B); block 0 first, so that its
   // space can then stage the register units' gradients
