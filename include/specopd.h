@@ -68,8 +68,9 @@ typedef enum { SPECOPD_F32 = 0, SPECOPD_BF16 = 1 } specopd_dtype;
  * Problem sizes:  T trunks of length L; B branches per trunk (one anchor
  * each); Wn nodes per branch (1 <= Wn <= 64); Hq query heads and Hkv kv heads
  * (Hq % Hkv == 0, query head h reads kv head h / (Hq/Hkv)); head size D in
- * {64, 128, 256}.  bf16 calls need one trunk's K (L * Hkv * D elements) under
- * 4 GiB, else SPECOPD_ERR_UNSUPPORTED.
+ * {64, 128, 256}.  bf16 calls need one trunk's K (L * Hkv * D elements) and
+ * one trunk's branch-node keys (B * Wn * Hkv * D elements) under 4 GiB each,
+ * else SPECOPD_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t T, L, B, Wn, Hq, Hkv, D;

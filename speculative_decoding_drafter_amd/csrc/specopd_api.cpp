@@ -30,8 +30,10 @@ specopd_status check_tree_desc(const specopd_tree_attn_desc* d) {
   if (double(d->T) * d->B > 2147483647.0 || nodes * d->Hq > 2147483647.0 ||
       double(d->T) * d->L * d->Hkv * d->D > 9.0e15)
     return SPECOPD_ERR_UNSUPPORTED;
-  // the matrix-core kernel addresses one trunk's K (and V) with 32-bit offsets
-  if (d->dtype == SPECOPD_BF16 && double(d->L) * d->Hkv * d->D * 2.0 > 4294967295.0)
+  // the matrix-core kernel addresses one trunk's K (and V), and the keys (and
+  // values) of one trunk's branch nodes, with 32-bit offsets
+  if (d->dtype == SPECOPD_BF16 && (double(d->L) * d->Hkv * d->D * 2.0 > 4294967295.0 ||
+                                   double(d->B) * d->Wn * d->Hkv * d->D * 2.0 > 4294967295.0))
     return SPECOPD_ERR_UNSUPPORTED;
   return SPECOPD_OK;
 }

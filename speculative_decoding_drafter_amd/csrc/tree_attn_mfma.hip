@@ -51,7 +51,8 @@
 // 256), one barrier per tile.  Lanes whose 16 bytes land on a row's pad
 // chunk load a harmless in-bounds chunk that is never read.  Tiles that need
 // no mask for any row of the wave run through a branch-free copy of the
-// step.
+// step; the last tiles of a unit (edge and tail tiles) through a second copy
+// that masks the scores it forms inside the step.
 //
 // Softmax is online in log2 units.  The score product starts from -m (m the
 // row's reference maximum), so scores arrive already shifted; the reference
@@ -253,6 +254,46 @@ __device__ __forceinline__ void dma_tile(int v, int ntrunk, int nt_total, int Lk
   }
 }
 
+// Reads N entries of the pack's branch table in LDS (one per lane and load),
+// in inline assembly that waits for LDS only (see dma_tile): all N reads go
+// out before the one wait.
+typedef const __attribute__((address_space(3))) int* lds_cint;
+template <int N>
+struct OrdGather;
+template <>
+struct OrdGather<3> {
+  static __device__ __forceinline__ void run(int (&r)[3], lds_cint const (&a)[3]) {
+    asm volatile("ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2])
+                 : "v"(a[0]), "v"(a[1]), "v"(a[2])
+                 : "memory");
+  }
+};
+template <>
+struct OrdGather<5> {
+  static __device__ __forceinline__ void run(int (&r)[5], lds_cint const (&a)[5]) {
+    asm volatile(
+        "ds_read_b32 %0, %5\n\tds_read_b32 %1, %6\n\tds_read_b32 %2, %7\n\tds_read_b32 %3, %8\n\t"
+        "ds_read_b32 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+        : "memory");
+  }
+};
+template <>
+struct OrdGather<9> {
+  static __device__ __forceinline__ void run(int (&r)[9], lds_cint const (&a)[9]) {
+    asm volatile(
+        "ds_read_b32 %0, %9\n\tds_read_b32 %1, %10\n\tds_read_b32 %2, %11\n\tds_read_b32 %3, %12\n\t"
+        "ds_read_b32 %4, %13\n\tds_read_b32 %5, %14\n\tds_read_b32 %6, %15\n\tds_read_b32 %7, %16\n\t"
+        "ds_read_b32 %8, %17\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "v"(a[8])
+        : "memory");
+  }
+};
+
 // LDS address of this lane's first transposed V read in a staged tile, as an
 // opaque value: the tile's reads then share one base register with immediate
 // offsets (otherwise the compiler hoists one address register per read out of
@@ -301,7 +342,10 @@ struct TileLoads {
   int toff[Geo<D>::JPW];
 };
 
-template <int D, bool KNEXT, bool MX, bool DMA>
+// With MASK the maxima are taken after the next tile's scores are masked:
+// score i of row block nb stays where bit 8(i/4) + i%4 of vis[nb] is set
+// (vis already shifted by this lane's 4h keys) and becomes -inf elsewhere.
+template <int D, bool KNEXT, bool MX, bool DMA, bool MASK = false>
 __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* knext,
                                              lds_cchar* __restrict__ vl,
                                              const bf16x8 (&qop)[Geo<D>::NB][D / 16],
@@ -309,7 +353,8 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
                                              const f32x16 (&Scur)[Geo<D>::NB], f32x16 (&Snext)[Geo<D>::NB],
                                              float (&lsum)[Geo<D>::NB],
                                              f32x16 (&oacc)[Geo<D>::NB][Geo<D>::OREG],
-                                             const TileLoads<D>& dma, float (&mx)[Geo<D>::NB]) {
+                                             const TileLoads<D>& dma, float (&mx)[Geo<D>::NB],
+                                             const uint32_t (&vis)[Geo<D>::NB]) {
   using Gm = Geo<D>;
   constexpr int NB = Gm::NB, KS = D / 16, OREG = Gm::OREG;
   constexpr int NPAIR = NB * 8;                    // pairs of probabilities per lane
@@ -385,8 +430,21 @@ __device__ __forceinline__ void tile_compute(bf16x8 (&kop)[D / 16], const char* 
         if (sl >= NPV / 2) {
           constexpr int NE = NB * 16, H = NPV / 2;
 #pragma unroll
-          for (int k = (sl - H) * NE / H; k < (sl - H + 1) * NE / H; ++k)
-            mx[k >> 4] = (k & 15) == 0 ? Snext[k >> 4][0] : fmaxf(mx[k >> 4], Snext[k >> 4][k & 15]);
+          for (int k = (sl - H) * NE / H; k < (sl - H + 1) * NE / H; ++k) {
+            const int nb = k >> 4, e = k & 15;
+            if constexpr (MASK) {
+              // all ones where the key is visible, else zero; then a bit
+              // select in inline assembly (the compiler's own form of this
+              // select on matrix-core results gave every element the first
+              // element's value).  The scores were written several products
+              // earlier, so the read needs no wait states.
+              const int keep = __builtin_amdgcn_sbfe(int(vis[nb]), 8 * (e >> 2) + (e & 3), 1);
+              float r;
+              asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(keep), "v"(Snext[nb][e]), "s"(0xff800000u));
+              Snext[nb][e] = r;
+            }
+            mx[nb] = e == 0 ? Snext[nb][0] : fmaxf(mx[nb], Snext[nb][e]);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -559,6 +617,12 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       toff[q] = ((code & 31) * kvrow + ((code >> 5) & 127) * 8 + g * D) * 2;
     }
 
+    // tail tiles in the loop: buffer resources over the trunk's branch-node
+    // K and V from this kv head's first element on (under 4 GiB, checked on
+    // the host); slots are a power of two keys apart
+    const int bbytes = int(uint32_t((size_t(p.B) * Wn * kvrow - size_t(g) * D) * 2));
+    const int lts = 31 - __builtin_clz(ts);
+
     // ---- tile loads: global -> LDS buffer b
 #define DMA_TILE_(v, b, LDS)                                                                                 \
   dma_tile<D, LDS>(v, ntrunk, nt_total, Lk, kvrow, Wn, ts, wave, tk, tv, bk, bv, ord + b0, s_ord,            \
@@ -711,14 +775,21 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
     bf16x8 kop[D / 16];
     if constexpr (EK) load_k<D>(smem + Gm::BUFB + koff, kop);  // tile 1 (stale data if n == 1: unused)
 
-    // Fast iterations: the scored tile needs no mask for this wave's rows and
-    // the tile loaded (if any) is a whole trunk tile, so the step is straight
-    // code.  Tiles [0, nomask) of the pack are visible to every row of the wave.
+    // Fast iterations (every one but the last): the straight-code step.  In
+    // the first ones the scored tile needs no mask for this wave's rows and
+    // the tile loaded (if any) is a whole trunk tile (the lane's offset into
+    // tile 0 plus the tile's offset as a scalar); tiles [0, nomask) of the
+    // pack are visible to every row of the wave.  The later ones (`fastx`)
+    // load tail tiles and trunk tiles that end past L too (the lane's whole
+    // offset in the range-checked part: keys past L read zeros), and mask
+    // the scored tile after the products where a row of the wave needs it.
     const int nomask = min(ntrunk, (wave_amin + 1) / KT);
     const int nwhole = min(ntrunk, Lk / KT);
-    int nfast = min(nomask - v0 - 1, n - 1);
-    if (v0 + n > nwhole) nfast = min(nfast, nwhole - v0 - AH);
-    if (n < AH) nfast = 0;  // the fixed wait below counts on AH tiles in flight from the start
+    int nplain = min(nomask - v0 - 1, n - 1);
+    if (v0 + n > nwhole) nplain = min(nplain, nwhole - v0 - AH);
+    // the fixed wait in the steps counts on AH tiles in flight from the start
+    const int nfast = n < AH ? 0 : n - 1;
+    if (n < AH) nplain = 0;
     auto fast = [&](int i, const f32x16 (&Sc)[NB], f32x16 (&Sn)[NB]) __attribute__((always_inline)) {
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
       TileLoads<D> tl;
@@ -733,8 +804,77 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
 #pragma unroll
       for (int q = 0; q < Gm::JPW; ++q) tl.toff[q] = toff[q];
       float mx[NB];
+      const uint32_t vis[NB] = {};
       tile_compute<D, EK, true, true>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn, lsum,
-                                      oacc, tl, mx);
+                                      oacc, tl, mx, vis);
+      settle_mx(Sn, mx);
+      // every fast iteration issues JPW loads (zero-record ones at the end),
+      // so exactly INFL tiles' loads follow those of tile i + NEED
+      wait_vm<INFL * Gm::JPW>();
+      lds_barrier();
+    };
+    auto fastx = [&](int i, const f32x16 (&Sc)[NB], f32x16 (&Sn)[NB]) __attribute__((always_inline)) {
+      if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
+      TileLoads<D> tl;
+      const int vl = v0 + i + AH;  // the tile this step loads
+      const bool on = i + AH < n;
+      tl.kvrow = kvrow;
+      tl.wave = wave;
+      tl.lb = buf(i + AH);
+      if (on && vl >= nwhole) {
+        tl.v = 0;
+        if (vl < ntrunk) {
+          const uint32_t to = uint32_t(vl) * uint32_t(KT * 2) * uint32_t(kvrow);
+          tl.kbase = kbase;
+          tl.vbase = vbase;
+          tl.tbytes = tbytes;
+#pragma unroll
+          for (int q = 0; q < Gm::JPW; ++q) tl.toff[q] = int(uint32_t(toff[q]) + to);
+        } else {
+          // tail key tau of the pack: slot tau / ts, node tau % ts (a slot's
+          // padding and keys past the last node load node 0 of a valid slot,
+          // which every row masks)
+          lds_cint la[Gm::JPW];
+          int node[Gm::JPW], br[Gm::JPW];
+#pragma unroll
+          for (int q = 0; q < Gm::JPW; ++q) {
+            int tau = (vl - ntrunk) * KT + (dcode[q] & 31);
+            if (tau >= nt_total) tau = 0;
+            node[q] = tau & (ts - 1);
+            if (node[q] >= Wn) node[q] = 0;
+            la[q] = (lds_cint)(s_ord) + (tau >> lts);
+          }
+          OrdGather<Gm::JPW>::run(br, la);
+          tl.kbase = bk;
+          tl.vbase = bv;
+          tl.tbytes = bbytes;
+#pragma unroll
+          for (int q = 0; q < Gm::JPW; ++q)
+            tl.toff[q] = ((br[q] * Wn + node[q]) * kvrow + ((dcode[q] >> 5) & 127) * 8) * 2;
+        }
+      } else {
+        tl.v = on ? vl : v0;
+        tl.kbase = kbase;
+        tl.vbase = vbase;
+        tl.tbytes = on ? tbytes : 0;
+#pragma unroll
+        for (int q = 0; q < Gm::JPW; ++q) tl.toff[q] = toff[q];
+      }
+      // visible keys of the tile whose scores the step forms, per row block
+      const int vn = v0 + i + 1;
+      uint32_t vis[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if (vn < ntrunk) {
+          const int lm = ra[nb] - vn * KT - 4 * h;  // key offsets 0..lm of the lane's keys are visible
+          vis[nb] = lm >= 31 ? ~0u : lm < 0 ? 0u : (2u << lm) - 1u;
+        } else {
+          vis[nb] = tail_window(rmask[nb], rslot[nb], ts, (vn - ntrunk) * KT) >> (4 * h);
+        }
+      }
+      float mx[NB];
+      tile_compute<D, EK, true, true, true>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sc, Sn,
+                                            lsum, oacc, tl, mx, vis);
       settle_mx(Sn, mx);
       // every fast iteration issues JPW loads (zero-record ones at the end),
       // so exactly INFL tiles' loads follow those of tile i + NEED
@@ -742,9 +882,13 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       lds_barrier();
     };
     int i = 0;
-    for (; i + 1 < nfast; i += 2) {
+    for (; i + 1 < nplain; i += 2) {
       fast(i, Sa, Sb);
       fast(i + 1, Sb, Sa);
+    }
+    for (; i + 1 < nfast; i += 2) {
+      fastx(i, Sa, Sb);
+      fastx(i + 1, Sb, Sa);
     }
     // remaining iterations: scores of tile i+1 overlap the probabilities of
     // tile i; after the last tile the scores are unused (they keep the block
@@ -754,8 +898,9 @@ __global__ __launch_bounds__(mfma_waves(D) * 64, 1) void tree_attn_mfma_kernel(c
       if constexpr (!EK) load_k<D>(buf(i + 1) + koff, kop);
       float mxu[NB];
       TileLoads<D> tl{};
+      const uint32_t visu[NB] = {};
       tile_compute<D, EK, false, false>(kop, buf(i + 2) + koff, v_base(buf(i) + voff), qop, cinit, Sa, Sb, lsum,
-                                        oacc, tl, mxu);
+                                        oacc, tl, mxu, visu);
       if (i + 1 < n) {
         mask(v0 + i + 1, Sb);
         settle(Sb);

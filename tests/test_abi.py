@@ -69,6 +69,7 @@ def _tcall(desc, ws_bytes=1 << 30, **over):
     ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),     # only SPECOPD_TREE_BATCH_INVARIANT is defined
     ("rope_base", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
     ("L", 20_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # one trunk's bf16 K beyond 4 GiB
+    ("B", 3_000_000, sd.SPECOPD_ERR_UNSUPPORTED),   # one trunk's bf16 branch-node keys beyond 4 GiB
 ])
 def test_tree_desc_errors(field, value, code):
     d = _tdesc()
