@@ -37,3 +37,5 @@ __all__ = [
     "suffix_sums", "e2etv", "e2etv_branch", "score_row_source", "new_score_rows",
     "shared_row_count", "trunk_prefill", "trunk_prefill_cache",
 ]
+from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, replay_span,
+                  anchor_state, gdn_branch, gdn_replay, update_counts)

@@ -90,11 +90,46 @@ class LossConfig:
 
 
 @dataclass(frozen=True)
+class GdnConfig:
+    """Linear-attention (GDN) branch replay workload: T trunks of length L
+    (first P tokens prompt) with a recurrent state checkpoint every C trunk
+    tokens, B anchored branches per trunk (each a tree of Wn nodes), H heads
+    with key and value size D.
+
+    Value laws: keys (trunk and branch) uniform on the unit sphere (Gaussian
+    draws scaled to unit length), values and queries N(0, 1), all rounded to
+    the dtype; decay gates uniform in [gate_lo, 1); write strengths uniform in
+    [0.05, 0.95); checkpoint states N(0, state_sd^2) in fp32."""
+
+    T: int
+    L: int
+    P: int
+    B: int
+    parent: Tuple[int, ...]
+    H: int
+    D: int
+    dtype: str  # "f32" | "bf16" (queries, keys, values)
+    C: int = 64
+    gate_lo: float = 0.85
+    state_sd: float = 0.1
+
+    @property
+    def Wn(self) -> int:
+        return len(self.parent)
+
+    @property
+    def NC(self) -> int:
+        """Checkpoints per trunk (state after every C tokens)."""
+        return self.L // self.C
+
+
+@dataclass(frozen=True)
 class Workload:
     cid: int
     name: str
     attn: Optional[AttnConfig]
     loss: Optional[LossConfig]
+    gdn: Optional[GdnConfig] = None
 
 
 _C4P, _C4D = chain(4)
@@ -116,6 +151,7 @@ WORKLOADS = {
         AttnConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, depth=_C8D,
                    Hq=32, Hkv=8, D=128, dtype="bf16"),
         LossConfig(R=64, parent=_C8P, V=VOCAB, dtype="bf16", recipe="noise"),
+        GdnConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, H=32, D=128, dtype="bf16"),
     ),
     3: Workload(
         3, "batch8",
@@ -123,6 +159,7 @@ WORKLOADS = {
                    Hq=32, Hkv=8, D=128, dtype="bf16"),
         LossConfig(R=8 * 128, parent=_C16P, V=VOCAB, dtype="bf16",
                    recipe="rho", sd=3.0, rho=0.8),
+        GdnConfig(T=8, L=8192, P=2048, B=128, parent=_C16P, H=32, D=128, dtype="bf16"),
     ),
     4: Workload(
         4, "loss_stress",
@@ -134,6 +171,7 @@ WORKLOADS = {
         AttnConfig(T=1, L=32768, P=8192, B=512, parent=FORK_PARENT,
                    depth=FORK_DEPTH, Hq=24, Hkv=4, D=256, dtype="bf16"),
         LossConfig(R=512, parent=FORK_PARENT, V=VOCAB, dtype="bf16", recipe="noise"),
+        GdnConfig(T=1, L=32768, P=8192, B=512, parent=FORK_PARENT, H=16, D=128, dtype="bf16"),
     ),
 }
 
@@ -148,4 +186,8 @@ def shrink_attn(cfg: AttnConfig, **kw) -> AttnConfig:
 
 
 def shrink_loss(cfg: LossConfig, **kw) -> LossConfig:
+    return dataclasses.replace(cfg, **kw)
+
+
+def shrink_gdn(cfg: GdnConfig, **kw) -> GdnConfig:
     return dataclasses.replace(cfg, **kw)

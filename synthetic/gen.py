@@ -29,7 +29,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-from .configs import AttnConfig, LossConfig
+from .configs import AttnConfig, GdnConfig, LossConfig
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -37,6 +37,8 @@ _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 _T_TRUNK_K, _T_TRUNK_V, _T_Q, _T_K, _T_V, _T_ANCH = 1, 2, 3, 4, 5, 6
 _T_DRAFT, _T_TARGET, _T_PERM, _T_PEAK = 11, 12, 13, 14
 _T_PF_Q, _T_PF_K, _T_PF_V = 21, 22, 23
+_T_G_CKPT, _T_G_TK, _T_G_TV, _T_G_TA, _T_G_TB = 31, 32, 33, 34, 35
+_T_G_Q, _T_G_K, _T_G_V, _T_G_A, _T_G_B = 36, 37, 38, 39, 40
 
 
 def derive_seed(seed: int, cid: int, tensor: int) -> int:
@@ -176,3 +178,54 @@ def gen_loss(cfg: LossConfig, seed: int = 0, device="cpu", cid: int = 0,
         "target": target.view(cfg.R, cfg.Wn, V),
         "parent": torch.from_numpy(parent).to(device),
     }
+
+
+def _unit_rows(shape, dtype, device, g, chunk_rows: int = 0) -> torch.Tensor:
+    """Vectors along the last dim uniform on the unit sphere: Gaussian draws
+    scaled to unit length in fp32, then rounded to dtype."""
+    out = torch.empty(shape, dtype=dtype, device=device)
+    step = shape[0] if chunk_rows <= 0 else chunk_rows
+    for r0 in range(0, shape[0], step):
+        r1 = min(shape[0], r0 + step)
+        x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        out[r0:r1].copy_(x / torch.linalg.vector_norm(x, dim=-1, keepdim=True))
+    return out
+
+
+def _uniform(shape, lo: float, hi: float, device, g) -> torch.Tensor:
+    return lo + (hi - lo) * torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+
+
+def gen_gdn(cfg: GdnConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[str, torch.Tensor]:
+    """GDN branch-replay inputs.
+
+    Layouts (row-major): ckpt [T][L/C][H][D][D] fp32 (state after trunk
+    tokens (m+1)C - 1, rows = value dims, columns = key dims); trunk_k,
+    trunk_v [T][L][H][D]; trunk_gate, trunk_beta [T][L][H] fp32; q, k, v
+    [T][B][Wn][H][D]; gate, beta [T][B][Wn][H] fp32; anchors [T][B];
+    parent [T][B][Wn] (int32).  Anchors as for tree attention."""
+    dt = _DT[cfg.dtype]
+    T, L, B, Wn, H, D, NC = cfg.T, cfg.L, cfg.B, cfg.Wn, cfg.H, cfg.D, cfg.NC
+    g = lambda tid: _gen(device, seed, cid, tid)
+    ck = torch.empty((T * NC * H, D, D), dtype=torch.float32, device=device)
+    gc = g(_T_G_CKPT)
+    for r0 in range(0, ck.shape[0], 256):
+        r1 = min(ck.shape[0], r0 + 256)
+        ck[r0:r1] = cfg.state_sd * torch.randn((r1 - r0, D, D), generator=gc, device=device, dtype=torch.float32)
+    out = {
+        "ckpt": ck.view(T, NC, H, D, D),
+        "trunk_k": _unit_rows((T * L, H, D), dt, device, g(_T_G_TK), 8192).view(T, L, H, D),
+        "trunk_v": _normal((T * L, H, D), dt, device, g(_T_G_TV), 8192).view(T, L, H, D),
+        "trunk_gate": _uniform((T, L, H), cfg.gate_lo, 1.0, device, g(_T_G_TA)),
+        "trunk_beta": _uniform((T, L, H), 0.05, 0.95, device, g(_T_G_TB)),
+        "q": _normal((T, B, Wn, H, D), dt, device, g(_T_G_Q)),
+        "k": _unit_rows((T, B, Wn, H, D), dt, device, g(_T_G_K)),
+        "v": _normal((T, B, Wn, H, D), dt, device, g(_T_G_V)),
+        "gate": _uniform((T, B, Wn, H), cfg.gate_lo, 1.0, device, g(_T_G_A)),
+        "beta": _uniform((T, B, Wn, H), 0.05, 0.95, device, g(_T_G_B)),
+    }
+    anch = anchors_for(cfg, seed, cid)
+    parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()
+    out["anchors"] = torch.from_numpy(anch).to(device)
+    out["parent"] = torch.from_numpy(parent).to(device)
+    return out
