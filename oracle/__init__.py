@@ -29,13 +29,15 @@ from .e2etv import (logsumexp, log_softmax, overlap, prefix_products, suffix_sum
                     e2etv, e2etv_branch)
 from .rows import score_row_source, new_score_rows, shared_row_count
 from .prefill import trunk_prefill, trunk_prefill_cache
+from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, replay_span,
+                  anchor_state, gdn_branch, gdn_replay, update_counts)
 
 __all__ = [
     "rope", "rope_angles", "walk_ancestors", "tree_depths", "check_positions",
     "branch_mask", "packed_tree_mask", "tree_attention_branch", "tree_attention",
     "tree_attention_packed", "logsumexp", "log_softmax", "overlap", "prefix_products",
     "suffix_sums", "e2etv", "e2etv_branch", "score_row_source", "new_score_rows",
-    "shared_row_count", "trunk_prefill", "trunk_prefill_cache",
+    "shared_row_count", "trunk_prefill", "trunk_prefill_cache", "gated_delta_update",
+    "gdn_read", "run_tokens", "trunk_checkpoints", "replay_span", "anchor_state", "gdn_branch",
+    "gdn_replay", "update_counts",
 ]
-from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, replay_span,
-                  anchor_state, gdn_branch, gdn_replay, update_counts)
