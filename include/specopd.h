@@ -14,6 +14,9 @@
  *                           §3.2, Eq. 18; rustineverything.app summary, §2.3).
  *   specopd_prefill_fwd     the causal pass over each trunk that fills that
  *                           cache (jaehun.me review, §3.1 step 1, §3.2(a)).
+ *   specopd_gdn_replay_fwd  branch scoring for a linear-attention (GDN)
+ *                           target by indexed state replay from trunk
+ *                           checkpoints (jaehun.me review, §3.2(c), Fig. 5).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -221,6 +224,77 @@ specopd_status specopd_prefill_fwd(const specopd_prefill_desc* desc, const void*
                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Linear-attention (GDN) branch scoring by indexed state replay             */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Problem sizes: T trunks of length L, B branches per trunk (one anchor
+ * each), Wn nodes per branch (1 <= Wn <= 64), H heads with key and value
+ * size D in {64, 128}, a checkpoint after every C trunk tokens
+ * (1 <= C <= 64; the pages use 64), so L / C checkpoints per trunk and head.
+ * T * L must stay below 2^28.
+ */
+typedef struct {
+  int32_t T, L, B, Wn, H, D, C;
+  specopd_dtype dtype; /* of trunk_k, trunk_v, q, k, v; everything else fp32 */
+  uint32_t flags;      /* reserved, must be 0                                  */
+} specopd_gdn_desc;
+
+/* Workspace bytes (a malformed-branch counter). */
+specopd_status specopd_gdn_workspace_size(const specopd_gdn_desc* desc, size_t* bytes);
+
+/*
+ * A linear-attention target cannot rewind its recurrent state to an anchor
+ * with a mask, so the trunk pass keeps immutable fp32 checkpoints of the
+ * state every C tokens; each branch copies the last checkpoint at or before
+ * its anchor, replays the trunk tokens after it up to the anchor, then runs
+ * its own tokens on that private copy (jaehun.me review, §3.2(c), Fig. 5).
+ * The recurrence, per head, is the gated delta rule as published for Gated
+ * DeltaNet (the pages name GDN without stating it):
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ * with S of [D (value)][D (key)] and keys expected to be unit length.
+ * A branch node's state is its parent's (the anchor state for a root)
+ * updated with the node's token; its output reads that state with its query.
+ *
+ *   ckpt        [T][L/C][H][D][D] fp32  checkpoint m: the state after trunk
+ *                                       tokens 0..(m+1)C-1 (rows = value
+ *                                       dims); may be NULL when L < C
+ *   trunk_k, trunk_v  [T][L][H][D]      trunk keys and values
+ *   trunk_gate, trunk_beta  [T][L][H]   fp32 decay gate alpha and write
+ *                                       strength beta of each trunk token
+ *   anchors     [T][B] int32            anchor a: the branch follows trunk
+ *                                       tokens 0..a
+ *   parent      [T][B][Wn] int32        -1 = attached to the anchor, else an
+ *                                       earlier node of the same branch
+ *   q, k, v     [T][B][Wn][H][D]        branch node queries, keys, values
+ *   gate, beta  [T][B][Wn][H] fp32      branch node alpha and beta
+ *   out         [T][B][Wn][H][D] fp32   out: every node's output
+ *   workspace / workspace_bytes         specopd_gdn_workspace_size bytes,
+ *                                       16-byte aligned
+ *
+ * The state is replayed in fp32 (the checkpoints' precision); inputs are
+ * converted to fp32 on load.  A branch whose anchor is outside [0, L) or
+ * whose parent map has a node not preceded by its parent gets NaN outputs
+ * and is counted (specopd_gdn_device_status).  All pointers 16-byte
+ * aligned; out must not alias an input.
+ */
+specopd_status specopd_gdn_replay_fwd(const specopd_gdn_desc* desc, const float* ckpt,
+                                      const void* trunk_k, const void* trunk_v,
+                                      const float* trunk_gate, const float* trunk_beta,
+                                      const int32_t* anchors, const int32_t* parent, const void* q,
+                                      const void* k, const void* v, const float* gate,
+                                      const float* beta, float* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* Synchronises `stream`; reports how many branches the last
+ * specopd_gdn_replay_fwd on this workspace found malformed (returning
+ * SPECOPD_ERR_DEVICE_VALIDATION if any).  `bad_branches` may be NULL. */
+specopd_status specopd_gdn_device_status(const specopd_gdn_desc* desc, const void* workspace,
+                                         size_t workspace_bytes, int32_t* bad_branches,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* E2E-TV surrogate                                                          */
 /* ------------------------------------------------------------------------ */
 
@@ -342,17 +416,18 @@ specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
 /* Kernel timing, for measurement harnesses.
  *
  * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd,
- * specopd_e2etv_fwd_bwd and specopd_prefill_fwd call record a pair of HIP
- * events on its stream around each launch of its main kernel (the attention
- * kernel proper, after the preparation kernel; the E2E-TV kernel, without
- * the small kernel that clears its counters; the attention kernel of each
- * prefilled trunk), so that a harness can divide a kernel's algorithmic work
+ * specopd_e2etv_fwd_bwd, specopd_prefill_fwd and specopd_gdn_replay_fwd call
+ * record a pair of HIP events on its stream around each launch of its main
+ * kernel (the attention kernel proper, after the preparation kernel; the
+ * E2E-TV kernel, without the small kernel that clears its counters; the
+ * attention kernel of each prefilled trunk; the GDN replay kernel, without
+ * the one that clears its counter), so that a harness can divide a kernel's algorithmic work
  * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is
  * created when timing is switched on and kept for the process).
  *
  * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
- * 1 E2E-TV, 2 prefill.  Waits for the recorded events and returns the summed elapsed
+ * 1 E2E-TV, 2 prefill, 3 GDN replay.  Waits for the recorded events and returns the summed elapsed
  * milliseconds and the number of recorded launches.  Returns
  * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
  * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while

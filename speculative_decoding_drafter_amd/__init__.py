@@ -13,4 +13,6 @@ from ._lib import (  # noqa: F401
     specopd_e2etv_device_status, specopd_e2etv_fwd_bwd_noalloc, E2ETV_NOALLOC_SCRATCH_BYTES,
     specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn, specopd_score_rows, score_rows,
     e2etv, PrefillDesc, prefill_desc, specopd_prefill_workspace_size, specopd_prefill_fwd, prefill,
+    GdnDesc, gdn_desc, specopd_gdn_workspace_size, specopd_gdn_replay_fwd, specopd_gdn_device_status,
+    gdn_replay,
 )

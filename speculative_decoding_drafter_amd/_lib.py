@@ -37,6 +37,7 @@ EXPORTS = (
     "specopd_e2etv_workspace_size", "specopd_e2etv_fwd_bwd", "specopd_e2etv_device_status",
     "specopd_e2etv_fwd_bwd_noalloc",
     "specopd_prefill_workspace_size", "specopd_prefill_fwd",
+    "specopd_gdn_workspace_size", "specopd_gdn_replay_fwd", "specopd_gdn_device_status",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
@@ -57,6 +58,11 @@ class E2etvDesc(ctypes.Structure):
 class PrefillDesc(ctypes.Structure):
     _fields_ = [("T", c_int32), ("L", c_int32), ("Hq", c_int32), ("Hkv", c_int32), ("D", c_int32),
                 ("dtype", c_int), ("rope_base", c_float), ("scale", c_float), ("flags", c_uint32)]
+
+
+class GdnDesc(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("L", c_int32), ("B", c_int32), ("Wn", c_int32), ("H", c_int32),
+                ("D", c_int32), ("C", c_int32), ("dtype", c_int), ("flags", c_uint32)]
 
 
 class SpecopdError(RuntimeError):
@@ -83,6 +89,9 @@ def _load():
                                                 POINTER(c_int32), POINTER(c_int32), P]
     lib.specopd_prefill_workspace_size.argtypes = [POINTER(PrefillDesc), POINTER(c_size_t)]
     lib.specopd_prefill_fwd.argtypes = [POINTER(PrefillDesc)] + [P] * 6 + [P, c_size_t, P]
+    lib.specopd_gdn_workspace_size.argtypes = [POINTER(GdnDesc), POINTER(c_size_t)]
+    lib.specopd_gdn_replay_fwd.argtypes = [POINTER(GdnDesc)] + [P] * 13 + [P, c_size_t, P]
+    lib.specopd_gdn_device_status.argtypes = [POINTER(GdnDesc), P, c_size_t, POINTER(c_int32), P]
     lib.specopd_kernel_timing.argtypes = [c_int]
     lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
@@ -263,6 +272,60 @@ def specopd_e2etv_device_status(desc, workspace, stream=None, with_deferred=Fals
 
 
 # ------------------------------------------------------------------ helpers
+
+
+def gdn_desc(T, L, B, Wn, H, D, C, dtype, flags=0):
+    return GdnDesc(T, L, B, Wn, H, D, C, _DT.get(dtype, dtype) if not isinstance(dtype, int) else dtype, flags)
+
+
+def specopd_gdn_workspace_size(desc: GdnDesc) -> int:
+    n = c_size_t(0)
+    st = LIB.specopd_gdn_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_gdn_workspace_size")
+    return n.value
+
+
+def specopd_gdn_replay_fwd(desc, ckpt, trunk_k, trunk_v, trunk_gate, trunk_beta, anchors, parent, q, k, v,
+                           gate, beta, out, workspace, stream=None, raw_status=False):
+    st = LIB.specopd_gdn_replay_fwd(
+        ctypes.byref(desc), _ptr(ckpt), _ptr(trunk_k), _ptr(trunk_v), _ptr(trunk_gate), _ptr(trunk_beta),
+        _ptr(anchors), _ptr(parent), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(out),
+        _ptr(workspace),
+        c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+        _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_gdn_replay_fwd")
+    return out
+
+
+def specopd_gdn_device_status(desc, workspace, stream=None) -> int:
+    bad = c_int32(0)
+    st = LIB.specopd_gdn_device_status(ctypes.byref(desc), _ptr(workspace),
+                                       c_size_t(workspace.numel() * workspace.element_size()),
+                                       ctypes.byref(bad), _stream(stream))
+    if st not in (SPECOPD_OK, SPECOPD_ERR_DEVICE_VALIDATION):
+        raise SpecopdError(st, "specopd_gdn_device_status")
+    return bad.value
+
+
+def gdn_replay(inp: dict, C=64, ws=None, out=None):
+    """GDN branch replay on generated inputs (dict of device tensors);
+    returns (out [T][B][Wn][H][D] fp32, desc, ws)."""
+    q = inp["q"]
+    T, B, Wn, H, D = q.shape
+    L = inp["trunk_k"].shape[1]
+    desc = gdn_desc(T, L, B, Wn, H, D, C, q.dtype)
+    if ws is None:
+        ws = workspace(specopd_gdn_workspace_size(desc), q.device)
+    if out is None:
+        out = torch.empty((T, B, Wn, H, D), dtype=torch.float32, device=q.device)
+    specopd_gdn_replay_fwd(desc, inp["ckpt"] if L // C > 0 else None, inp["trunk_k"], inp["trunk_v"],
+                           inp["trunk_gate"], inp["trunk_beta"], inp["anchors"], inp["parent"], q, inp["k"],
+                           inp["v"], inp["gate"], inp["beta"], out, ws)
+    return out, desc, ws
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

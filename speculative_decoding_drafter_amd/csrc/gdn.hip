@@ -1,0 +1,342 @@
+// Linear-attention (GDN) branch scoring by indexed state replay (gfx950).
+//
+// What is computed (jaehun.me review of SpecOPD, §3.2(c) and Fig. 5): a
+// linear-attention target keeps one recurrent state per head, which a mask
+// cannot rewind to an anchor.  The trunk pass stores the state as immutable
+// fp32 checkpoints every C trunk tokens; a branch restores its anchor's state
+// by copying the nearest checkpoint at or before the anchor into private
+// registers and replaying only the trunk tokens after it, then updates and
+// reads that copy with its own tokens.  The recurrence is the gated delta
+// rule as published for Gated DeltaNet (the pages name GDN without stating
+// it): per head, with a state S of [Dv][Dk] and unit keys,
+//     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+//         = alpha_t S_{t-1} + u_t k_t^T,  u_t = beta_t (v_t - alpha_t S_{t-1} k_t),
+//     o_t = S_t q_t.
+// A branch node's state is its parent's state (the anchor's for a root)
+// updated with the node's own token.
+//
+// One workgroup per (trunk, branch, head).  The D x D state lives in
+// registers: lane l of wave w holds row 64 (w mod D/64) + l, columns
+// [D/2 * (w div D/64), + D/2), as S / g with one running scale g for the
+// whole state, so a token's decay costs one scalar multiply and its update
+// one fused multiply-add per element.  The token's key, query and the next
+// token's key are the same for every lane of a wave, so they are read into
+// scalar registers and used as the scalar operand of the vector FMAs; a
+// token's value is one element per lane.  Per token each lane forms its
+// partial S k (for the next token) and S q (its output) over its columns
+// while it updates them; the two column halves of a row exchange partials
+// through LDS, one barrier per token.
+//
+// The order of work is a list built by one thread from the parent map:
+// replay the trunk suffix, then the nodes in index order; a node whose
+// parent is not the node just processed starts again from the checkpoint
+// and replays the trunk suffix and the path down to its parent (no
+// outputs), so no state copy is ever stored.  Malformed branches (anchor
+// outside the trunk, a parent that does not precede its node) get NaN
+// outputs and are counted in the workspace.
+#include "device_common.h"
+#include "internal.h"
+
+namespace specopd {
+
+namespace {
+
+// Work-list entries (16 bits): the offset of a trunk token from the first
+// token after the checkpoint, or kNode | j for branch node j; kRestore when
+// the checkpoint is reloaded first, and kMarker (with kRestore) to reload it
+// when no trunk token follows the checkpoint.
+constexpr int kNode = 1 << 8;
+constexpr int kRestore = 1 << 9;
+constexpr int kMarker = 1 << 10;
+constexpr int kChunk = 8;  // columns per uniform load
+
+// Loads through the constant address space: the inputs are never written
+// while the kernel runs, and a uniform load from there becomes a scalar load
+// (a plain global pointer would be read by vector loads, since the kernel
+// also stores to global memory).
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* cptr(const void* p) {
+  return (const __attribute__((address_space(4))) T*)(p);
+}
+
+template <typename IN>
+struct In8;
+template <>
+struct In8<uint16_t> {
+  // eight consecutive bf16 values of a uniform row, as fp32
+  static __device__ __forceinline__ void get(const uint16_t* __restrict__ p, float (&x)[kChunk]) {
+    const u32x4 w = *cptr<u32x4>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_lo(w[i]);
+      x[2 * i + 1] = bf16_hi(w[i]);
+    }
+  }
+  static __device__ __forceinline__ float one(const uint16_t* __restrict__ p) { return bf16_to_f32(*p); }
+};
+template <>
+struct In8<float> {
+  static __device__ __forceinline__ void get(const float* __restrict__ p, float (&x)[kChunk]) {
+    const f32x4 a = *cptr<f32x4>(p);
+    const f32x4 b = *cptr<f32x4>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+  static __device__ __forceinline__ float one(const float* __restrict__ p) { return *p; }
+};
+
+struct GdnArgs {
+  const float* __restrict__ ckpt;
+  const void *trunk_k, *trunk_v, *q, *k, *v;
+  const float *trunk_gate, *trunk_beta, *gate, *beta;
+  const int32_t *anchors, *parent;
+  float* out;
+  int32_t* bad;
+  int T, L, B, Wn, H, C, NC;
+};
+
+// The longest work list: with C <= 64 (host check), at most Wn restarts of
+// one checkpoint, C - 1 trunk tokens and a path of Wn - 1 nodes, plus Wn nodes.
+constexpr int kMaxList = 64 * (1 + 63 + 63) + 64;
+
+template <int D, typename IN>
+__global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a) {
+  constexpr int NCOL = D / 2;  // columns per lane
+  constexpr int RB = D / 64;   // 64-row blocks
+  constexpr int NCH = NCOL / kChunk;
+  __shared__ uint16_t s_list[kMaxList];
+  __shared__ int s_par[64];
+  __shared__ int s_n;
+  __shared__ float s_x[2][2][2][64 * RB];  // [buffer][column half][S k, S q][row]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = wave / RB, r = (wave % RB) * 64 + lane;
+  const int c0 = half * NCOL;
+  const int h = blockIdx.x % a.H;
+  const int tb = blockIdx.x / a.H;  // trunk * B + branch
+  const int t = tb / a.B;
+  const int Wn = a.Wn;
+  const int anc = a.anchors[tb];
+  const IN* const tk = static_cast<const IN*>(a.trunk_k);
+  const IN* const tv = static_cast<const IN*>(a.trunk_v);
+  const IN* const bq = static_cast<const IN*>(a.q);
+  const IN* const bk = static_cast<const IN*>(a.k);
+  const IN* const bv = static_cast<const IN*>(a.v);
+
+  // ---- the work list (one thread, from the parent map staged in LDS)
+  if (tid < Wn) s_par[tid] = a.parent[size_t(tb) * Wn + tid];
+  __syncthreads();
+  if (tid == 0) {
+    bool ok = anc >= 0 && anc < a.L;
+    for (int j = 0; j < Wn && ok; ++j) ok = s_par[j] >= -1 && s_par[j] < j;
+    int n = -1;
+    if (ok) {
+      const int t0 = (anc + 1) / a.C * a.C;  // first trunk token after the checkpoint
+      n = 0;
+      int cur = -2;                          // state held: -1 the anchor's, j node j's
+      for (int j = 0; j < Wn; ++j) {
+        const int p = s_par[j];
+        if (p != cur) {
+          // checkpoint, trunk suffix, then the path from the root down to p
+          s_list[n++] = uint16_t(kRestore | (t0 <= anc ? 0 : kMarker));
+          for (int x = 1; t0 + x <= anc; ++x) s_list[n++] = uint16_t(x);
+          int depth = 0;
+          for (int x = p; x >= 0; x = s_par[x]) ++depth;
+          for (int d = depth - 1; d >= 0; --d) {
+            int x = p;
+            for (int k = 0; k < d; ++k) x = s_par[x];
+            s_list[n++] = uint16_t(kNode | x);
+          }
+        }
+        s_list[n++] = uint16_t(kNode | j);
+        cur = j;
+      }
+    }
+    s_n = n;
+    if (!ok && h == 0) atomicAdd(a.bad, 1);
+  }
+  __syncthreads();
+  const int n = s_n;
+  float* const orow0 = a.out + size_t(tb) * Wn * a.H * D;
+  if (n < 0) {
+    if (half == 0)
+      for (int j = 0; j < Wn; ++j) orow0[(size_t(j) * a.H + h) * D + r] = __builtin_nanf("");
+    return;
+  }
+
+  // token e: e >= 0 trunk token e, e < 0 branch node -1-e
+  const int t0 = (anc + 1) / a.C * a.C;
+  auto decode = [&](int x) -> int { return (x & kNode) ? -1 - (x & (kNode - 1)) : t0 + (x & (kNode - 1)); };
+  auto krow = [&](int e) -> const IN* {
+    return e >= 0 ? tk + ((size_t(t) * a.L + e) * a.H + h) * D
+                  : bk + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D;
+  };
+  auto vval = [&](int e) -> float {
+    return In8<IN>::one((e >= 0 ? tv + ((size_t(t) * a.L + e) * a.H + h) * D
+                                : bv + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D) + r);
+  };
+  auto gate = [&](int e) -> float {
+    return e >= 0 ? cptr<float>(a.trunk_gate)[(size_t(t) * a.L + e) * a.H + h]
+                  : cptr<float>(a.gate)[(size_t(tb) * Wn + (-1 - e)) * a.H + h];
+  };
+  auto strength = [&](int e) -> float {
+    return e >= 0 ? cptr<float>(a.trunk_beta)[(size_t(t) * a.L + e) * a.H + h]
+                  : cptr<float>(a.beta)[(size_t(tb) * Wn + (-1 - e)) * a.H + h];
+  };
+  auto entry = [&](int i) -> int { return __builtin_amdgcn_readfirstlane(int(s_list[i])); };
+
+  float St[NCOL];
+  float g = 1.f;  // the state is g * St
+  int buf = 0;
+  // sums of the two column halves' partials of this lane's row
+  auto exchange = [&](float y, float o) -> float2 {
+    s_x[buf][half][0][r] = y;
+    s_x[buf][half][1][r] = o;
+    __syncthreads();
+    const float y2 = s_x[buf][half ^ 1][0][r], o2 = s_x[buf][half ^ 1][1][r];
+    buf ^= 1;
+    return make_float2(y + y2, o + o2);
+  };
+  // the checkpoint at or before the anchor (the zero state if none)
+  auto restore = [&]() {
+    const int c = (anc + 1) / a.C - 1;
+    if (c >= 0) {
+      const float* src = a.ckpt + ((size_t(t) * a.NC + c) * a.H + h) * size_t(D) * D + size_t(r) * D + c0;
+#pragma unroll
+      for (int i = 0; i < NCOL; i += 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
+        St[i] = x[0];
+        St[i + 1] = x[1];
+        St[i + 2] = x[2];
+        St[i + 3] = x[3];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCOL; ++i) St[i] = 0.f;
+    }
+    g = 1.f;
+  };
+  // this lane's part of S k for key row kr
+  auto dot_k = [&](const IN* kr) -> float {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      float x[kChunk];
+      In8<IN>::get(kr + c0 + ch * kChunk, x);
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) acc[i & 3] = __builtin_fmaf(St[ch * kChunk + i], x[i], acc[i & 3]);
+    }
+    return g * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  };
+
+  // the token about to be processed: e, its gate, strength, value element and
+  // y = S_{t-1} k_t (whole row)
+  int e = 0;
+  float al = 1.f, be = 0.f, vr = 0.f, y = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const int ent = entry(i);
+    if (ent & kRestore) {
+      restore();
+      int x = ent & ~kRestore;
+      if (x & kMarker) x = entry(++i);  // no trunk token to replay: the next entry follows directly
+      e = decode(x);
+      y = exchange(dot_k(krow(e)), 0.f).x;
+      al = gate(e);
+      be = strength(e);
+      vr = vval(e);
+    }
+    // S_t = alpha S_{t-1} + u k^T, u = beta (v - alpha y); as g St with
+    // g <- alpha g and St += (u / g) k, the scale folded into St when small
+    const float u = be * (vr - al * y);
+    float gn = al * g;
+    float w;
+    if (gn < 0x1p-30f) {
+#pragma unroll
+      for (int c = 0; c < NCOL; ++c) St[c] *= gn;
+      gn = 1.f;
+      w = u;
+    } else {
+      w = u / gn;
+    }
+    g = gn;
+    // the next entry, when it continues from this state
+    const bool more = i + 1 < n && !(entry(i + 1) & kRestore);
+    const int en = more ? decode(entry(i + 1)) : e;
+    float aln = 1.f, ben = 0.f, vrn = 0.f;
+    if (more) {
+      aln = gate(en);
+      ben = strength(en);
+      vrn = vval(en);
+    }
+    const bool outp = e < 0;
+    const IN* const kr = krow(e);
+    const IN* const kn = krow(en);
+    const IN* const qr = outp ? bq + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D : kr;
+    float ay[4] = {0.f, 0.f, 0.f, 0.f}, ao[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      float xk[kChunk], xn[kChunk], xq[kChunk];
+      In8<IN>::get(kr + c0 + ch * kChunk, xk);
+      In8<IN>::get(kn + c0 + ch * kChunk, xn);
+      In8<IN>::get(qr + c0 + ch * kChunk, xq);
+#pragma unroll
+      for (int c = 0; c < kChunk; ++c) {
+        const int cc = ch * kChunk + c;
+        St[cc] = __builtin_fmaf(w, xk[c], St[cc]);
+        ay[c & 3] = __builtin_fmaf(St[cc], xn[c], ay[c & 3]);
+        ao[c & 3] = __builtin_fmaf(St[cc], xq[c], ao[c & 3]);
+      }
+    }
+    const float2 s = exchange(g * ((ay[0] + ay[1]) + (ay[2] + ay[3])), g * ((ao[0] + ao[1]) + (ao[2] + ao[3])));
+    if (outp && half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = s.y;
+    y = s.x;
+    e = en;
+    al = aln;
+    be = ben;
+    vr = vrn;
+  }
+}
+
+__global__ void gdn_zero_kernel(int32_t* __restrict__ bad) {
+  if (threadIdx.x == 0) *bad = 0;
+}
+
+}  // namespace
+
+hipError_t launch_gdn_replay(const specopd_gdn_desc& d, const GdnCallArgs& c, hipStream_t s) {
+  GdnArgs a{};
+  a.ckpt = c.ckpt;
+  a.trunk_k = c.trunk_k;
+  a.trunk_v = c.trunk_v;
+  a.q = c.q;
+  a.k = c.k;
+  a.v = c.v;
+  a.trunk_gate = c.trunk_gate;
+  a.trunk_beta = c.trunk_beta;
+  a.gate = c.gate;
+  a.beta = c.beta;
+  a.anchors = c.anchors;
+  a.parent = c.parent;
+  a.out = c.out;
+  a.bad = reinterpret_cast<int32_t*>(c.ws);
+  a.T = d.T; a.L = d.L; a.B = d.B; a.Wn = d.Wn; a.H = d.H; a.C = d.C; a.NC = d.L / d.C;
+  gdn_zero_kernel<<<1, 64, 0, s>>>(a.bad);
+  const dim3 grid(unsigned(size_t(d.T) * d.B * d.H));
+  timing_mark(3, 0, s);
+  const bool bf = d.dtype == SPECOPD_BF16;
+  if (d.D == 128) {
+    if (bf) gdn_replay_kernel<128, uint16_t><<<grid, 256, 0, s>>>(a);
+    else gdn_replay_kernel<128, float><<<grid, 256, 0, s>>>(a);
+  } else {
+    if (bf) gdn_replay_kernel<64, uint16_t><<<grid, 128, 0, s>>>(a);
+    else gdn_replay_kernel<64, float><<<grid, 128, 0, s>>>(a);
+  }
+  timing_mark(3, 1, s);
+  return hipGetLastError();
+}
+
+}  // namespace specopd

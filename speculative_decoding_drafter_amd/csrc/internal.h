@@ -184,10 +184,25 @@ hipError_t launch_e2etv(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStre
 constexpr size_t kE2etvScratchBytes = SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES;
 hipError_t e2etv_scratch(void** ptr);
 
+// ---------------------------------------------------------------- GDN replay
+// Workspace: one int32, the count of malformed branches of the last call.
+constexpr size_t kGdnWsBytes = 256;
+struct GdnCallArgs {
+  const float* ckpt;
+  const void *trunk_k, *trunk_v;
+  const float *trunk_gate, *trunk_beta;
+  const int32_t *anchors, *parent;
+  const void *q, *k, *v;
+  const float *gate, *beta;
+  float* out;
+  char* ws;
+};
+hipError_t launch_gdn_replay(const specopd_gdn_desc& d, const GdnCallArgs& a, hipStream_t s);
+
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`
-// (0 attention, 1 E2E-TV, 2 prefill) when timing is on; otherwise does
-// nothing (also for a negative `which`).
+// (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay) when timing is on;
+// otherwise does nothing (also for a negative `which`).
 void timing_mark(int which, int phase, hipStream_t s);
 
 }  // namespace specopd

@@ -38,6 +38,21 @@ specopd_status check_tree_desc(const specopd_tree_attn_desc* d) {
   return SPECOPD_OK;
 }
 
+specopd_status check_gdn_desc(const specopd_gdn_desc* d) {
+  if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->T < 1 || d->L < 1 || d->B < 1 || d->Wn < 1 || d->H < 1 || d->C < 1 || d->D < 1)
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->dtype != SPECOPD_F32 && d->dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->D != 64 && d->D != 128) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->Wn > 64 || d->C > 64) return SPECOPD_ERR_UNSUPPORTED;  // the work list's bound
+  // grid and element offsets
+  if (double(d->T) * d->B * d->H > 2147483647.0 || double(d->T) * d->L >= double(1 << 28) ||
+      double(d->T) * d->L * d->H * d->D > 9.0e15 || double(d->T) * d->B * d->Wn * d->H * d->D > 9.0e15)
+    return SPECOPD_ERR_UNSUPPORTED;
+  return SPECOPD_OK;
+}
+
 specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
   if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->T < 1 || d->L < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
@@ -95,7 +110,7 @@ struct TimingState {
   std::mutex mu;
   bool on = false;
   bool failed = false;
-  std::vector<hipEvent_t> ev[3];  // per call kind: start, stop, start, stop, ...
+  std::vector<hipEvent_t> ev[4];  // per call kind: start, stop, start, stop, ...
   std::vector<hipEvent_t> pool;   // created up front, so recording costs no allocation
   void clear() {
     for (auto& v : ev) {
@@ -116,7 +131,7 @@ namespace specopd {
 void timing_mark(int which, int phase, hipStream_t s) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on || which < 0 || which > 2) return;
+  if (!t.on || which < 0 || which > 3) return;
   auto& v = t.ev[which];
   if (phase == 1 && v.size() % 2 == 0) return;  // no open start
   if (phase == 0 && v.size() % 2 == 1) return;  // already open
@@ -169,7 +184,7 @@ specopd_status specopd_kernel_timing(int enable) {
 }
 
 specopd_status specopd_kernel_time(int which, double* total_ms, int* launches) {
-  if (which < 0 || which > 2 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (which < 0 || which > 3 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   if (t.failed) return SPECOPD_ERR_HIP;
@@ -258,6 +273,61 @@ specopd_status specopd_prefill_fwd(const specopd_prefill_desc* desc, const void*
   a.scale = desc->scale > 0.f ? desc->scale : float(1.0 / sqrt(double(desc->D)));
   hipError_t e = launch_prefill(*desc, a, stream);
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_gdn_workspace_size(const specopd_gdn_desc* desc, size_t* bytes) {
+  specopd_status st = check_gdn_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!bytes) return SPECOPD_ERR_INVALID_ARGUMENT;
+  *bytes = kGdnWsBytes;
+  return SPECOPD_OK;
+}
+
+specopd_status specopd_gdn_replay_fwd(const specopd_gdn_desc* desc, const float* ckpt,
+                                      const void* trunk_k, const void* trunk_v,
+                                      const float* trunk_gate, const float* trunk_beta,
+                                      const int32_t* anchors, const int32_t* parent, const void* q,
+                                      const void* k, const void* v, const float* gate,
+                                      const float* beta, float* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  specopd_status st = check_gdn_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const bool need_ckpt = desc->L / desc->C > 0;
+  const void* ptrs[] = {trunk_k, trunk_v, trunk_gate, trunk_beta, anchors, parent, q, k, v, gate, beta, out};
+  for (const void* p : ptrs)
+    if (!p) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (need_ckpt && !ckpt) return SPECOPD_ERR_INVALID_ARGUMENT;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (need_ckpt && !aligned16(ckpt)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  const void* ins[] = {ckpt, trunk_k, trunk_v, trunk_gate, trunk_beta, anchors, parent, q, k, v, gate, beta};
+  for (const void* p : ins)
+    if (p == out) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!workspace || workspace_bytes < kGdnWsBytes || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  GdnCallArgs a{};
+  a.ckpt = ckpt;
+  a.trunk_k = trunk_k; a.trunk_v = trunk_v;
+  a.trunk_gate = trunk_gate; a.trunk_beta = trunk_beta;
+  a.anchors = anchors; a.parent = parent;
+  a.q = q; a.k = k; a.v = v;
+  a.gate = gate; a.beta = beta;
+  a.out = out;
+  a.ws = static_cast<char*>(workspace);
+  hipError_t e = launch_gdn_replay(*desc, a, stream);
+  return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_gdn_device_status(const specopd_gdn_desc* desc, const void* workspace,
+                                         size_t workspace_bytes, int32_t* bad_branches,
+                                         hipStream_t stream) {
+  specopd_status st = check_gdn_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!workspace || workspace_bytes < kGdnWsBytes || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  int32_t bad = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SPECOPD_ERR_HIP;
+  if (hipMemcpy(&bad, workspace, sizeof(bad), hipMemcpyDeviceToHost) != hipSuccess) return SPECOPD_ERR_HIP;
+  if (bad_branches) *bad_branches = bad;
+  return bad != 0 ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
 }
 
 specopd_status specopd_score_rows(const specopd_tree_attn_desc* desc, const int32_t* anchors,

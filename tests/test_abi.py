@@ -290,3 +290,60 @@ def test_noalloc_rejects_host_errors_before_the_gpu():
     assert call(_edesc(), draft=0) == sd.SPECOPD_ERR_INVALID_ARGUMENT
     assert call(_edesc(), grad=FAKE) == sd.SPECOPD_ERR_INVALID_ARGUMENT  # grad aliases draft
     assert call(_edesc(Wn=65)) == sd.SPECOPD_ERR_UNSUPPORTED
+
+
+def _gdesc(**kw):
+    base = dict(T=2, L=300, B=4, Wn=7, H=4, D=128, C=64, dtype=sd.SPECOPD_BF16)
+    base.update(kw)
+    return sd.gdn_desc(**base)
+
+
+def _gcall(desc, ws_bytes=256, **over):
+    names = ("ckpt", "trunk_k", "trunk_v", "trunk_gate", "trunk_beta", "anchors", "parent", "q", "k",
+             "v", "gate", "beta", "out", "ws")
+    args = {n: FAKE + 16 * i for i, n in enumerate(names)}
+    args.update(over)
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_gdn_replay_fwd(
+        ctypes.byref(desc), *[P(args[n]) for n in names[:-1]], P(args["ws"]), ctypes.c_size_t(ws_bytes),
+        P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 256, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("D", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("C", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("C", 65, sd.SPECOPD_ERR_UNSUPPORTED),       # longer replays than the work list holds
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("Wn", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("H", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("dtype", 5, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 300_000_000, sd.SPECOPD_ERR_UNSUPPORTED),  # T * L beyond 2^28 tokens
+])
+def test_gdn_desc_errors(field, value, code):
+    d = _gdesc()
+    setattr(d, field, value)
+    assert _gcall(d) == code
+    n = ctypes.c_size_t(0)
+    assert sd.LIB.specopd_gdn_workspace_size(ctypes.byref(d), ctypes.byref(n)) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ckpt=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),              # L >= C: checkpoints needed
+    (dict(parent=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(gate=FAKE + 8), sd.SPECOPD_ERR_INVALID_ARGUMENT),       # misaligned
+    (dict(out=FAKE + 16), sd.SPECOPD_ERR_INVALID_ARGUMENT),       # out aliases trunk_k
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+])
+def test_gdn_pointer_errors(over, code):
+    assert _gcall(_gdesc(), **over) == code
+
+
+def test_gdn_workspace_and_short_trunks():
+    d = _gdesc()
+    need = sd.specopd_gdn_workspace_size(d)
+    assert _gcall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+    bad = ctypes.c_int32(0)
+    assert sd.LIB.specopd_gdn_device_status(ctypes.byref(d), ctypes.c_void_p(None), 0, ctypes.byref(bad),
+                                            None) == sd.SPECOPD_ERR_WORKSPACE
