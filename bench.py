@@ -19,7 +19,9 @@ with the HBM bytes and matrix-core / vector-ALU busy fractions of the
 rocprofv3 counter summaries under profiles/ while those match the kernel
 sources.  `other_workloads` repeats the measurement for the --also
 workloads.  `prefill` measures, separately, the trunk prefill that fills the
-cache (specopd_prefill_fwd) on the workload's trunks.  `cpu_baseline` times
+cache (specopd_prefill_fwd) on the workload's trunks, and `gdn` the branch
+scoring of a linear-attention (GDN) target by indexed state replay
+(specopd_gdn_replay_fwd) on the workload's trunks and tree.  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same workload, on one core and
 on every usable core (reported, not a target).
 """
@@ -87,6 +89,74 @@ def prefill_flops(cfg):
     """Algorithmic FLOPs of one trunk's causal prefill: token s reads s + 1
     keys, 4*D*Hq per (row, key)."""
     return 4.0 * cfg.D * cfg.Hq * cfg.L * (cfg.L + 1) / 2.0
+
+
+FP32_FMA_TFLOPS = 78.6         # the fp32 vector rate without packed-FP32 instructions
+
+
+def gdn_flops(cfg, anchors):
+    """Algorithmic FLOPs of a GDN replay call: per head, every replayed trunk
+    token and every branch node is one gated delta-rule update (S k and the
+    rank-1 update, 4 D^2), every node one read (S q, 2 D^2); a branch
+    replays the (a + 1) mod C trunk tokens after its checkpoint once."""
+    import numpy as np
+    rep = float(((anchors.astype(np.int64) + 1) % cfg.C).sum())
+    nodes = float(cfg.T * cfg.B * cfg.Wn)
+    D2 = float(cfg.D) * cfg.D
+    return cfg.H * (4.0 * D2 * (rep + nodes) + 2.0 * D2 * nodes)
+
+
+def bench_gdn(sd, wl, seed, steps, warmup, dev, stream):
+    """GDN branch replay (specopd_gdn_replay_fwd) for a linear-attention
+    target on the workload's trunks and tree, timed on its own: it is the
+    scoring step's counterpart for GDN layers, not part of the GQA step."""
+    import torch
+    from synthetic import gen_gdn
+    gc = wl.gdn
+    gi = gen_gdn(gc, seed, device=dev, cid=wl.cid)
+    out, desc, ws = sd.gdn_replay(gi, C=gc.C)
+
+    def call():
+        sd.gdn_replay(gi, C=gc.C, ws=ws, out=out)
+
+    for _ in range(max(1, warmup)):
+        call()
+    n = max(1, min(steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / n
+    sd.specopd_kernel_timing(True)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    tot, cnt = sd.specopd_kernel_time(3)
+    sd.specopd_kernel_timing(False)
+    if sd.specopd_gdn_device_status(desc, ws) != 0:
+        raise SystemExit("GDN replay reported malformed branches")
+    kern_ms = tot / cnt
+    fl = gdn_flops(gc, gi["anchors"].cpu().numpy())
+    tf = fl / (kern_ms / 1e3) / 1e12
+    rows = gc.T * gc.B * gc.Wn
+    res = {
+        "metric": "GDN branch rows/s (indexed state replay)", "value": rows / (call_ms / 1e3),
+        "unit": "rows/s", "calls": n, "call_ms": call_ms,
+        "config": {"T": gc.T, "L": gc.L, "B": gc.B, "Wn": gc.Wn, "H": gc.H, "D": gc.D, "C": gc.C,
+                   "dtype": gc.dtype},
+        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP32_PEAK_TFLOPS, "peak_without_packed_fp32": FP32_FMA_TFLOPS,
+                     "frac_without_packed_fp32": tf / FP32_FMA_TFLOPS, "traffic": None,
+                     "kernel": "gdn_replay_kernel (specopd_gdn_replay_fwd)", "ms": kern_ms,
+                     "alg_flops_per_launch": fl},
+    }
+    del gi, out, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_prefill(sd, wl, seed, steps, warmup, dev, stream):
@@ -425,6 +495,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the GDN branch-replay measurement")
     ap.add_argument("--eager", action="store_true",
                     help="time plain calls instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -461,6 +532,8 @@ def main():
     if wl.attn is not None and not args.no_prefill:
         res["prefill"] = bench_prefill(sd, wl, args.seed, args.steps, args.warmup, dev,
                                        torch.cuda.current_stream())
+    if wl.gdn is not None and not args.no_gdn:
+        res["gdn"] = bench_gdn(sd, wl, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
     others = {}
     for c in [int(x) for x in args.also.split(",") if x.strip()]:
         if c == args.workload:

@@ -11,11 +11,14 @@ trunk pass produced (jaehun.me review §3.2(c), Fig. 5; §3.2 consistency).
 
 Tolerance.  The kernel keeps the state in fp32 as g * St (one scale per
 head) and forms each S k and S q as a sum of D fp32 products in a fixed
-order; the oracle runs in fp64.  Each update adds at most a few units of
-fp32 rounding (2^-24) relative to the largest state row times |k| = 1, and
-a branch runs at most C - 1 + Wn updates, so with states and values of
-order one the state error stays below ~1e-5; an output reads it against a
-query of norm ~sqrt(D).  The check allows 2e-4 + 2e-4 |ref| per element."""
+order; the oracle runs in fp64.  Each update adds a few units of fp32
+rounding (2^-24 ~ 6e-8) relative to the state's row norms (order one with
+unit keys and values of order one), and a branch runs at most C - 1 + Wn
+updates (about 80), so the state's error stays near 80 * 4 * 6e-8 ~ 2e-5
+relative in the worst case and far less on average (errors of either sign);
+an output reads the state against a query of norm ~sqrt(D).  Measured: at
+most 1.6e-6 absolute against outputs up to ~10.  The check allows 2e-5 +
+2e-5 |ref| per element."""
 
 import numpy as np
 import pytest
@@ -27,8 +30,8 @@ from synthetic import FORK_PARENT, WORKLOADS, chain, gen_gdn, shrink_gdn
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-ATOL = 2e-4
-RTOL = 2e-4
+ATOL = 2e-5
+RTOL = 2e-5
 
 
 def _np(t):
