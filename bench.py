@@ -142,6 +142,8 @@ def bench_gdn(sd, wl, seed, steps, warmup, dev, stream):
     fl = gdn_flops(gc, gi["anchors"].cpu().numpy())
     tf = fl / (kern_ms / 1e3) / 1e12
     rows = gc.T * gc.B * gc.Wn
+    pg = profile_summary(f"gdn_replay_{wl.name}", GDN_SRC)
+    t_g = _counter(pg, "hbm_bytes_per_launch")
     res = {
         "metric": "GDN branch rows/s (indexed state replay)", "value": rows / (call_ms / 1e3),
         "unit": "rows/s", "calls": n, "call_ms": call_ms,
@@ -149,7 +151,10 @@ def bench_gdn(sd, wl, seed, steps, warmup, dev, stream):
                    "dtype": gc.dtype},
         "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / FP32_PEAK_TFLOPS, "peak_without_packed_fp32": FP32_FMA_TFLOPS,
-                     "frac_without_packed_fp32": tf / FP32_FMA_TFLOPS, "traffic": None,
+                     "frac_without_packed_fp32": tf / FP32_FMA_TFLOPS,
+                     "traffic": None if t_g is None else t_g / (kern_ms / 1e3) / 1e9,
+                     "traffic_unit": "GB/s", "traffic_bytes_per_launch": t_g,
+                     "valu_busy_pct": _counter(pg, "valu_busy_pct"),
                      "kernel": "gdn_replay_kernel (specopd_gdn_replay_fwd)", "ms": kern_ms,
                      "alg_flops_per_launch": fl},
     }
@@ -315,6 +320,10 @@ LOSS_SRC = ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
             "speculative_decoding_drafter_amd/csrc/device_common.h",
             "speculative_decoding_drafter_amd/csrc/internal.h",
             "speculative_decoding_drafter_amd/build.py"]
+GDN_SRC = ["speculative_decoding_drafter_amd/csrc/gdn.hip",
+           "speculative_decoding_drafter_amd/csrc/device_common.h",
+           "speculative_decoding_drafter_amd/csrc/internal.h",
+           "speculative_decoding_drafter_amd/build.py"]
 
 
 def _counter(kv, key):
