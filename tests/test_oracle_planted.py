@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import test_oracle_e2etv as te
+import test_oracle_gdn as tg
 import test_oracle_prefill as tp
 import test_oracle_tree_attention as tt
 
@@ -70,6 +71,28 @@ CASES = {
     "prefill kv head transposed": (
         "oracle.prefill", "trunk_prefill", "g = h // G", "g = h % Hkv",
         [lambda: tp.test_prefill_is_library_causal_attention(0, 37, 4, 2, 16)]),
+    "delta rule adds the old association": (
+        "oracle.gdn", "gated_delta_update", "(S - float(beta) * np.outer(Sk, k))",
+        "(S + float(beta) * np.outer(Sk, k))",
+        [tg.test_update_is_the_linear_map_on_the_flattened_state, tg.test_full_strength_write_reads_back_the_value]),
+    "gate applied after the write": (
+        "oracle.gdn", "gated_delta_update",
+        "float(alpha) * (S - float(beta) * np.outer(Sk, k)) + float(beta) * np.outer(v, k)",
+        "float(alpha) * (S - float(beta) * np.outer(Sk, k) + float(beta) * np.outer(v, k))",
+        [tg.test_update_is_the_linear_map_on_the_flattened_state, tg.test_first_token_from_zero_state]),
+    "replay starts one token late": (
+        "oracle.gdn", "replay_span", "return m - 1, m * C", "return m - 1, m * C + 1",
+        [lambda: tg.test_replayed_anchor_state_equals_the_full_history(9), tg.test_figure5_replay_spans]),
+    "checkpoint taken a token early": (
+        "oracle.gdn", "trunk_checkpoints", "if (t + 1) % C == 0:", "if (t + 2) % C == 0 and t + 2 <= L:",
+        [tg.test_checkpoints_are_states_after_every_C_tokens]),
+    "node output reads its parent's state": (
+        "oracle.gdn", "gdn_branch", "out[j, h] = gdn_read(Sj, q[j][h])", "out[j, h] = gdn_read(Sp, q[j][h])",
+        [lambda: tg.test_branch_equals_full_recomputation_of_its_history(8)]),
+    "branch nodes chained in index order": (
+        "oracle.gdn", "gdn_branch", "Sp = Sa if parent[j] < 0 else states[int(parent[j])]",
+        "Sp = Sa if j == 0 else states[j - 1]",
+        [tg.test_sibling_subtrees_do_not_see_each_other]),
     "score row of the node itself": (
         "oracle.rows", "score_row_source", 'else ("node", p)', 'else ("node", int(j))',
         [tt.test_fig3_toy_tree]),
