@@ -34,6 +34,8 @@
 // outputs), so no state copy is ever stored.  Malformed branches (anchor
 // outside the trunk, a parent that does not precede its node) get NaN
 // outputs and are counted in the workspace.
+#include <utility>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -42,51 +44,99 @@ namespace specopd {
 namespace {
 
 // Work-list entries (16 bits): the offset of a trunk token from the first
-// token after the checkpoint, or kNode | j for branch node j; kRestore when
-// the checkpoint is reloaded first, and kMarker (with kRestore) to reload it
-// when no trunk token follows the checkpoint.
+// token after the checkpoint, or kNode | j for branch node j; kRestore on the
+// first token after which the state restarts from the checkpoint.
 constexpr int kNode = 1 << 8;
 constexpr int kRestore = 1 << 9;
-constexpr int kMarker = 1 << 10;
-constexpr int kChunk = 8;  // columns per uniform load
 
-// Loads through the constant address space: the inputs are never written
-// while the kernel runs, and a uniform load from there becomes a scalar load
-// (a plain global pointer would be read by vector loads, since the kernel
-// also stores to global memory).
+// Uniform loads through the constant address space become scalar loads (a
+// plain global pointer would be read by vector loads, since the kernel also
+// stores to global memory); the inputs are never written while it runs.
 template <typename T>
 __device__ __forceinline__ const __attribute__((address_space(4))) T* cptr(const void* p) {
   return (const __attribute__((address_space(4))) T*)(p);
 }
 
-template <typename IN>
-struct In8;
+// A lane's slice of a key or query row: V consecutive elements of its half,
+// starting at column V * (lane mod 16), raw as loaded and as fp32.
+template <typename IN, int V>
+struct Slice;
 template <>
-struct In8<uint16_t> {
-  // eight consecutive bf16 values of a uniform row, as fp32
-  static __device__ __forceinline__ void get(const uint16_t* __restrict__ p, float (&x)[kChunk]) {
-    const u32x4 w = *cptr<u32x4>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16_lo(w[i]);
-      x[2 * i + 1] = bf16_hi(w[i]);
-    }
+struct Slice<uint16_t, 4> {
+  using raw = u32x2;
+  static __device__ __forceinline__ raw load(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+  static __device__ __forceinline__ void cvt(raw w, float (&x)[4]) {
+    x[0] = bf16_lo(w[0]);
+    x[1] = bf16_hi(w[0]);
+    x[2] = bf16_lo(w[1]);
+    x[3] = bf16_hi(w[1]);
   }
-  static __device__ __forceinline__ float one(const uint16_t* __restrict__ p) { return bf16_to_f32(*p); }
 };
 template <>
-struct In8<float> {
-  static __device__ __forceinline__ void get(const float* __restrict__ p, float (&x)[kChunk]) {
-    const f32x4 a = *cptr<f32x4>(p);
-    const f32x4 b = *cptr<f32x4>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = a[i];
-      x[4 + i] = b[i];
-    }
+struct Slice<uint16_t, 2> {
+  using raw = uint32_t;
+  static __device__ __forceinline__ raw load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  static __device__ __forceinline__ void cvt(raw w, float (&x)[2]) {
+    x[0] = bf16_lo(w);
+    x[1] = bf16_hi(w);
   }
-  static __device__ __forceinline__ float one(const float* __restrict__ p) { return *p; }
 };
+template <>
+struct Slice<float, 4> {
+  using raw = f32x4;
+  static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ void cvt(raw w, float (&x)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = w[i];
+  }
+};
+template <>
+struct Slice<float, 2> {
+  using raw = f32x2;
+  static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+  static __device__ __forceinline__ void cvt(raw w, float (&x)[2]) {
+    x[0] = w[0];
+    x[1] = w[1];
+  }
+};
+
+// acc += x[lane X of this lane's 16-lane row] * y: the DPP row broadcast
+// reads the slice element of column V * X + j in the FMA's own operand
+// fetch, so a row element costs no separate move.  (The compiler does not
+// fold a broadcast move into v_fmac_f32, hence the asm.)
+template <int X>
+__device__ __forceinline__ void fmac_bcast(float& acc, float x, float y) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(x), "v"(y), "n"(X));
+}
+
+// A DPP source must not be written by a VALU instruction in the two
+// preceding wait states, nor EXEC by a SALU one in the five before; the
+// broadcast operands pass through this before each pass, which orders their
+// last writes (and any EXEC write) at least five wait states ahead.
+__device__ __forceinline__ void dpp_guard(float (&a)[4], float (&b)[4], float (&c)[4]) {
+  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
+               "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
+}
+__device__ __forceinline__ void dpp_guard(float (&a)[2], float (&b)[2], float (&c)[2]) {
+  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(c[0]), "+v"(c[1]));
+}
+
+// One token's pass over a lane's NCOL columns: St += w k^T (k broadcast from
+// kr), then the partial sums of S k' (k' from kn) and S q (from q).
+template <int V, int... C>
+__device__ __forceinline__ void token_pass(float (&St)[sizeof...(C)], const float (&kr)[V], const float (&kn)[V],
+                                           const float (&q)[V], float w, float (&ay)[2], float (&ao)[2],
+                                           std::integer_sequence<int, C...>) {
+  ((fmac_bcast<C / V>(St[C], kr[C % V], w), fmac_bcast<C / V>(ay[C & 1], kn[C % V], St[C]),
+    fmac_bcast<C / V>(ao[C & 1], q[C % V], St[C])),
+   ...);
+}
+// The partial sums of S k alone (after a restore).
+template <int V, int... C>
+__device__ __forceinline__ void dot_pass(const float (&St)[sizeof...(C)], const float (&kr)[V], float (&ay)[2],
+                                         std::integer_sequence<int, C...>) {
+  (fmac_bcast<C / V>(ay[C & 1], kr[C % V], St[C]), ...);
+}
 
 struct GdnArgs {
   const float* __restrict__ ckpt;
@@ -98,15 +148,17 @@ struct GdnArgs {
   int T, L, B, Wn, H, C, NC;
 };
 
-// The longest work list: with C <= 64 (host check), at most Wn restarts of
-// one checkpoint, C - 1 trunk tokens and a path of Wn - 1 nodes, plus Wn nodes.
-constexpr int kMaxList = 64 * (1 + 63 + 63) + 64;
+// The longest work list: with C <= 64 (host check), at most Wn restarts, each
+// replaying at most C - 1 trunk tokens and a path of at most Wn - 1 nodes,
+// plus the Wn nodes themselves.
+constexpr int kMaxList = 64 * (63 + 63) + 64;
 
 template <int D, typename IN>
 __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a) {
-  constexpr int NCOL = D / 2;  // columns per lane
-  constexpr int RB = D / 64;   // 64-row blocks
-  constexpr int NCH = NCOL / kChunk;
+  constexpr int NCOL = D / 2;   // columns per lane
+  constexpr int RB = D / 64;    // 64-row blocks
+  constexpr int V = NCOL / 16;  // slice elements per lane
+  using SL = Slice<IN, V>;
   __shared__ uint16_t s_list[kMaxList];
   __shared__ int s_par[64];
   __shared__ int s_n;
@@ -115,7 +167,7 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = wave / RB, r = (wave % RB) * 64 + lane;
-  const int c0 = half * NCOL;
+  const int c0 = half * NCOL + V * (lane & 15);  // this lane's slice of a row
   const int h = blockIdx.x % a.H;
   const int tb = blockIdx.x / a.H;  // trunk * B + branch
   const int t = tb / a.B;
@@ -140,10 +192,10 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
       int cur = -2;                          // state held: -1 the anchor's, j node j's
       for (int j = 0; j < Wn; ++j) {
         const int p = s_par[j];
+        const int first = n;
         if (p != cur) {
           // checkpoint, trunk suffix, then the path from the root down to p
-          s_list[n++] = uint16_t(kRestore | (t0 <= anc ? 0 : kMarker));
-          for (int x = 1; t0 + x <= anc; ++x) s_list[n++] = uint16_t(x);
+          for (int x = 0; t0 + x <= anc; ++x) s_list[n++] = uint16_t(x);
           int depth = 0;
           for (int x = p; x >= 0; x = s_par[x]) ++depth;
           for (int d = depth - 1; d >= 0; --d) {
@@ -153,6 +205,7 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
           }
         }
         s_list[n++] = uint16_t(kNode | j);
+        if (p != cur) s_list[first] |= uint16_t(kRestore);
         cur = j;
       }
     }
@@ -170,14 +223,21 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
 
   // token e: e >= 0 trunk token e, e < 0 branch node -1-e
   const int t0 = (anc + 1) / a.C * a.C;
-  auto decode = [&](int x) -> int { return (x & kNode) ? -1 - (x & (kNode - 1)) : t0 + (x & (kNode - 1)); };
+  auto token = [&](int i) -> int {
+    const int x = __builtin_amdgcn_readfirstlane(int(s_list[i < n ? i : n - 1])) & ~kRestore;
+    return (x & kNode) ? -1 - (x & (kNode - 1)) : t0 + x;
+  };
   auto krow = [&](int e) -> const IN* {
     return e >= 0 ? tk + ((size_t(t) * a.L + e) * a.H + h) * D
                   : bk + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D;
   };
+  // a node's query row; a trunk token has none, so any valid row
+  auto qrow = [&](int e) -> const IN* {
+    return e < 0 ? bq + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D : krow(e);
+  };
   auto vval = [&](int e) -> float {
-    return In8<IN>::one((e >= 0 ? tv + ((size_t(t) * a.L + e) * a.H + h) * D
-                                : bv + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D) + r);
+    return load_f32((e >= 0 ? tv + ((size_t(t) * a.L + e) * a.H + h) * D
+                            : bv + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D) + r);
   };
   auto gate = [&](int e) -> float {
     return e >= 0 ? cptr<float>(a.trunk_gate)[(size_t(t) * a.L + e) * a.H + h]
@@ -187,7 +247,6 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
     return e >= 0 ? cptr<float>(a.trunk_beta)[(size_t(t) * a.L + e) * a.H + h]
                   : cptr<float>(a.beta)[(size_t(tb) * Wn + (-1 - e)) * a.H + h];
   };
-  auto entry = [&](int i) -> int { return __builtin_amdgcn_readfirstlane(int(s_list[i])); };
 
   float St[NCOL];
   float g = 1.f;  // the state is g * St
@@ -205,7 +264,7 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
   auto restore = [&]() {
     const int c = (anc + 1) / a.C - 1;
     if (c >= 0) {
-      const float* src = a.ckpt + ((size_t(t) * a.NC + c) * a.H + h) * size_t(D) * D + size_t(r) * D + c0;
+      const float* src = a.ckpt + ((size_t(t) * a.NC + c) * a.H + h) * size_t(D) * D + size_t(r) * D + half * NCOL;
 #pragma unroll
       for (int i = 0; i < NCOL; i += 4) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(src + i);
@@ -220,34 +279,28 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
     }
     g = 1.f;
   };
-  // this lane's part of S k for key row kr
-  auto dot_k = [&](const IN* kr) -> float {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      float x[kChunk];
-      In8<IN>::get(kr + c0 + ch * kChunk, x);
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i) acc[i & 3] = __builtin_fmaf(St[ch * kChunk + i], x[i], acc[i & 3]);
-    }
-    return g * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
-  };
 
-  // the token about to be processed: e, its gate, strength, value element and
-  // y = S_{t-1} k_t (whole row)
-  int e = 0;
-  float al = 1.f, be = 0.f, vr = 0.f, y = 0.f;
+  // the token about to be processed: e, its key kr, the next token's key kn,
+  // its query q (nodes), gate, strength, value element and y = S_{t-1} k_t
+  int e = token(0);
+  float kr[V], kn[V], q[V];
+  SL::cvt(SL::load(krow(e) + c0), kr);
+  SL::cvt(SL::load(krow(token(1)) + c0), kn);
+  SL::cvt(SL::load(qrow(e) + c0), q);
+  float al = gate(e), be = strength(e), vr = vval(e), y = 0.f;
   for (int i = 0; i < n; ++i) {
-    const int ent = entry(i);
-    if (ent & kRestore) {
+    const bool rst = __builtin_amdgcn_readfirstlane(int(s_list[i])) & kRestore;
+    // the next iteration's rows and scalars, loaded during this one
+    const int e1 = token(i + 1), e2 = token(i + 2);
+    const typename SL::raw rk = SL::load(krow(e2) + c0);
+    const typename SL::raw rq = SL::load(qrow(e1) + c0);
+    const float al1 = gate(e1), be1 = strength(e1), vr1 = vval(e1);
+    if (rst) {
       restore();
-      int x = ent & ~kRestore;
-      if (x & kMarker) x = entry(++i);  // no trunk token to replay: the next entry follows directly
-      e = decode(x);
-      y = exchange(dot_k(krow(e)), 0.f).x;
-      al = gate(e);
-      be = strength(e);
-      vr = vval(e);
+      float a2[2] = {0.f, 0.f};
+      dpp_guard(kr, kn, q);
+      dot_pass<V>(St, kr, a2, std::make_integer_sequence<int, NCOL>{});
+      y = exchange(a2[0] + a2[1], 0.f).x;
     }
     // S_t = alpha S_{t-1} + u k^T, u = beta (v - alpha y); as g St with
     // g <- alpha g and St += (u / g) k, the scale folded into St when small
@@ -263,41 +316,20 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
       w = u / gn;
     }
     g = gn;
-    // the next entry, when it continues from this state
-    const bool more = i + 1 < n && !(entry(i + 1) & kRestore);
-    const int en = more ? decode(entry(i + 1)) : e;
-    float aln = 1.f, ben = 0.f, vrn = 0.f;
-    if (more) {
-      aln = gate(en);
-      ben = strength(en);
-      vrn = vval(en);
-    }
-    const bool outp = e < 0;
-    const IN* const kr = krow(e);
-    const IN* const kn = krow(en);
-    const IN* const qr = outp ? bq + ((size_t(tb) * Wn + (-1 - e)) * a.H + h) * D : kr;
-    float ay[4] = {0.f, 0.f, 0.f, 0.f}, ao[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      float xk[kChunk], xn[kChunk], xq[kChunk];
-      In8<IN>::get(kr + c0 + ch * kChunk, xk);
-      In8<IN>::get(kn + c0 + ch * kChunk, xn);
-      In8<IN>::get(qr + c0 + ch * kChunk, xq);
-#pragma unroll
-      for (int c = 0; c < kChunk; ++c) {
-        const int cc = ch * kChunk + c;
-        St[cc] = __builtin_fmaf(w, xk[c], St[cc]);
-        ay[c & 3] = __builtin_fmaf(St[cc], xn[c], ay[c & 3]);
-        ao[c & 3] = __builtin_fmaf(St[cc], xq[c], ao[c & 3]);
-      }
-    }
-    const float2 s = exchange(g * ((ay[0] + ay[1]) + (ay[2] + ay[3])), g * ((ao[0] + ao[1]) + (ao[2] + ao[3])));
-    if (outp && half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = s.y;
+    float ay[2] = {0.f, 0.f}, ao[2] = {0.f, 0.f};
+    dpp_guard(kr, kn, q);
+    token_pass<V>(St, kr, kn, q, w, ay, ao, std::make_integer_sequence<int, NCOL>{});
+    const float2 s = exchange(g * (ay[0] + ay[1]), g * (ao[0] + ao[1]));
+    if (e < 0 && half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = s.y;
     y = s.x;
-    e = en;
-    al = aln;
-    be = ben;
-    vr = vrn;
+    e = e1;
+    al = al1;
+    be = be1;
+    vr = vr1;
+#pragma unroll
+    for (int j = 0; j < V; ++j) kr[j] = kn[j];
+    SL::cvt(rk, kn);
+    SL::cvt(rq, q);
   }
 }
 
