@@ -34,8 +34,6 @@
 // outputs), so no state copy is ever stored.  Malformed branches (anchor
 // outside the trunk, a parent that does not precede its node) get NaN
 // outputs and are counted in the workspace.
-#include <utility>
-
 #include "device_common.h"
 #include "internal.h"
 
@@ -100,42 +98,91 @@ struct Slice<float, 2> {
   }
 };
 
-// acc += x[lane X of this lane's 16-lane row] * y: the DPP row broadcast
-// reads the slice element of column V * X + j in the FMA's own operand
-// fetch, so a row element costs no separate move.  (The compiler does not
-// fold a broadcast move into v_fmac_f32, hence the asm.)
-template <int X>
-__device__ __forceinline__ void fmac_bcast(float& acc, float x, float y) {
-  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(x), "v"(y), "n"(X));
-}
+// One token's pass over a lane's NCOL columns as a single block of
+// v_fmac_f32_dpp: the DPP row broadcast (row_newbcast:X) hands every lane
+// the slice element of lane X of its 16-lane row, i.e. the row element of
+// column V * X + j, in the FMA's own operand fetch.  Per column c:
+//   St[c] += k[c] w;   y += k'[c] St[c];   o += q[c] St[c]
+// (k the token's key, k' the next token's, q its query), two columns at a
+// time with two accumulators each.  A DPP source must not be written by a
+// VALU instruction in the two wait states before, nor EXEC by a SALU one in
+// the five before: each block starts with five.  (The compiler neither folds
+// a broadcast move into v_fmac_f32 nor knows the hazards inside an asm
+// block, hence one block per pass.)
+#define GDN_BC(X) " row_newbcast:" #X " row_mask:0xf bank_mask:0xf\n\t"
+#define GDN_FULL(A, B, JA, JB, X)                     \
+  "v_fmac_f32_dpp %" #A ", %[k" #JA "], %[w]" GDN_BC(X) \
+  "v_fmac_f32_dpp %" #B ", %[k" #JB "], %[w]" GDN_BC(X) \
+  "v_fmac_f32_dpp %[y0], %[n" #JA "], %" #A GDN_BC(X)   \
+  "v_fmac_f32_dpp %[y1], %[n" #JB "], %" #B GDN_BC(X)   \
+  "v_fmac_f32_dpp %[o0], %[q" #JA "], %" #A GDN_BC(X)   \
+  "v_fmac_f32_dpp %[o1], %[q" #JB "], %" #B GDN_BC(X)
+// a trunk token has no output: the update and S k'
+#define GDN_NOQ(A, B, JA, JB, X)                      \
+  "v_fmac_f32_dpp %" #A ", %[k" #JA "], %[w]" GDN_BC(X) \
+  "v_fmac_f32_dpp %" #B ", %[k" #JB "], %[w]" GDN_BC(X) \
+  "v_fmac_f32_dpp %[y0], %[n" #JA "], %" #A GDN_BC(X)   \
+  "v_fmac_f32_dpp %[y1], %[n" #JB "], %" #B GDN_BC(X)
+// S k alone (after a restore)
+#define GDN_DOT(A, B, JA, JB, X)                    \
+  "v_fmac_f32_dpp %[y0], %[k" #JA "], %" #A GDN_BC(X) \
+  "v_fmac_f32_dpp %[y1], %[k" #JB "], %" #B GDN_BC(X)
+// column pairs: 64 columns, 4 slice elements per lane (D = 128)
+#define GDN_COLS64(M)                                                                              \
+  M(0, 1, 0, 1, 0) M(2, 3, 2, 3, 0) M(4, 5, 0, 1, 1) M(6, 7, 2, 3, 1) M(8, 9, 0, 1, 2)             \
+  M(10, 11, 2, 3, 2) M(12, 13, 0, 1, 3) M(14, 15, 2, 3, 3) M(16, 17, 0, 1, 4) M(18, 19, 2, 3, 4)   \
+  M(20, 21, 0, 1, 5) M(22, 23, 2, 3, 5) M(24, 25, 0, 1, 6) M(26, 27, 2, 3, 6) M(28, 29, 0, 1, 7)   \
+  M(30, 31, 2, 3, 7) M(32, 33, 0, 1, 8) M(34, 35, 2, 3, 8) M(36, 37, 0, 1, 9) M(38, 39, 2, 3, 9)   \
+  M(40, 41, 0, 1, 10) M(42, 43, 2, 3, 10) M(44, 45, 0, 1, 11) M(46, 47, 2, 3, 11)                   \
+  M(48, 49, 0, 1, 12) M(50, 51, 2, 3, 12) M(52, 53, 0, 1, 13) M(54, 55, 2, 3, 13)                   \
+  M(56, 57, 0, 1, 14) M(58, 59, 2, 3, 14) M(60, 61, 0, 1, 15) M(62, 63, 2, 3, 15)
+// column pairs: 32 columns, 2 slice elements per lane (D = 64)
+#define GDN_COLS32(M)                                                                              \
+  M(0, 1, 0, 1, 0) M(2, 3, 0, 1, 1) M(4, 5, 0, 1, 2) M(6, 7, 0, 1, 3) M(8, 9, 0, 1, 4)             \
+  M(10, 11, 0, 1, 5) M(12, 13, 0, 1, 6) M(14, 15, 0, 1, 7) M(16, 17, 0, 1, 8) M(18, 19, 0, 1, 9)   \
+  M(20, 21, 0, 1, 10) M(22, 23, 0, 1, 11) M(24, 25, 0, 1, 12) M(26, 27, 0, 1, 13)                   \
+  M(28, 29, 0, 1, 14) M(30, 31, 0, 1, 15)
+#define GDN_ST16(S, o)                                                                              \
+  "+v"(S[o]), "+v"(S[o + 1]), "+v"(S[o + 2]), "+v"(S[o + 3]), "+v"(S[o + 4]), "+v"(S[o + 5]),        \
+      "+v"(S[o + 6]), "+v"(S[o + 7]), "+v"(S[o + 8]), "+v"(S[o + 9]), "+v"(S[o + 10]), "+v"(S[o + 11]), \
+      "+v"(S[o + 12]), "+v"(S[o + 13]), "+v"(S[o + 14]), "+v"(S[o + 15])
+#define GDN_IN4(N, x) [N##0] "v"(x[0]), [N##1] "v"(x[1]), [N##2] "v"(x[2]), [N##3] "v"(x[3])
+#define GDN_IN2(N, x) [N##0] "v"(x[0]), [N##1] "v"(x[1])
 
-// A DPP source must not be written by a VALU instruction in the two
-// preceding wait states, nor EXEC by a SALU one in the five before; the
-// broadcast operands pass through this before each pass, which orders their
-// last writes (and any EXEC write) at least five wait states ahead.
-__device__ __forceinline__ void dpp_guard(float (&a)[4], float (&b)[4], float (&c)[4]) {
-  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]),
-               "+v"(b[3]), "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]));
+// St += w k^T with the partial sums of S k' and, when out is nonzero (a
+// branch node), of S q; the choice is a branch inside the block, so both
+// paths keep the state in the same registers
+__device__ __forceinline__ void token_pass(float (&St)[64], const float (&kr)[4], const float (&kn)[4],
+                                           const float (&q)[4], float w, float (&y)[2], float (&o)[2], int out) {
+  asm("s_nop 4\n\t"
+      "s_cmp_eq_u32 %[out], 0\n\t"
+      "s_cbranch_scc1 1f\n\t" GDN_COLS64(GDN_FULL) "s_branch 2f\n"
+      "1:\n\t" GDN_COLS64(GDN_NOQ) "2:"
+      : GDN_ST16(St, 0), GDN_ST16(St, 16), GDN_ST16(St, 32), GDN_ST16(St, 48), [y0] "+v"(y[0]), [y1] "+v"(y[1]),
+        [o0] "+v"(o[0]), [o1] "+v"(o[1])
+      : GDN_IN4(k, kr), GDN_IN4(n, kn), GDN_IN4(q, q), [w] "v"(w), [out] "s"(out)
+      : "scc");
 }
-__device__ __forceinline__ void dpp_guard(float (&a)[2], float (&b)[2], float (&c)[2]) {
-  asm volatile("s_nop 4" : "+v"(a[0]), "+v"(a[1]), "+v"(b[0]), "+v"(b[1]), "+v"(c[0]), "+v"(c[1]));
+__device__ __forceinline__ void token_pass(float (&St)[32], const float (&kr)[2], const float (&kn)[2],
+                                           const float (&q)[2], float w, float (&y)[2], float (&o)[2], int out) {
+  asm("s_nop 4\n\t"
+      "s_cmp_eq_u32 %[out], 0\n\t"
+      "s_cbranch_scc1 1f\n\t" GDN_COLS32(GDN_FULL) "s_branch 2f\n"
+      "1:\n\t" GDN_COLS32(GDN_NOQ) "2:"
+      : GDN_ST16(St, 0), GDN_ST16(St, 16), [y0] "+v"(y[0]), [y1] "+v"(y[1]), [o0] "+v"(o[0]), [o1] "+v"(o[1])
+      : GDN_IN2(k, kr), GDN_IN2(n, kn), GDN_IN2(q, q), [w] "v"(w), [out] "s"(out)
+      : "scc");
 }
-
-// One token's pass over a lane's NCOL columns: St += w k^T (k broadcast from
-// kr), then the partial sums of S k' (k' from kn) and S q (from q).
-template <int V, int... C>
-__device__ __forceinline__ void token_pass(float (&St)[sizeof...(C)], const float (&kr)[V], const float (&kn)[V],
-                                           const float (&q)[V], float w, float (&ay)[2], float (&ao)[2],
-                                           std::integer_sequence<int, C...>) {
-  ((fmac_bcast<C / V>(St[C], kr[C % V], w), fmac_bcast<C / V>(ay[C & 1], kn[C % V], St[C]),
-    fmac_bcast<C / V>(ao[C & 1], q[C % V], St[C])),
-   ...);
+// the partial sums of S k
+__device__ __forceinline__ void dot_pass(float (&St)[64], const float (&kr)[4], float (&y)[2]) {
+  asm("s_nop 4\n\t" GDN_COLS64(GDN_DOT)
+      : GDN_ST16(St, 0), GDN_ST16(St, 16), GDN_ST16(St, 32), GDN_ST16(St, 48), [y0] "+v"(y[0]), [y1] "+v"(y[1])
+      : GDN_IN4(k, kr));
 }
-// The partial sums of S k alone (after a restore).
-template <int V, int... C>
-__device__ __forceinline__ void dot_pass(const float (&St)[sizeof...(C)], const float (&kr)[V], float (&ay)[2],
-                                         std::integer_sequence<int, C...>) {
-  (fmac_bcast<C / V>(ay[C & 1], kr[C % V], St[C]), ...);
+__device__ __forceinline__ void dot_pass(float (&St)[32], const float (&kr)[2], float (&y)[2]) {
+  asm("s_nop 4\n\t" GDN_COLS32(GDN_DOT)
+      : GDN_ST16(St, 0), GDN_ST16(St, 16), [y0] "+v"(y[0]), [y1] "+v"(y[1])
+      : GDN_IN2(k, kr));
 }
 
 struct GdnArgs {
@@ -154,7 +201,7 @@ struct GdnArgs {
 constexpr int kMaxList = 64 * (63 + 63) + 64;
 
 template <int D, typename IN>
-__global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a) {
+__device__ __forceinline__ void gdn_replay(const GdnArgs& a) {
   constexpr int NCOL = D / 2;   // columns per lane
   constexpr int RB = D / 64;    // 64-row blocks
   constexpr int V = NCOL / 16;  // slice elements per lane
@@ -298,8 +345,7 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
     if (rst) {
       restore();
       float a2[2] = {0.f, 0.f};
-      dpp_guard(kr, kn, q);
-      dot_pass<V>(St, kr, a2, std::make_integer_sequence<int, NCOL>{});
+      dot_pass(St, kr, a2);
       y = exchange(a2[0] + a2[1], 0.f).x;
     }
     // S_t = alpha S_{t-1} + u k^T, u = beta (v - alpha y); as g St with
@@ -313,12 +359,11 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
       gn = 1.f;
       w = u;
     } else {
-      w = u / gn;
+      w = u * __builtin_amdgcn_rcpf(gn);
     }
     g = gn;
     float ay[2] = {0.f, 0.f}, ao[2] = {0.f, 0.f};
-    dpp_guard(kr, kn, q);
-    token_pass<V>(St, kr, kn, q, w, ay, ao, std::make_integer_sequence<int, NCOL>{});
+    token_pass(St, kr, kn, q, w, ay, ao, e < 0);
     const float2 s = exchange(g * (ay[0] + ay[1]), g * (ao[0] + ao[1]));
     if (e < 0 && half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = s.y;
     y = s.x;
@@ -331,6 +376,17 @@ __global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a
     SL::cvt(rk, kn);
     SL::cvt(rq, q);
   }
+}
+
+template <int D, typename IN>
+__global__ __launch_bounds__(D / 32 * 64) void gdn_replay_kernel(const GdnArgs a) {
+  gdn_replay<D, IN>(a);
+}
+// bf16 slices leave the D = 128 kernel at 96 VGPRs: five workgroups per CU
+template <>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void gdn_replay_kernel<128, uint16_t>(
+    const GdnArgs a) {
+  gdn_replay<128, uint16_t>(a);
 }
 
 __global__ void gdn_zero_kernel(int32_t* __restrict__ bad) {
