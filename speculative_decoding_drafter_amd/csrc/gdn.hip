@@ -15,17 +15,19 @@
 // A branch node's state is its parent's state (the anchor's for a root)
 // updated with the node's own token.
 //
-// One workgroup per (trunk, branch, head).  The D x D state lives in
-// registers: lane l of wave w holds row 64 (w mod D/64) + l, columns
-// [D/2 * (w div D/64), + D/2), as S / g with one running scale g for the
-// whole state, so a token's decay costs one scalar multiply and its update
-// one fused multiply-add per element.  The token's key, query and the next
-// token's key are the same for every lane of a wave, so they are read into
-// scalar registers and used as the scalar operand of the vector FMAs; a
-// token's value is one element per lane.  Per token each lane forms its
-// partial S k (for the next token) and S q (its output) over its columns
-// while it updates them; the two column halves of a row exchange partials
-// through LDS, one barrier per token.
+// One workgroup per (trunk, branch, head), D/32 waves.  The D x D state
+// lives in registers: lanes l and l + 32 of wave w hold row 32 w + (l mod 32),
+// the first and the second half of its columns, as S / g with one running
+// scale g for the whole state, so a token's decay costs one scalar multiply
+// and its update one fused multiply-add per element.  Key and query rows are
+// read as per-lane slices (four or two consecutive elements per lane, each
+// 16-lane row of the wave holding one half of the row) and reach every lane
+// through DPP row broadcasts in the FMAs' operands; a token's value is one
+// element per row.  Per token each lane updates its columns and, in the same
+// pass, forms its part of S k for the next token and of S q for its output;
+// the two halves of a row are summed by a lane swap within the wave, so the
+// waves of a workgroup never wait for each other after the list is built.
+// The next token's rows are loaded while the current one is processed.
 //
 // The order of work is a list built by one thread from the parent map:
 // replay the trunk suffix, then the nodes in index order; a node whose
@@ -203,17 +205,15 @@ constexpr int kMaxList = 64 * (63 + 63) + 64;
 template <int D, typename IN>
 __device__ __forceinline__ void gdn_replay(const GdnArgs& a) {
   constexpr int NCOL = D / 2;   // columns per lane
-  constexpr int RB = D / 64;    // 64-row blocks
   constexpr int V = NCOL / 16;  // slice elements per lane
   using SL = Slice<IN, V>;
   __shared__ uint16_t s_list[kMaxList];
   __shared__ int s_par[64];
   __shared__ int s_n;
-  __shared__ float s_x[2][2][2][64 * RB];  // [buffer][column half][S k, S q][row]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = wave / RB, r = (wave % RB) * 64 + lane;
+  const int half = lane >> 5, r = wave * 32 + (lane & 31);
   const int c0 = half * NCOL + V * (lane & 15);  // this lane's slice of a row
   const int h = blockIdx.x % a.H;
   const int tb = blockIdx.x / a.H;  // trunk * B + branch
@@ -297,15 +297,14 @@ __device__ __forceinline__ void gdn_replay(const GdnArgs& a) {
 
   float St[NCOL];
   float g = 1.f;  // the state is g * St
-  int buf = 0;
-  // sums of the two column halves' partials of this lane's row
-  auto exchange = [&](float y, float o) -> float2 {
-    s_x[buf][half][0][r] = y;
-    s_x[buf][half][1][r] = o;
-    __syncthreads();
-    const float y2 = s_x[buf][half ^ 1][0][r], o2 = s_x[buf][half ^ 1][1][r];
-    buf ^= 1;
-    return make_float2(y + y2, o + o2);
+  // the sum of the two column halves' partials of this lane's row (lanes l
+  // and l + 32): v_permlane32_swap trades the upper half of one register
+  // with the lower half of the other, so with both holding x each ends with
+  // x[l mod 32] in one and x[l mod 32 + 32] in the other
+  auto halves = [&](float x) -> float {
+    float p = x, q = x;
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(p), "+v"(q));
+    return p + q;
   };
   // the checkpoint at or before the anchor (the zero state if none)
   auto restore = [&]() {
@@ -346,7 +345,7 @@ __device__ __forceinline__ void gdn_replay(const GdnArgs& a) {
       restore();
       float a2[2] = {0.f, 0.f};
       dot_pass(St, kr, a2);
-      y = exchange(a2[0] + a2[1], 0.f).x;
+      y = halves(a2[0] + a2[1]);
     }
     // S_t = alpha S_{t-1} + u k^T, u = beta (v - alpha y); as g St with
     // g <- alpha g and St += (u / g) k, the scale folded into St when small
@@ -364,9 +363,11 @@ __device__ __forceinline__ void gdn_replay(const GdnArgs& a) {
     g = gn;
     float ay[2] = {0.f, 0.f}, ao[2] = {0.f, 0.f};
     token_pass(St, kr, kn, q, w, ay, ao, e < 0);
-    const float2 s = exchange(g * (ay[0] + ay[1]), g * (ao[0] + ao[1]));
-    if (e < 0 && half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = s.y;
-    y = s.x;
+    y = halves(g * (ay[0] + ay[1]));
+    if (e < 0) {
+      const float o = halves(g * (ao[0] + ao[1]));
+      if (half == 0) orow0[(size_t(-1 - e) * a.H + h) * D + r] = o;
+    }
     e = e1;
     al = al1;
     be = be1;
