@@ -306,12 +306,18 @@ typedef struct {
   specopd_dtype grad_dtype;    /* gradient output                            */
   double norm_count;           /* <= 0: R*Wn; else the global count (Eq. 18) */
   float grad_scale;            /* factor applied to the gradient (1 = dLoss) */
-  uint32_t flags;              /* reserved, must be 0                        */
+  uint32_t flags;              /* 0 or SPECOPD_E2ETV_DEFER_ALL               */
   int32_t wait_polls;          /* bound on a row's polls for its branch; <= 0:
                                   2^20 (see specopd_e2etv_fwd_bwd)           */
   int32_t target_rows;         /* rows of target_logits when target_row is
                                   given (ignored otherwise)                  */
 } specopd_e2etv_desc;
+
+/* Every row that needs its branch's scan skips the wait for its siblings and
+ * is finished by the follow-up kernel of the same call, exactly as a row
+ * whose bounded wait gave up (see wait_polls); the outputs are the same.  It
+ * makes that path run on every call, for tests; normal callers pass 0. */
+#define SPECOPD_E2ETV_DEFER_ALL 1u
 
 specopd_status specopd_e2etv_workspace_size(const specopd_e2etv_desc* desc, size_t* bytes);
 

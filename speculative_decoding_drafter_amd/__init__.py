@@ -7,7 +7,7 @@ ABI of include/specopd.h); this package is its thin Python binding.
 from ._lib import (  # noqa: F401
     EXPORTS, LIB, LIB_PATH, SpecopdError, TreeAttnDesc, E2etvDesc, SPECOPD_OK,
     SPECOPD_ERR_INVALID_ARGUMENT, SPECOPD_ERR_UNSUPPORTED, SPECOPD_ERR_WORKSPACE, SPECOPD_ERR_HIP,
-    SPECOPD_ERR_DEVICE_VALIDATION, SPECOPD_F32, SPECOPD_BF16, SPECOPD_TREE_BATCH_INVARIANT, status_string, specopd_version,
+    SPECOPD_ERR_DEVICE_VALIDATION, SPECOPD_F32, SPECOPD_BF16, SPECOPD_TREE_BATCH_INVARIANT, SPECOPD_E2ETV_DEFER_ALL, status_string, specopd_version,
     tree_attn_desc, e2etv_desc, specopd_tree_attn_workspace_size, specopd_tree_attn_fwd,
     specopd_tree_attn_device_status, specopd_e2etv_workspace_size, specopd_e2etv_fwd_bwd,
     specopd_e2etv_device_status, specopd_e2etv_fwd_bwd_noalloc, E2ETV_NOALLOC_SCRATCH_BYTES,

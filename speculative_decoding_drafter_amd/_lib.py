@@ -27,6 +27,7 @@ SPECOPD_F32 = 0
 SPECOPD_BF16 = 1
 
 SPECOPD_TREE_BATCH_INVARIANT = 1
+SPECOPD_E2ETV_DEFER_ALL = 1
 
 E2ETV_NOALLOC_SCRATCH_BYTES = 4 << 20  # SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES
 
@@ -374,14 +375,14 @@ def prefill(q, k, v, rope_base=10000.0, scale=0.0, ws=None, outs=None):
 
 
 def e2etv(draft, target, parent, grad=True, grad_dtype=torch.float32, norm_count=0.0,
-          grad_scale=1.0, ws=None, outs=None, wait_polls=0, target_row=None):
+          grad_scale=1.0, ws=None, outs=None, wait_polls=0, target_row=None, flags=0):
     """E2E-TV forward + gradient; returns dict of device tensors.  With
     target_row ([R][Wn] int32), target is a matrix of score rows [rows][V]
     and node n's target distribution is row target_row[n] of it."""
     R, Wn, V = draft.shape
     dev = draft.device
     desc = e2etv_desc(R, Wn, V, draft.dtype, grad_dtype, norm_count, grad_scale,
-                      wait_polls=wait_polls,
+                      flags=flags, wait_polls=wait_polls,
                       target_rows=target.numel() // V if target_row is not None else 0)
     if ws is None:
         ws = workspace(specopd_e2etv_workspace_size(desc), dev)

@@ -217,6 +217,7 @@ struct FusedArgs {
   double count;
   float grad_scale;
   int spin_limit;
+  int defer_all;  // every row that may defer does so without waiting
   unsigned long long* slot;  // [N] posted (alpha, G) of every row, 0 until posted
   int32_t* ticket;
   int32_t* done;    // branches that reported their numerator
@@ -265,7 +266,8 @@ __device__ __forceinline__ double lane_f64(double v, int l) {
 // walks the nodes in index order (children come after their parents) with
 // every value held by its node's lane, so every row of a branch does the
 // same arithmetic in the same order, in whichever kernel it runs.
-// When the wait gives up and `can_defer`, the row records its log-sum-exps,
+// When the wait gives up (or, with SPECOPD_E2ETV_DEFER_ALL, without waiting)
+// and `can_defer`, the row records its log-sum-exps,
 // appends itself to the deferred list and sets s_val[2]; its scan and
 // gradient are then done by e2etv_rescue_kernel.
 __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, int j,
@@ -281,7 +283,7 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
   // branch have nothing to wait for
   unsigned long long v = (post && lane == j) ? mine : 0ull;
   bool have = lane >= Wn || (post && lane == j);
-  for (int spins = 0;;) {
+  for (int spins = 0; !(can_defer && a.defer_all);) {
     if (!have) {
       v = __hip_atomic_load(bs + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       have = (v & kPosted) != 0;
@@ -292,7 +294,7 @@ __device__ __forceinline__ void post_and_scan(const FusedArgs& a, int n, int r, 
     else
       __builtin_amdgcn_s_sleep(8);
   }
-  if (can_defer && __builtin_amdgcn_ballot_w64(!have) != 0) {
+  if (can_defer && (a.defer_all || __builtin_amdgcn_ballot_w64(!have) != 0)) {
     if (lane == 0) {
       a.lse[n] = make_float2(nlz, nlt);
       const int at = __hip_atomic_fetch_add(a.ndefer, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -931,6 +933,7 @@ hipError_t launch_all(const specopd_e2etv_desc& d, const E2etvArgs& a, hipStream
   f.count = d.norm_count > 0 ? d.norm_count : double(N);
   f.grad_scale = d.grad_scale;
   f.spin_limit = spin_limit;
+  f.defer_all = (d.flags & SPECOPD_E2ETV_DEFER_ALL) != 0;
   f.slot = reinterpret_cast<unsigned long long*>(a.ws + L.slot);
   f.ticket = reinterpret_cast<int32_t*>(a.ws + L.ticket);
   f.done = reinterpret_cast<int32_t*>(a.ws + e2etv_done_offset(L));

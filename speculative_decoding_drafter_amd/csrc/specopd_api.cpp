@@ -75,7 +75,7 @@ specopd_status check_e2etv_desc(const specopd_e2etv_desc* d) {
   if (d->Wn > 64) return SPECOPD_ERR_UNSUPPORTED;
   if (d->logits_dtype != SPECOPD_F32 && d->logits_dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->grad_dtype != SPECOPD_F32 && d->grad_dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
-  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if ((d->flags & ~SPECOPD_E2ETV_DEFER_ALL) != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (!isfinite(d->norm_count) || !isfinite(d->grad_scale)) return SPECOPD_ERR_INVALID_ARGUMENT;
   const double rows = double(d->R) * d->Wn;
   if (rows > 2147483647.0) return SPECOPD_ERR_UNSUPPORTED;

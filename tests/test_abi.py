@@ -32,6 +32,13 @@ def test_every_declared_symbol_is_exported():
     assert set(_lib.EXPORTS) == set(names)
 
 
+def test_flag_constants_match_the_header():
+    src = open(HDR).read()
+    for name in ("SPECOPD_TREE_BATCH_INVARIANT", "SPECOPD_E2ETV_DEFER_ALL"):
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)u", src)
+        assert m and int(m.group(1)) == getattr(sd, name), name
+
+
 def test_version_and_status_strings():
     assert sd.specopd_version() == 2
     assert sd.status_string(0) == "ok"

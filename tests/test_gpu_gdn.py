@@ -200,3 +200,19 @@ def test_deterministic(gpu_ok):
     b, _, _ = sd.gdn_replay(inp, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+def test_kernel_timing_records_each_call(gpu_ok):
+    cfg = shrink_gdn(WORKLOADS[3].gdn, T=1, L=200, P=16, B=8, H=2, D=128)
+    inp = gen_gdn(cfg, 12, device=DEV, cid=3)
+    out, desc, ws = _run(inp)
+    sd.specopd_kernel_timing(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(2):
+        sd.gdn_replay(inp, ws=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms, n = sd.specopd_kernel_time(3)
+    sd.specopd_kernel_timing(False)
+    assert n == 2 and 0 < ms <= e0.elapsed_time(e1) * 1.05

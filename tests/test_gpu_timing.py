@@ -42,5 +42,6 @@ def test_kernel_timing_records_each_call(gpu_ok):
     torch.cuda.synchronize()
     assert sd.specopd_kernel_time(0) == (0.0, 0)
     assert sd.specopd_kernel_time(2) == (0.0, 0)  # prefill: nothing recorded
+    assert sd.specopd_kernel_time(3) == (0.0, 0)  # GDN replay: nothing recorded
     with pytest.raises(sd.SpecopdError):
-        sd.specopd_kernel_time(3)
+        sd.specopd_kernel_time(4)
