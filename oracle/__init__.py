@@ -30,7 +30,8 @@ from .e2etv import (logsumexp, log_softmax, overlap, prefix_products, suffix_sum
 from .rows import score_row_source, new_score_rows, shared_row_count
 from .prefill import trunk_prefill, trunk_prefill_cache
 from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, replay_span,
-                  anchor_state, gdn_branch, gdn_replay, update_counts)
+                  anchor_state, gdn_branch, gdn_replay, update_counts, conv_history, branch_conv,
+                  gdn_branch_conv)
 
 __all__ = [
     "rope", "rope_angles", "walk_ancestors", "tree_depths", "check_positions",
@@ -39,5 +40,5 @@ __all__ = [
     "suffix_sums", "e2etv", "e2etv_branch", "score_row_source", "new_score_rows",
     "shared_row_count", "trunk_prefill", "trunk_prefill_cache", "gated_delta_update",
     "gdn_read", "run_tokens", "trunk_checkpoints", "replay_span", "anchor_state", "gdn_branch",
-    "gdn_replay", "update_counts",
+    "gdn_replay", "update_counts", "conv_history", "branch_conv", "gdn_branch_conv",
 ]

@@ -14,6 +14,9 @@ What the pages fix ([R] §3.2(c), Fig. 5; [S] §1):
     execution, replay included, are counted against cacheless scoring
     (24.9x at L = 2048, W = 7, K = 512).
 
+  * [R] §3.2(c): the convolution history, like the recurrent state, follows
+    only the branch's ancestors.
+
 Readings where the pages are silent:
   * the recurrence is the gated delta rule as published for Gated DeltaNet:
     per head, with a state S of shape [Dv][Dk],
@@ -30,6 +33,12 @@ Readings where the pages are silent:
     updated with the node's own (k, v, alpha, beta); its output reads that
     state with the node's query.  Nodes come in an order where each parent
     precedes its children.
+  * the convolution is Gated DeltaNet's short convolution: per channel a
+    causal depthwise convolution of width K over the layer's projected
+    inputs, then SiLU (z sigmoid(z)); q and k are then scaled to unit length
+    per head (x / sqrt(sum x^2 + 1e-6), the epsilon guarding a zero vector).
+    For a branch node the K inputs are the node's own, then its ancestors',
+    then trunk tokens a, a - 1, ..., with zeros before the trunk's start.
 """
 
 from __future__ import annotations
@@ -166,3 +175,60 @@ def update_counts(L, anchors, W, C=64):
     replay = np.array([int(a) + 1 - replay_span(a, C)[1] for a in anchors])
     shared = int(L + np.sum(replay) + len(anchors) * (W - 1))
     return cacheless, shared
+
+
+def conv_history(a, parent, j, K):
+    """The K inputs node j's convolution reads, newest first: ('n', i) for
+    branch node i, ('t', s) for trunk token s, None before the trunk."""
+    out = []
+    x = int(j)
+    s = int(a)
+    for _ in range(K):
+        if x >= 0:
+            out.append(("n", x))
+            x = int(parent[x])
+        elif s >= 0:
+            out.append(("t", s))
+            s -= 1
+        else:
+            out.append(None)
+    return out
+
+
+def branch_conv(trunk_x, x, w, a, parent, D=None, l2norm=False):
+    """One branch's convolved inputs [Wn][C]: trunk_x [L][C] and x [Wn][C] are
+    the layer's projected inputs before the convolution, w [C][K] its weights
+    (w[:, i] multiplies the i-th newest input).  With l2norm, every head of D
+    channels is scaled to unit length."""
+    trunk_x = np.asarray(trunk_x, np.float64)
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    check_branch(parent, a, trunk_x.shape[0])
+    Wn, C = x.shape
+    K = w.shape[1]
+    out = np.empty((Wn, C))
+    for j in range(Wn):
+        z = np.zeros(C)
+        for i, src in enumerate(conv_history(a, parent, j, K)):
+            if src is None:
+                continue
+            z += w[:, i] * (x[src[1]] if src[0] == "n" else trunk_x[src[1]])
+        y = z / (1.0 + np.exp(-z))
+        if l2norm:
+            y = y.reshape(-1, D)
+            y = y / np.sqrt((y * y).sum(axis=1, keepdims=True) + 1e-6)
+            y = y.reshape(C)
+        out[j] = y
+    return out
+
+
+def gdn_branch_conv(trunk_x, x, w, anchors, parent, D=None, l2norm=False, branches=None):
+    """Every branch's convolved inputs: trunk_x [T][L][C], x [T][B][Wn][C] ->
+    [T][B][Wn][C] (NaN for branches not in ``branches`` when given)."""
+    x = np.asarray(x, np.float64)
+    T, B = x.shape[:2]
+    out = np.full(x.shape, np.nan)
+    todo = branches if branches is not None else [(t, b) for t in range(T) for b in range(B)]
+    for t, b in todo:
+        out[t, b] = branch_conv(trunk_x[t], x[t, b], w, anchors[t, b], parent[t, b], D, l2norm)
+    return out

@@ -199,3 +199,83 @@ def test_update_counts_match_the_page_ratio():
     # the replay after the nearest checkpoint averages (C - 1) / 2 tokens
     rep = [a + 1 - gdn.replay_span(a)[1] for a in range(64 * 10)]
     assert np.mean(rep) == 31.5 and max(rep) == 63 and min(rep) == 0
+
+
+# ---- the short convolution along the parent map ([R] §3.2(c): the
+# convolution history follows only the branch's ancestors)
+
+def _silu(z):
+    from scipy.special import expit
+    return z * expit(z)
+
+
+@pytest.mark.parametrize("K,a", [(4, 37), (3, 5), (4, 1), (2, 0)])
+def test_chain_conv_is_the_causal_convolution_of_its_history(K, a):
+    """For a chain, the branch is a continuation of the trunk: each node's
+    output is the plain causal convolution (numpy's) of the sequence trunk
+    0..a followed by the nodes, zero-padded before the trunk's start."""
+    rng = np.random.default_rng(20 + K + a)
+    L, Wn, C = 40, 6, 5
+    trunk_x, x = rng.normal(size=(L, C)), rng.normal(size=(Wn, C))
+    w = rng.normal(size=(C, K))
+    parent = np.arange(Wn) - 1
+    got = gdn.branch_conv(trunk_x, x, w, a, parent)
+    seq = np.concatenate([trunk_x[: a + 1], x])
+    for c in range(C):
+        full = np.convolve(seq[:, c], w[c])  # full[t] = sum_i w[c, i] seq[t - i]
+        np.testing.assert_allclose(got[:, c], _silu(full[a + 1: a + 1 + Wn]), rtol=0, atol=1e-13)
+
+
+def test_fork_history_follows_the_parent_map():
+    # the forked tree of the long-context configuration: node 7 hangs off
+    # node 3, so its window skips nodes 4-6; a root reaches into the trunk
+    par = [-1, 0, 1, 2, 3, 4, 5, 3, 7, 8]
+    assert gdn.conv_history(100, par, 7, 4) == [("n", 7), ("n", 3), ("n", 2), ("n", 1)]
+    assert gdn.conv_history(100, par, 8, 4) == [("n", 8), ("n", 7), ("n", 3), ("n", 2)]
+    assert gdn.conv_history(100, par, 1, 4) == [("n", 1), ("n", 0), ("t", 100), ("t", 99)]
+    assert gdn.conv_history(1, par, 0, 4) == [("n", 0), ("t", 1), ("t", 0), None]
+
+
+def test_conv_ignores_nodes_outside_the_window():
+    """Poisoning a node changes exactly the outputs whose window holds it."""
+    rng = np.random.default_rng(31)
+    par = [-1, 0, 1, 2, 3, 4, 5, 3, 7, 8]
+    L, C, K, a = 50, 4, 4, 30
+    trunk_x, x, w = rng.normal(size=(L, C)), rng.normal(size=(len(par), C)), rng.normal(size=(C, K))
+    base = gdn.branch_conv(trunk_x, x, w, a, par)
+    for poison in range(len(par)):
+        xp = x.copy()
+        xp[poison] = np.nan
+        got = gdn.branch_conv(trunk_x, xp, w, a, par)
+        for j in range(len(par)):
+            sees = ("n", poison) in gdn.conv_history(a, par, j, K)
+            assert np.isnan(got[j]).all() == sees
+            if not sees:
+                np.testing.assert_array_equal(got[j], base[j])
+
+
+def test_width_one_is_silu_of_the_scaled_input():
+    rng = np.random.default_rng(32)
+    x, w = rng.normal(size=(3, 6)), rng.normal(size=(6, 1))
+    got = gdn.branch_conv(rng.normal(size=(10, 6)), x, w, 4, [-1, 0, 0])
+    np.testing.assert_allclose(got, _silu(x * w[:, 0]), rtol=0, atol=1e-14)
+
+
+def test_l2norm_gives_unit_heads_in_the_same_direction():
+    rng = np.random.default_rng(33)
+    H, D = 3, 8
+    trunk_x, x, w = rng.normal(size=(20, H * D)), rng.normal(size=(4, H * D)), rng.normal(size=(H * D, 4))
+    par = [-1, 0, 1, 1]
+    plain = gdn.branch_conv(trunk_x, x, w, 10, par).reshape(4, H, D)
+    unit = gdn.branch_conv(trunk_x, x, w, 10, par, D=D, l2norm=True).reshape(4, H, D)
+    nrm = np.linalg.norm(plain, axis=2, keepdims=True)
+    np.testing.assert_allclose(unit, plain / np.sqrt(nrm ** 2 + 1e-6), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(np.linalg.norm(unit, axis=2), 1.0, atol=1e-5)
+
+
+def test_conv_of_malformed_branch_raises():
+    x, w = np.zeros((3, 2)), np.ones((2, 4))
+    with pytest.raises(ValueError):
+        gdn.branch_conv(np.zeros((5, 2)), x, w, 5, [-1, 0, 1])
+    with pytest.raises(ValueError):
+        gdn.branch_conv(np.zeros((5, 2)), x, w, 2, [-1, 2, 1])

@@ -93,6 +93,18 @@ CASES = {
         "oracle.gdn", "gdn_branch", "Sp = Sa if parent[j] < 0 else states[int(parent[j])]",
         "Sp = Sa if j == 0 else states[j - 1]",
         [tg.test_sibling_subtrees_do_not_see_each_other]),
+    "conv window walks node indices, not parents": (
+        "oracle.gdn", "conv_history", "x = int(parent[x])", "x = x - 1",
+        [tg.test_fork_history_follows_the_parent_map, tg.test_conv_ignores_nodes_outside_the_window]),
+    "conv trunk history starts a token early": (
+        "oracle.gdn", "conv_history", "s = int(a)\n", "s = int(a) - 1\n",
+        [lambda: tg.test_chain_conv_is_the_causal_convolution_of_its_history(4, 37)]),
+    "conv activation sign flipped": (
+        "oracle.gdn", "branch_conv", "y = z / (1.0 + np.exp(-z))", "y = z / (1.0 + np.exp(z))",
+        [tg.test_width_one_is_silu_of_the_scaled_input]),
+    "conv weights applied newest-last": (
+        "oracle.gdn", "branch_conv", "z += w[:, i] *", "z += w[:, K - 1 - i] *",
+        [lambda: tg.test_chain_conv_is_the_causal_convolution_of_its_history(3, 5)]),
     "score row of the node itself": (
         "oracle.rows", "score_row_source", 'else ("node", p)', 'else ("node", int(j))',
         [tt.test_fig3_toy_tree]),
