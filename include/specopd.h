@@ -1,7 +1,7 @@
 /*
  * libspecopd — branch-parallel target scoring for SpecOPD on MI355X (gfx950).
  *
- * Three operations, all defined by the pages describing arXiv 2611.02846,
+ * The operations, all defined by the pages describing arXiv 2611.02846,
  * "SpecOPD: Branch-Parallel On-Policy Distillation for Speculative Decoding":
  *
  *   specopd_tree_attn_fwd   tree-masked GQA attention of every branch node
@@ -17,6 +17,9 @@
  *   specopd_gdn_replay_fwd  branch scoring for a linear-attention (GDN)
  *                           target by indexed state replay from trunk
  *                           checkpoints (jaehun.me review, §3.2(c), Fig. 5).
+ *   specopd_gdn_conv_fwd    that layer's short convolution for branch nodes,
+ *                           its history following the branch's ancestors
+ *                           (jaehun.me review, §3.2(c)).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -294,6 +297,46 @@ specopd_status specopd_gdn_device_status(const specopd_gdn_desc* desc, const voi
                                          size_t workspace_bytes, int32_t* bad_branches,
                                          hipStream_t stream);
 
+/*
+ * The layer's short convolution for branch nodes (jaehun.me review, §3.2(c):
+ * the convolution history, like the recurrent state, follows only the
+ * branch's ancestors).  Gated DeltaNet convolves its projected q, k and v
+ * per channel with a causal window of K inputs, applies SiLU (z sigmoid(z))
+ * and scales q and k to unit length per head, before the recurrence above.
+ * A branch node's K inputs are its own, its ancestors' (nearest first), then
+ * trunk tokens a, a-1, ... of its anchor a (zeros before token 0).  One call
+ * convolves one of q, k, v:
+ *
+ *   trunk_x   [T][L][H*D]       the trunk's projected inputs before the
+ *                               convolution (tokens a-K+2..a are read)
+ *   x         [T][B][Wn][H*D]   the nodes' projected inputs
+ *   w         [H*D][K] fp32     w[c][i] multiplies channel c of the i-th
+ *                               newest input (i = 0: the node itself)
+ *   anchors, parent             as for specopd_gdn_replay_fwd
+ *   out       [T][B][Wn][H*D]   out: SiLU(sum_i w[c][i] x_i[c]), computed in
+ *                               fp32; with SPECOPD_GDN_CONV_L2NORM each
+ *                               head's D values are then divided by
+ *                               sqrt(sum of their squares + 1e-6)
+ *
+ * trunk_x, x and out share desc->dtype.  A node whose window meets a parent
+ * that does not precede its child, or whose anchor is outside [0, L), gets
+ * NaN outputs (specopd_gdn_replay_fwd on the same parent map counts such
+ * branches).  No workspace.  All pointers 16-byte aligned; out must not alias
+ * an input.
+ */
+typedef struct {
+  int32_t T, L, B, Wn, H, D; /* as specopd_gdn_desc (D in {64, 128})           */
+  int32_t K;                 /* convolution width, 1 <= K <= 8                 */
+  specopd_dtype dtype;       /* of trunk_x, x and out                          */
+  uint32_t flags;            /* 0 or SPECOPD_GDN_CONV_L2NORM                   */
+} specopd_gdn_conv_desc;
+
+#define SPECOPD_GDN_CONV_L2NORM 1u
+
+specopd_status specopd_gdn_conv_fwd(const specopd_gdn_conv_desc* desc, const void* trunk_x,
+                                    const void* x, const float* w, const int32_t* anchors,
+                                    const int32_t* parent, void* out, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* E2E-TV surrogate                                                          */
 /* ------------------------------------------------------------------------ */
@@ -427,13 +470,13 @@ specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
  * kernel (the attention kernel proper, after the preparation kernel; the
  * E2E-TV kernel, without the small kernel that clears its counters; the
  * attention kernel of each prefilled trunk; the GDN replay kernel, without
- * the one that clears its counter), so that a harness can divide a kernel's algorithmic work
+ * the one that clears its counter; the GDN convolution kernel), so that a harness can divide a kernel's algorithmic work
  * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is
  * created when timing is switched on and kept for the process).
  *
  * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
- * 1 E2E-TV, 2 prefill, 3 GDN replay.  Waits for the recorded events and returns the summed elapsed
+ * 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution.  Waits for the recorded events and returns the summed elapsed
  * milliseconds and the number of recorded launches.  Returns
  * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
  * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while

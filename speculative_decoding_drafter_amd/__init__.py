@@ -14,5 +14,5 @@ from ._lib import (  # noqa: F401
     specopd_kernel_timing, specopd_kernel_time, workspace, tree_attn, specopd_score_rows, score_rows,
     e2etv, PrefillDesc, prefill_desc, specopd_prefill_workspace_size, specopd_prefill_fwd, prefill,
     GdnDesc, gdn_desc, specopd_gdn_workspace_size, specopd_gdn_replay_fwd, specopd_gdn_device_status,
-    gdn_replay,
+    gdn_replay, GdnConvDesc, gdn_conv_desc, specopd_gdn_conv_fwd, gdn_conv, SPECOPD_GDN_CONV_L2NORM,
 )

@@ -28,6 +28,7 @@ SPECOPD_BF16 = 1
 
 SPECOPD_TREE_BATCH_INVARIANT = 1
 SPECOPD_E2ETV_DEFER_ALL = 1
+SPECOPD_GDN_CONV_L2NORM = 1
 
 E2ETV_NOALLOC_SCRATCH_BYTES = 4 << 20  # SPECOPD_E2ETV_NOALLOC_SCRATCH_BYTES
 
@@ -39,6 +40,7 @@ EXPORTS = (
     "specopd_e2etv_fwd_bwd_noalloc",
     "specopd_prefill_workspace_size", "specopd_prefill_fwd",
     "specopd_gdn_workspace_size", "specopd_gdn_replay_fwd", "specopd_gdn_device_status",
+    "specopd_gdn_conv_fwd",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
@@ -64,6 +66,11 @@ class PrefillDesc(ctypes.Structure):
 class GdnDesc(ctypes.Structure):
     _fields_ = [("T", c_int32), ("L", c_int32), ("B", c_int32), ("Wn", c_int32), ("H", c_int32),
                 ("D", c_int32), ("C", c_int32), ("dtype", c_int), ("flags", c_uint32)]
+
+
+class GdnConvDesc(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("L", c_int32), ("B", c_int32), ("Wn", c_int32), ("H", c_int32),
+                ("D", c_int32), ("K", c_int32), ("dtype", c_int), ("flags", c_uint32)]
 
 
 class SpecopdError(RuntimeError):
@@ -93,6 +100,7 @@ def _load():
     lib.specopd_gdn_workspace_size.argtypes = [POINTER(GdnDesc), POINTER(c_size_t)]
     lib.specopd_gdn_replay_fwd.argtypes = [POINTER(GdnDesc)] + [P] * 13 + [P, c_size_t, P]
     lib.specopd_gdn_device_status.argtypes = [POINTER(GdnDesc), P, c_size_t, POINTER(c_int32), P]
+    lib.specopd_gdn_conv_fwd.argtypes = [POINTER(GdnConvDesc)] + [P] * 7
     lib.specopd_kernel_timing.argtypes = [c_int]
     lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
@@ -327,6 +335,33 @@ def gdn_replay(inp: dict, C=64, ws=None, out=None):
                            inp["trunk_gate"], inp["trunk_beta"], inp["anchors"], inp["parent"], q, inp["k"],
                            inp["v"], inp["gate"], inp["beta"], out, ws)
     return out, desc, ws
+
+
+def gdn_conv_desc(T, L, B, Wn, H, D, K, dtype, flags=0):
+    return GdnConvDesc(T, L, B, Wn, H, D, K, _DT.get(dtype, dtype) if not isinstance(dtype, int) else dtype,
+                       flags)
+
+
+def specopd_gdn_conv_fwd(desc, trunk_x, x, w, anchors, parent, out, stream=None, raw_status=False):
+    st = LIB.specopd_gdn_conv_fwd(ctypes.byref(desc), _ptr(trunk_x), _ptr(x), _ptr(w), _ptr(anchors),
+                                  _ptr(parent), _ptr(out), _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_gdn_conv_fwd")
+    return out
+
+
+def gdn_conv(trunk_x, x, w, anchors, parent, H, l2norm=False, out=None):
+    """Short convolution of branch-node inputs x [T][B][Wn][H*D] along the
+    parent map, trunk_x [T][L][H*D], w [H*D][K] fp32; returns (out, desc)."""
+    T, B, Wn, C = x.shape
+    desc = gdn_conv_desc(T, trunk_x.shape[1], B, Wn, H, C // H, w.shape[1], x.dtype,
+                         SPECOPD_GDN_CONV_L2NORM if l2norm else 0)
+    if out is None:
+        out = torch.empty_like(x)
+    specopd_gdn_conv_fwd(desc, trunk_x, x, w, anchors, parent, out)
+    return out, desc
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

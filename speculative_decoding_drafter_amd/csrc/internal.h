@@ -198,10 +198,12 @@ struct GdnCallArgs {
   char* ws;
 };
 hipError_t launch_gdn_replay(const specopd_gdn_desc& d, const GdnCallArgs& a, hipStream_t s);
+hipError_t launch_gdn_conv(const specopd_gdn_conv_desc& d, const void* trunk_x, const void* x, const float* w,
+                           const int32_t* anchors, const int32_t* parent, void* out, hipStream_t s);
 
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`
-// (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay) when timing is on;
+// (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution) when timing is on;
 // otherwise does nothing (also for a negative `which`).
 void timing_mark(int which, int phase, hipStream_t s);
 

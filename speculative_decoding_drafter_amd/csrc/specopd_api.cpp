@@ -53,6 +53,21 @@ specopd_status check_gdn_desc(const specopd_gdn_desc* d) {
   return SPECOPD_OK;
 }
 
+specopd_status check_gdn_conv_desc(const specopd_gdn_conv_desc* d) {
+  if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->T < 1 || d->L < 1 || d->B < 1 || d->Wn < 1 || d->H < 1 || d->D < 1 || d->K < 1)
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->dtype != SPECOPD_F32 && d->dtype != SPECOPD_BF16) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if ((d->flags & ~SPECOPD_GDN_CONV_L2NORM) != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->D != 64 && d->D != 128) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->Wn > 64 || d->K > 8) return SPECOPD_ERR_UNSUPPORTED;
+  // grid (one workgroup per node) and element offsets
+  if (double(d->T) * d->B * d->Wn > 2147483647.0 || double(d->T) * d->L >= double(1 << 28) ||
+      double(d->T) * d->L * d->H * d->D > 9.0e15 || double(d->T) * d->B * d->Wn * d->H * d->D > 9.0e15)
+    return SPECOPD_ERR_UNSUPPORTED;
+  return SPECOPD_OK;
+}
+
 specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
   if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->T < 1 || d->L < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
@@ -110,7 +125,7 @@ struct TimingState {
   std::mutex mu;
   bool on = false;
   bool failed = false;
-  std::vector<hipEvent_t> ev[4];  // per call kind: start, stop, start, stop, ...
+  std::vector<hipEvent_t> ev[5];  // per call kind: start, stop, start, stop, ...
   std::vector<hipEvent_t> pool;   // created up front, so recording costs no allocation
   void clear() {
     for (auto& v : ev) {
@@ -131,7 +146,7 @@ namespace specopd {
 void timing_mark(int which, int phase, hipStream_t s) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on || which < 0 || which > 3) return;
+  if (!t.on || which < 0 || which > 4) return;
   auto& v = t.ev[which];
   if (phase == 1 && v.size() % 2 == 0) return;  // no open start
   if (phase == 0 && v.size() % 2 == 1) return;  // already open
@@ -184,7 +199,7 @@ specopd_status specopd_kernel_timing(int enable) {
 }
 
 specopd_status specopd_kernel_time(int which, double* total_ms, int* launches) {
-  if (which < 0 || which > 3 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (which < 0 || which > 4 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   if (t.failed) return SPECOPD_ERR_HIP;
@@ -314,6 +329,21 @@ specopd_status specopd_gdn_replay_fwd(const specopd_gdn_desc* desc, const float*
   a.out = out;
   a.ws = static_cast<char*>(workspace);
   hipError_t e = launch_gdn_replay(*desc, a, stream);
+  return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_gdn_conv_fwd(const specopd_gdn_conv_desc* desc, const void* trunk_x,
+                                    const void* x, const float* w, const int32_t* anchors,
+                                    const int32_t* parent, void* out, hipStream_t stream) {
+  specopd_status st = check_gdn_conv_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const void* ins[] = {trunk_x, x, w, anchors, parent};
+  for (const void* p : ins)
+    if (!p || !aligned16(p) || p == out) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!out || !aligned16(out)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  timing_mark(4, 0, stream);
+  hipError_t e = launch_gdn_conv(*desc, trunk_x, x, w, anchors, parent, out, stream);
+  timing_mark(4, 1, stream);
   return e == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
 }
 

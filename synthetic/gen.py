@@ -39,6 +39,7 @@ _T_DRAFT, _T_TARGET, _T_PERM, _T_PEAK = 11, 12, 13, 14
 _T_PF_Q, _T_PF_K, _T_PF_V = 21, 22, 23
 _T_G_CKPT, _T_G_TK, _T_G_TV, _T_G_TA, _T_G_TB = 31, 32, 33, 34, 35
 _T_G_Q, _T_G_K, _T_G_V, _T_G_A, _T_G_B = 36, 37, 38, 39, 40
+_T_G_CX, _T_G_CTX, _T_G_CW = 41, 42, 43
 
 
 def derive_seed(seed: int, cid: int, tensor: int) -> int:
@@ -223,6 +224,28 @@ def gen_gdn(cfg: GdnConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[s
         "v": _normal((T, B, Wn, H, D), dt, device, g(_T_G_V)),
         "gate": _uniform((T, B, Wn, H), cfg.gate_lo, 1.0, device, g(_T_G_A)),
         "beta": _uniform((T, B, Wn, H), 0.05, 0.95, device, g(_T_G_B)),
+    }
+    anch = anchors_for(cfg, seed, cid)
+    parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()
+    out["anchors"] = torch.from_numpy(anch).to(device)
+    out["parent"] = torch.from_numpy(parent).to(device)
+    return out
+
+
+def gen_gdn_conv(cfg: GdnConfig, seed: int = 0, device="cpu", cid: int = 0, K: int = 4) -> Dict[str, torch.Tensor]:
+    """Inputs of the branch short convolution of one projection (q, k or v).
+
+    trunk_x [T][L][H*D] and x [T][B][Wn][H*D]: N(0,1) projections before the
+    convolution, in cfg.dtype; w [H*D][K] fp32 N(0, 1/K) weights; anchors and
+    parent as gen_gdn draws them (the same seed gives the same tree)."""
+    dt = _DT[cfg.dtype]
+    T, L, B, Wn, C = cfg.T, cfg.L, cfg.B, cfg.Wn, cfg.H * cfg.D
+    g = lambda tid: _gen(device, seed, cid, tid)
+    w = torch.randn((C, K), generator=g(_T_G_CW), device=device, dtype=torch.float32) / float(np.sqrt(K))
+    out = {
+        "trunk_x": _normal((T * L, C), dt, device, g(_T_G_CTX), 8192).view(T, L, C),
+        "x": _normal((T * B * Wn, C), dt, device, g(_T_G_CX), 8192).view(T, B, Wn, C),
+        "w": w,
     }
     anch = anchors_for(cfg, seed, cid)
     parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_flag_constants_match_the_header():
     src = open(HDR).read()
-    for name in ("SPECOPD_TREE_BATCH_INVARIANT", "SPECOPD_E2ETV_DEFER_ALL"):
+    for name in ("SPECOPD_TREE_BATCH_INVARIANT", "SPECOPD_E2ETV_DEFER_ALL", "SPECOPD_GDN_CONV_L2NORM"):
         m = re.search(r"#define\s+" + name + r"\s+(\d+)u", src)
         assert m and int(m.group(1)) == getattr(sd, name), name
 
@@ -345,6 +345,42 @@ def test_gdn_desc_errors(field, value, code):
 ])
 def test_gdn_pointer_errors(over, code):
     assert _gcall(_gdesc(), **over) == code
+
+
+def _cdesc(**kw):
+    base = dict(T=2, L=300, B=4, Wn=7, H=4, D=128, K=4, dtype=sd.SPECOPD_BF16)
+    base.update(kw)
+    return sd.gdn_conv_desc(**base)
+
+
+def _ccall(desc, **over):
+    names = ("trunk_x", "x", "w", "anchors", "parent", "out")
+    args = {n: FAKE + 16 * i for i, n in enumerate(names)}
+    args.update(over)
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_gdn_conv_fwd(ctypes.byref(desc), *[P(args[n]) for n in names], P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 256, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("K", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("K", 9, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("B", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("dtype", 5, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 2, sd.SPECOPD_ERR_INVALID_ARGUMENT),   # only SPECOPD_GDN_CONV_L2NORM is defined
+    ("L", 300_000_000, sd.SPECOPD_ERR_UNSUPPORTED),
+])
+def test_gdn_conv_desc_errors(field, value, code):
+    d = _cdesc()
+    setattr(d, field, value)
+    assert _ccall(d) == code
+
+
+@pytest.mark.parametrize("over", [dict(w=0), dict(parent=0), dict(out=0), dict(x=FAKE + 8),
+                                  dict(out=FAKE + 16)])  # the last: out aliases x
+def test_gdn_conv_pointer_errors(over):
+    assert _ccall(_cdesc(), **over) == sd.SPECOPD_ERR_INVALID_ARGUMENT
 
 
 def test_gdn_workspace_and_short_trunks():
