@@ -43,5 +43,7 @@ def test_kernel_timing_records_each_call(gpu_ok):
     assert sd.specopd_kernel_time(0) == (0.0, 0)
     assert sd.specopd_kernel_time(2) == (0.0, 0)  # prefill: nothing recorded
     assert sd.specopd_kernel_time(3) == (0.0, 0)  # GDN replay: nothing recorded
-    with pytest.raises(sd.SpecopdError):
-        sd.specopd_kernel_time(4)
+    assert sd.specopd_kernel_time(4) == (0.0, 0)  # GDN convolution: nothing recorded
+    for bad in (-1, 99):
+        with pytest.raises(sd.SpecopdError):
+            sd.specopd_kernel_time(bad)
