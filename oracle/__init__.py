@@ -32,6 +32,8 @@ from .prefill import trunk_prefill, trunk_prefill_cache
 from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, replay_span,
                   anchor_state, gdn_branch, gdn_replay, update_counts, conv_history, branch_conv,
                   gdn_branch_conv)
+from .qsa import (rms_norm, compress_group, sequence_group_keys, select_topk, plain_row_select,
+                  branch_group_keys, qsa_branch_select, qsa_select, causal_tail, round_bf16)
 
 __all__ = [
     "rope", "rope_angles", "walk_ancestors", "tree_depths", "check_positions",
@@ -41,4 +43,6 @@ __all__ = [
     "shared_row_count", "trunk_prefill", "trunk_prefill_cache", "gated_delta_update",
     "gdn_read", "run_tokens", "trunk_checkpoints", "replay_span", "anchor_state", "gdn_branch",
     "gdn_replay", "update_counts", "conv_history", "branch_conv", "gdn_branch_conv",
+    "rms_norm", "compress_group", "sequence_group_keys", "select_topk", "plain_row_select",
+    "branch_group_keys", "qsa_branch_select", "qsa_select", "causal_tail", "round_bf16",
 ]

@@ -124,12 +124,39 @@ class GdnConfig:
 
 
 @dataclass(frozen=True)
+class QsaConfig:
+    """Sparse-attention (QSA) block-selection workload: T trunks of length L
+    (first P tokens prompt), B anchored branches per trunk (each a tree of Wn
+    nodes), indexer key size Di, topk groups of 4 tokens kept per node.
+
+    Value laws: raw indexer keys and indexer queries N(0, 1) in bf16; the
+    RMSNorm gain 1 + N(0, 0.1^2) in fp32; the trunk's group-key cache N(0, 1)
+    in bf16 where a test does not build it from the raw keys (a compressed key
+    has unit root-mean-square times the gain, and a Gaussian vector is
+    unchanged in law by the rotation, so the draw has the cache's scale)."""
+
+    T: int
+    L: int
+    P: int
+    B: int
+    parent: Tuple[int, ...]
+    Di: int
+    topk: int
+    dtype: str = "bf16"
+
+    @property
+    def Wn(self) -> int:
+        return len(self.parent)
+
+
+@dataclass(frozen=True)
 class Workload:
     cid: int
     name: str
     attn: Optional[AttnConfig]
     loss: Optional[LossConfig]
     gdn: Optional[GdnConfig] = None
+    qsa: Optional[QsaConfig] = None
 
 
 _C4P, _C4D = chain(4)
@@ -145,6 +172,7 @@ WORKLOADS = {
         AttnConfig(T=1, L=64, P=16, B=4, parent=_C4P, depth=_C4D,
                    Hq=2, Hkv=1, D=64, dtype="f32"),
         LossConfig(R=4, parent=_C4P, V=1000, dtype="f32", recipe="indep", sd=2.0),
+        qsa=QsaConfig(T=1, L=64, P=16, B=4, parent=_C4P, Di=64, topk=4),
     ),
     2: Workload(
         2, "layer8b",
@@ -152,6 +180,7 @@ WORKLOADS = {
                    Hq=32, Hkv=8, D=128, dtype="bf16"),
         LossConfig(R=64, parent=_C8P, V=VOCAB, dtype="bf16", recipe="noise"),
         GdnConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, H=32, D=128, dtype="bf16"),
+        QsaConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, Di=128, topk=64),
     ),
     3: Workload(
         3, "batch8",
@@ -160,6 +189,7 @@ WORKLOADS = {
         LossConfig(R=8 * 128, parent=_C16P, V=VOCAB, dtype="bf16",
                    recipe="rho", sd=3.0, rho=0.8),
         GdnConfig(T=8, L=8192, P=2048, B=128, parent=_C16P, H=32, D=128, dtype="bf16"),
+        QsaConfig(T=8, L=8192, P=2048, B=128, parent=_C16P, Di=128, topk=512),
     ),
     4: Workload(
         4, "loss_stress",
@@ -172,6 +202,7 @@ WORKLOADS = {
                    depth=FORK_DEPTH, Hq=24, Hkv=4, D=256, dtype="bf16"),
         LossConfig(R=512, parent=FORK_PARENT, V=VOCAB, dtype="bf16", recipe="noise"),
         GdnConfig(T=1, L=32768, P=8192, B=512, parent=FORK_PARENT, H=16, D=128, dtype="bf16"),
+        QsaConfig(T=1, L=32768, P=8192, B=512, parent=FORK_PARENT, Di=128, topk=512),
     ),
 }
 
@@ -186,6 +217,10 @@ def shrink_attn(cfg: AttnConfig, **kw) -> AttnConfig:
 
 
 def shrink_loss(cfg: LossConfig, **kw) -> LossConfig:
+    return dataclasses.replace(cfg, **kw)
+
+
+def shrink_qsa(cfg: QsaConfig, **kw) -> QsaConfig:
     return dataclasses.replace(cfg, **kw)
 
 

@@ -29,7 +29,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-from .configs import AttnConfig, GdnConfig, LossConfig
+from .configs import AttnConfig, GdnConfig, LossConfig, QsaConfig
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -40,6 +40,7 @@ _T_PF_Q, _T_PF_K, _T_PF_V = 21, 22, 23
 _T_G_CKPT, _T_G_TK, _T_G_TV, _T_G_TA, _T_G_TB = 31, 32, 33, 34, 35
 _T_G_Q, _T_G_K, _T_G_V, _T_G_A, _T_G_B = 36, 37, 38, 39, 40
 _T_G_CX, _T_G_CTX, _T_G_CW = 41, 42, 43
+_T_Q_TRAW, _T_Q_TGK, _T_Q_X, _T_Q_Y, _T_Q_GAMMA = 51, 52, 53, 54, 55
 
 
 def derive_seed(seed: int, cid: int, tensor: int) -> int:
@@ -251,4 +252,35 @@ def gen_gdn_conv(cfg: GdnConfig, seed: int = 0, device="cpu", cid: int = 0, K: i
     parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()
     out["anchors"] = torch.from_numpy(anch).to(device)
     out["parent"] = torch.from_numpy(parent).to(device)
+    return out
+
+
+def gen_qsa(cfg: QsaConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[str, torch.Tensor]:
+    """QSA block-selection inputs.
+
+    Layouts (row-major): trunk_raw [T][L][Di] and trunk_gk [T][L/4][Di]
+    (bf16); x, y [T][B][Wn][Di] (bf16, the nodes' raw indexer keys and
+    indexer queries); gamma [Di] fp32; anchors [T][B]; parent, pos
+    [T][B][Wn] int32 (pos = anchor + 1 + depth).  trunk_gk is drawn, not
+    computed from trunk_raw (see QsaConfig); a test that needs the two
+    consistent replaces it."""
+    dt = _DT[cfg.dtype]
+    T, L, B, Wn, Di = cfg.T, cfg.L, cfg.B, cfg.Wn, cfg.Di
+    g = lambda tid: _gen(device, seed, cid, tid)
+    out = {
+        "trunk_raw": _normal((T * L, Di), dt, device, g(_T_Q_TRAW), 65536).view(T, L, Di),
+        "trunk_gk": _normal((T * (L // 4), Di), dt, device, g(_T_Q_TGK), 65536).view(T, L // 4, Di),
+        "x": _normal((T * B * Wn, Di), dt, device, g(_T_Q_X), 65536).view(T, B, Wn, Di),
+        "y": _normal((T * B * Wn, Di), dt, device, g(_T_Q_Y), 65536).view(T, B, Wn, Di),
+        "gamma": 1.0 + 0.1 * torch.randn((Di,), generator=g(_T_Q_GAMMA), device=device, dtype=torch.float32),
+    }
+    anch = anchors_for(cfg, seed, cid)
+    parent = np.broadcast_to(np.asarray(cfg.parent, np.int32), (T, B, Wn)).copy()
+    depth = np.zeros(Wn, np.int64)
+    for j, p in enumerate(cfg.parent):
+        depth[j] = 0 if p < 0 else depth[p] + 1
+    pos = (anch[:, :, None].astype(np.int64) + 1 + depth[None, None, :]).astype(np.int32)
+    out["anchors"] = torch.from_numpy(anch).to(device)
+    out["parent"] = torch.from_numpy(parent).to(device)
+    out["pos"] = torch.from_numpy(np.ascontiguousarray(pos)).to(device)
     return out

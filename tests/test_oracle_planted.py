@@ -16,6 +16,7 @@ import oracle
 import test_oracle_e2etv as te
 import test_oracle_gdn as tg
 import test_oracle_prefill as tp
+import test_oracle_qsa as tq
 import test_oracle_tree_attention as tt
 
 # (oracle module, function, text in its source, replacement, pins)
@@ -108,6 +109,31 @@ CASES = {
     "score row of the node itself": (
         "oracle.rows", "score_row_source", 'else ("node", p)', 'else ("node", int(j))',
         [tt.test_fig3_toy_tree]),
+    "boundary group filled with reference tokens after the anchor": (
+        "oracle.qsa", "branch_group_keys", "if q > anchor:", "if q > anchor + GROUP:",
+        [lambda: tq.test_branch_rows_equal_plain_sequence(1),
+         lambda: tq.test_reference_tokens_after_the_anchor_do_not_leak(0)]),
+    "incomplete group is a candidate": (
+        "oracle.qsa", "qsa_branch_select", "G = (p + 1) // GROUP", "G = (p + GROUP) // GROUP",
+        [lambda: tq.test_branch_rows_equal_plain_sequence(2)]),
+    "query read unrotated": (
+        "oracle.qsa", "qsa_branch_select", "s = keys @ rnd(rope(y[j], p, base))", "s = keys @ rnd(y[j])",
+        [lambda: tq.test_branch_rows_equal_plain_sequence(4)]),
+    "branch group rotated at its last token": (
+        "oracle.qsa", "branch_group_keys", "gamma, p - (GROUP - 1), base, eps)",
+        "gamma, p, base, eps)", [tq.test_siblings_share_keys_before_the_fork_only]),
+    "boundary group shifted one trunk token": (
+        "oracle.qsa", "branch_group_keys", "toks.append(trunk_raw[q])", "toks.append(trunk_raw[q - 1])",
+        [tq.test_siblings_share_keys_before_the_fork_only]),
+    "RMSNorm by the sum of squares": (
+        "oracle.qsa", "rms_norm", "np.mean(u * u, axis=-1, keepdims=True)",
+        "np.sum(u * u, axis=-1, keepdims=True)", [tq.test_hand_values_two_dims]),
+    "top-k in score order": (
+        "oracle.qsa", "select_topk", "return np.sort(order[:k])", "return order[:k]",
+        [lambda: tq.test_topk_matches_sorting_rule(3)]),
+    "bf16 rounding ties away from even": (
+        "oracle.qsa", "round_bf16", "b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000",
+        "b = (b + 0x8000) & 0xFFFF0000", [tq.test_round_bf16_ties_to_even]),
 }
 
 
