@@ -20,6 +20,10 @@
  *   specopd_gdn_conv_fwd    that layer's short convolution for branch nodes,
  *                           its history following the branch's ancestors
  *                           (jaehun.me review, §3.2(c)).
+ *   specopd_qsa_trunk_groups_fwd, specopd_qsa_select_fwd
+ *                           block selection of a sparse-attention (QSA)
+ *                           target with branch-consistent indexer groups
+ *                           (jaehun.me review, §3.2(b) and Fig. 4).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -462,6 +466,80 @@ specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
                                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Sparse attention (QSA): block selection with branch-consistent groups     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * A QSA-style sparse layer picks, for each query, blocks of 4 consecutive
+ * tokens ("groups") by a compressed indexer key and reads the top-k of them
+ * (jaehun.me review, §3.2(b) and its Fig. 4 walk-through).  A group's key is
+ * the mean of its 4 tokens' raw indexer keys, RMS-normalised
+ * (u / sqrt(mean(u^2) + eps) * gamma), then rotated (rotate-half, base
+ * rope_base, as for the attention) at the group's first position.  A query
+ * at position p scores every group complete at p, g < floor((p + 1) / 4), by
+ * the dot product of that key with its own indexer query rotated at p; the
+ * k best are kept, ties going to the lower group, and are returned in
+ * increasing group order (all of them when there are at most k).  The tokens
+ * of p's incomplete group are the causal tail that attention reads without
+ * selection.  One indexer head: the selection serves every attention head.
+ *
+ * specopd_qsa_trunk_groups_fwd -- the trunk pass's group cache:
+ *   trunk_raw [T][L][Di] bf16   raw indexer keys of the trunk tokens
+ *   gamma     [Di] fp32         RMSNorm gain
+ *   trunk_gk  [T][L/4][Di] bf16 out: the key of every complete trunk group
+ *
+ * specopd_qsa_select_fwd -- selection for every branch node.  On a branch
+ * with anchor a, groups complete at the anchor (g < floor((a + 1) / 4))
+ * reuse trunk_gk as given; the group holding the anchor, when incomplete,
+ * and every later group are compressed again from the node's own history
+ * (itself, its ancestors, then trunk tokens a, a-1, ...), so reference tokens
+ * after the anchor never enter a key and the sub-branches of a fork keep
+ * groups of their own:
+ *   trunk_gk  [T][L/4][Di] bf16 the trunk's group cache (entries of groups
+ *                               not complete at an anchor are not read)
+ *   trunk_raw [T][L][Di] bf16   trunk raw keys (the boundary groups' tokens)
+ *   x, y      [T][B][Wn][Di] bf16  the nodes' raw indexer keys and their
+ *                               indexer queries (unrotated)
+ *   gamma     [Di] fp32         as above
+ *   anchors [T][B], parent and pos [T][B][Wn] int32   as for tree attention
+ *   sel       [T][B][Wn][topk] int32  out: selected groups, increasing;
+ *                               -1 past the node's number of candidates
+ *   score     [T][B][Wn][topk] fp32   out: their scores; -inf past it
+ *   bkey      [T][B][Wn][Di] bf16 or NULL  out: the key of the group that
+ *                               the node completes (position 3 mod 4), else 0
+ * Scores are fp32 sums of products of the bf16-rounded rotated query and
+ * key (the matrix cores' arithmetic).  A malformed branch (anchor outside
+ * [0, L), a parent that does not precede its child, pos != anchor + 1 +
+ * depth) gets sel = -1, NaN scores and zero bkey rows on every node and is counted in the
+ * workspace (specopd_qsa_device_status).  Pointers 16-byte aligned; outputs
+ * must not alias inputs.  (L + Wn) / 4 above 15360 (a row's candidate
+ * scores are held in LDS) gives SPECOPD_ERR_UNSUPPORTED.
+ */
+typedef struct {
+  int32_t T, L, B, Wn; /* Wn <= 64                                      */
+  int32_t Di;          /* indexer key size: 64, 128 or 256              */
+  int32_t topk;        /* groups kept per node, >= 1                    */
+  float rope_base;     /* <= 0 means 10000                              */
+  float eps;           /* RMSNorm epsilon; <= 0 means 1e-6              */
+  uint32_t flags;      /* 0                                             */
+} specopd_qsa_desc;
+
+specopd_status specopd_qsa_trunk_groups_fwd(const specopd_qsa_desc* desc, const void* trunk_raw,
+                                            const float* gamma, void* trunk_gk, hipStream_t stream);
+specopd_status specopd_qsa_workspace_size(const specopd_qsa_desc* desc, size_t* bytes);
+specopd_status specopd_qsa_select_fwd(const specopd_qsa_desc* desc, const void* trunk_gk,
+                                      const void* trunk_raw, const void* x, const void* y,
+                                      const float* gamma, const int32_t* anchors,
+                                      const int32_t* parent, const int32_t* pos, int32_t* sel,
+                                      float* score, void* bkey, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+/* Waits for the stream; SPECOPD_ERR_DEVICE_VALIDATION with *bad_branches > 0
+ * when the last select call on this workspace found malformed branches. */
+specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const void* workspace,
+                                         size_t workspace_bytes, int32_t* bad_branches,
+                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing, for measurement harnesses.
  *
  * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd,
@@ -470,13 +548,15 @@ specopd_status specopd_e2etv_fwd_bwd_noalloc(const specopd_e2etv_desc* desc,
  * kernel (the attention kernel proper, after the preparation kernel; the
  * E2E-TV kernel, without the small kernel that clears its counters; the
  * attention kernel of each prefilled trunk; the GDN replay kernel, without
- * the one that clears its counter; the GDN convolution kernel), so that a harness can divide a kernel's algorithmic work
+ * the one that clears its counter; the GDN convolution kernel; the QSA
+ * scoring kernel and the QSA top-k kernel), so that a harness can divide a kernel's algorithmic work
  * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is
  * created when timing is switched on and kept for the process).
  *
  * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
- * 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution.  Waits for the recorded events and returns the summed elapsed
+ * 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution, 5 QSA scores,
+ * 6 QSA top-k.  Waits for the recorded events and returns the summed elapsed
  * milliseconds and the number of recorded launches.  Returns
  * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
  * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while

@@ -15,4 +15,6 @@ from ._lib import (  # noqa: F401
     e2etv, PrefillDesc, prefill_desc, specopd_prefill_workspace_size, specopd_prefill_fwd, prefill,
     GdnDesc, gdn_desc, specopd_gdn_workspace_size, specopd_gdn_replay_fwd, specopd_gdn_device_status,
     gdn_replay, GdnConvDesc, gdn_conv_desc, specopd_gdn_conv_fwd, gdn_conv, SPECOPD_GDN_CONV_L2NORM,
+    QsaDesc, qsa_desc, specopd_qsa_trunk_groups_fwd, specopd_qsa_workspace_size, specopd_qsa_select_fwd,
+    specopd_qsa_device_status, qsa_trunk_groups, qsa_select,
 )

@@ -41,6 +41,8 @@ EXPORTS = (
     "specopd_prefill_workspace_size", "specopd_prefill_fwd",
     "specopd_gdn_workspace_size", "specopd_gdn_replay_fwd", "specopd_gdn_device_status",
     "specopd_gdn_conv_fwd",
+    "specopd_qsa_trunk_groups_fwd", "specopd_qsa_workspace_size", "specopd_qsa_select_fwd",
+    "specopd_qsa_device_status",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
@@ -73,6 +75,11 @@ class GdnConvDesc(ctypes.Structure):
                 ("D", c_int32), ("K", c_int32), ("dtype", c_int), ("flags", c_uint32)]
 
 
+class QsaDesc(ctypes.Structure):
+    _fields_ = [("T", c_int32), ("L", c_int32), ("B", c_int32), ("Wn", c_int32), ("Di", c_int32),
+                ("topk", c_int32), ("rope_base", c_float), ("eps", c_float), ("flags", c_uint32)]
+
+
 class SpecopdError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -101,6 +108,10 @@ def _load():
     lib.specopd_gdn_replay_fwd.argtypes = [POINTER(GdnDesc)] + [P] * 13 + [P, c_size_t, P]
     lib.specopd_gdn_device_status.argtypes = [POINTER(GdnDesc), P, c_size_t, POINTER(c_int32), P]
     lib.specopd_gdn_conv_fwd.argtypes = [POINTER(GdnConvDesc)] + [P] * 7
+    lib.specopd_qsa_trunk_groups_fwd.argtypes = [POINTER(QsaDesc), P, P, P, P]
+    lib.specopd_qsa_workspace_size.argtypes = [POINTER(QsaDesc), POINTER(c_size_t)]
+    lib.specopd_qsa_select_fwd.argtypes = [POINTER(QsaDesc)] + [P] * 11 + [P, c_size_t, P]
+    lib.specopd_qsa_device_status.argtypes = [POINTER(QsaDesc), P, c_size_t, POINTER(c_int32), P]
     lib.specopd_kernel_timing.argtypes = [c_int]
     lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
@@ -131,7 +142,8 @@ def specopd_kernel_timing(enable: bool) -> None:
 
 
 def specopd_kernel_time(which: int):
-    """(total ms, launches) recorded for the attention (0), E2E-TV (1) or prefill (2) kernel."""
+    """(total ms, launches) recorded for the attention (0), E2E-TV (1), prefill (2),
+    GDN replay (3), GDN convolution (4), QSA scoring (5) or QSA top-k (6) kernel."""
     ms, n = c_double(0.0), c_int(0)
     st = LIB.specopd_kernel_time(int(which), ctypes.byref(ms), ctypes.byref(n))
     if st != SPECOPD_OK:
@@ -362,6 +374,82 @@ def gdn_conv(trunk_x, x, w, anchors, parent, H, l2norm=False, out=None):
         out = torch.empty_like(x)
     specopd_gdn_conv_fwd(desc, trunk_x, x, w, anchors, parent, out)
     return out, desc
+
+
+def qsa_desc(T, L, B, Wn, Di, topk, rope_base=10000.0, eps=0.0, flags=0):
+    return QsaDesc(T, L, B, Wn, Di, topk, rope_base, eps, flags)
+
+
+def specopd_qsa_trunk_groups_fwd(desc, trunk_raw, gamma, trunk_gk, stream=None, raw_status=False):
+    st = LIB.specopd_qsa_trunk_groups_fwd(ctypes.byref(desc), _ptr(trunk_raw), _ptr(gamma), _ptr(trunk_gk),
+                                          _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_qsa_trunk_groups_fwd")
+    return trunk_gk
+
+
+def specopd_qsa_workspace_size(desc: QsaDesc) -> int:
+    n = c_size_t(0)
+    st = LIB.specopd_qsa_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_qsa_workspace_size")
+    return n.value
+
+
+def specopd_qsa_select_fwd(desc, trunk_gk, trunk_raw, x, y, gamma, anchors, parent, pos, sel, score, bkey,
+                           ws, stream=None, raw_status=False):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = LIB.specopd_qsa_select_fwd(ctypes.byref(desc), _ptr(trunk_gk), _ptr(trunk_raw), _ptr(x), _ptr(y),
+                                    _ptr(gamma), _ptr(anchors), _ptr(parent), _ptr(pos), _ptr(sel),
+                                    _ptr(score), _ptr(bkey), _ptr(ws), c_size_t(nbytes), _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_qsa_select_fwd")
+    return sel, score
+
+
+def specopd_qsa_device_status(desc, workspace, stream=None) -> int:
+    bad = c_int32(0)
+    st = LIB.specopd_qsa_device_status(ctypes.byref(desc), _ptr(workspace),
+                                       c_size_t(workspace.numel() * workspace.element_size()),
+                                       ctypes.byref(bad), _stream(stream))
+    if st not in (SPECOPD_OK, SPECOPD_ERR_DEVICE_VALIDATION):
+        raise SpecopdError(st, "specopd_qsa_device_status")
+    return bad.value
+
+
+def qsa_trunk_groups(trunk_raw, gamma, rope_base=10000.0, eps=0.0, out=None):
+    """Group-key cache [T][L/4][Di] of trunk raw indexer keys trunk_raw
+    [T][L][Di] (bf16), gain gamma [Di] fp32."""
+    T, L, Di = trunk_raw.shape
+    desc = qsa_desc(T, L, 1, 1, Di, 1, rope_base, eps)
+    if out is None:
+        out = torch.empty((T, L // 4, Di), dtype=trunk_raw.dtype, device=trunk_raw.device)
+    specopd_qsa_trunk_groups_fwd(desc, trunk_raw, gamma, out)
+    return out
+
+
+def qsa_select(inp: dict, topk: int, rope_base=10000.0, eps=0.0, ws=None, outs=None, want_bkey=True):
+    """Block selection of every branch node on generated inputs (dict of
+    device tensors: trunk_gk, trunk_raw, x, y, gamma, anchors, parent, pos);
+    returns dict(sel, score, bkey, desc, ws)."""
+    x = inp["x"]
+    T, B, Wn, Di = x.shape
+    L = inp["trunk_raw"].shape[1]
+    desc = qsa_desc(T, L, B, Wn, Di, topk, rope_base, eps)
+    if ws is None:
+        ws = workspace(specopd_qsa_workspace_size(desc), x.device)
+    if outs is None:
+        outs = {"sel": torch.empty((T, B, Wn, topk), dtype=torch.int32, device=x.device),
+                "score": torch.empty((T, B, Wn, topk), dtype=torch.float32, device=x.device),
+                "bkey": torch.empty_like(x) if want_bkey else None}
+    specopd_qsa_select_fwd(desc, inp["trunk_gk"], inp["trunk_raw"], x, inp["y"], inp["gamma"],
+                           inp["anchors"], inp["parent"], inp["pos"], outs["sel"], outs["score"],
+                           outs.get("bkey"), ws)
+    return dict(outs, desc=desc, ws=ws)
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

@@ -201,10 +201,36 @@ hipError_t launch_gdn_replay(const specopd_gdn_desc& d, const GdnCallArgs& a, hi
 hipError_t launch_gdn_conv(const specopd_gdn_conv_desc& d, const void* trunk_x, const void* x, const float* w,
                            const int32_t* anchors, const int32_t* parent, void* out, hipStream_t s);
 
+// ---------------------------------------------------------------- QSA selection
+// Workspace layout (offsets in bytes, each 256-aligned):
+//   bad    int32  [1]           malformed branches of the last select call
+//   ncand  int32  [T*B*Wn]      candidate groups of every node (-1: malformed)
+//   sc     fp32   [T*B*Wn][Gs]  every candidate's score, Gs >= (L + Wn) / 4
+struct QsaWs {
+  size_t bad, ncand, sc, total;
+  int Gs;
+};
+QsaWs qsa_ws_layout(const specopd_qsa_desc& d);
+constexpr int kQsaMaxCand = 15360;  // a row's scores in LDS: 60 KiB
+struct QsaCallArgs {
+  const void *trunk_gk, *trunk_raw, *x, *y;
+  const float* gamma;
+  const int32_t *anchors, *parent, *pos;
+  int32_t* sel;
+  float* score;
+  void* bkey;
+  char* ws;
+};
+hipError_t launch_qsa_trunk_groups(const specopd_qsa_desc& d, const void* raw, const float* gamma, void* gk,
+                                   hipStream_t s);
+hipError_t launch_qsa_select(const specopd_qsa_desc& d, const QsaCallArgs& a, hipStream_t s);
+
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`
-// (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution) when timing is on;
+// (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution,
+// 5 QSA scores, 6 QSA top-k) when timing is on;
 // otherwise does nothing (also for a negative `which`).
+constexpr int kTimingKinds = 7;
 void timing_mark(int which, int phase, hipStream_t s);
 
 }  // namespace specopd

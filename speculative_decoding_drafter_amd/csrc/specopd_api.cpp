@@ -68,6 +68,23 @@ specopd_status check_gdn_conv_desc(const specopd_gdn_conv_desc* d) {
   return SPECOPD_OK;
 }
 
+specopd_status check_qsa_desc(const specopd_qsa_desc* d) {
+  if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->T < 1 || d->L < 1 || d->B < 1 || d->Wn < 1 || d->Di < 1 || d->topk < 1)
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(d->rope_base) && isfinite(d->eps))) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->Di != 64 && d->Di != 128 && d->Di != 256) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->Wn > 64) return SPECOPD_ERR_UNSUPPORTED;
+  if ((double(d->L) + d->Wn) / 4.0 > double(kQsaMaxCand)) return SPECOPD_ERR_UNSUPPORTED;
+  // grids (one workgroup per branch, one per node) and element offsets
+  const double rows = double(d->T) * d->B * d->Wn;
+  if (rows > 2147483647.0 || rows * d->topk > 9.0e15 || rows * (double(d->L) + d->Wn) > 9.0e15 ||
+      double(d->T) * d->L * d->Di > 9.0e15 || rows * d->Di > 9.0e15)
+    return SPECOPD_ERR_UNSUPPORTED;
+  return SPECOPD_OK;
+}
+
 specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
   if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->T < 1 || d->L < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
@@ -125,7 +142,7 @@ struct TimingState {
   std::mutex mu;
   bool on = false;
   bool failed = false;
-  std::vector<hipEvent_t> ev[5];  // per call kind: start, stop, start, stop, ...
+  std::vector<hipEvent_t> ev[kTimingKinds];  // per call kind: start, stop, start, stop, ...
   std::vector<hipEvent_t> pool;   // created up front, so recording costs no allocation
   void clear() {
     for (auto& v : ev) {
@@ -146,7 +163,7 @@ namespace specopd {
 void timing_mark(int which, int phase, hipStream_t s) {
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  if (!t.on || which < 0 || which > 4) return;
+  if (!t.on || which < 0 || which >= kTimingKinds) return;
   auto& v = t.ev[which];
   if (phase == 1 && v.size() % 2 == 0) return;  // no open start
   if (phase == 0 && v.size() % 2 == 1) return;  // already open
@@ -199,7 +216,7 @@ specopd_status specopd_kernel_timing(int enable) {
 }
 
 specopd_status specopd_kernel_time(int which, double* total_ms, int* launches) {
-  if (which < 0 || which > 4 || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (which < 0 || which >= kTimingKinds || !total_ms || !launches) return SPECOPD_ERR_INVALID_ARGUMENT;
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   if (t.failed) return SPECOPD_ERR_HIP;
@@ -356,6 +373,73 @@ specopd_status specopd_gdn_device_status(const specopd_gdn_desc* desc, const voi
   int32_t bad = 0;
   if (hipStreamSynchronize(stream) != hipSuccess) return SPECOPD_ERR_HIP;
   if (hipMemcpy(&bad, workspace, sizeof(bad), hipMemcpyDeviceToHost) != hipSuccess) return SPECOPD_ERR_HIP;
+  if (bad_branches) *bad_branches = bad;
+  return bad != 0 ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
+}
+
+specopd_status specopd_qsa_trunk_groups_fwd(const specopd_qsa_desc* desc, const void* trunk_raw,
+                                            const float* gamma, void* trunk_gk, hipStream_t stream) {
+  specopd_status st = check_qsa_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!trunk_raw || !gamma || !trunk_gk) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!aligned16(trunk_raw) || !aligned16(gamma) || !aligned16(trunk_gk)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (trunk_gk == trunk_raw || trunk_gk == gamma) return SPECOPD_ERR_INVALID_ARGUMENT;
+  return launch_qsa_trunk_groups(*desc, trunk_raw, gamma, trunk_gk, stream) == hipSuccess ? SPECOPD_OK
+                                                                                           : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_qsa_workspace_size(const specopd_qsa_desc* desc, size_t* bytes) {
+  specopd_status st = check_qsa_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!bytes) return SPECOPD_ERR_INVALID_ARGUMENT;
+  *bytes = qsa_ws_layout(*desc).total;
+  return SPECOPD_OK;
+}
+
+specopd_status specopd_qsa_select_fwd(const specopd_qsa_desc* desc, const void* trunk_gk,
+                                      const void* trunk_raw, const void* x, const void* y,
+                                      const float* gamma, const int32_t* anchors,
+                                      const int32_t* parent, const int32_t* pos, int32_t* sel,
+                                      float* score, void* bkey, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  specopd_status st = check_qsa_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const void* ins[] = {trunk_gk, trunk_raw, x, y, gamma, anchors, parent, pos};
+  const void* outs[] = {sel, score, bkey};
+  for (const void* p : ins)
+    if (!p || !aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!sel || !score) return SPECOPD_ERR_INVALID_ARGUMENT;
+  for (const void* o : outs) {
+    if (!o) continue;
+    if (!aligned16(o)) return SPECOPD_ERR_INVALID_ARGUMENT;
+    for (const void* p : ins)
+      if (p == o) return SPECOPD_ERR_INVALID_ARGUMENT;
+  }
+  if (sel == static_cast<void*>(score) || bkey == static_cast<void*>(sel) || bkey == static_cast<void*>(score))
+    return SPECOPD_ERR_INVALID_ARGUMENT;
+  const QsaWs w = qsa_ws_layout(*desc);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  QsaCallArgs a{};
+  a.trunk_gk = trunk_gk; a.trunk_raw = trunk_raw;
+  a.x = x; a.y = y;
+  a.gamma = gamma;
+  a.anchors = anchors; a.parent = parent; a.pos = pos;
+  a.sel = sel; a.score = score; a.bkey = bkey;
+  a.ws = static_cast<char*>(workspace);
+  return launch_qsa_select(*desc, a, stream) == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const void* workspace,
+                                         size_t workspace_bytes, int32_t* bad_branches,
+                                         hipStream_t stream) {
+  specopd_status st = check_qsa_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const QsaWs w = qsa_ws_layout(*desc);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  int32_t bad = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SPECOPD_ERR_HIP;
+  if (hipMemcpy(&bad, static_cast<const char*>(workspace) + w.bad, sizeof(bad), hipMemcpyDeviceToHost) != hipSuccess)
+    return SPECOPD_ERR_HIP;
   if (bad_branches) *bad_branches = bad;
   return bad != 0 ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
 }

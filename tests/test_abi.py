@@ -390,3 +390,78 @@ def test_gdn_workspace_and_short_trunks():
     bad = ctypes.c_int32(0)
     assert sd.LIB.specopd_gdn_device_status(ctypes.byref(d), ctypes.c_void_p(None), 0, ctypes.byref(bad),
                                             None) == sd.SPECOPD_ERR_WORKSPACE
+
+
+def _qdesc(**kw):
+    base = dict(T=2, L=4096, B=8, Wn=10, Di=128, topk=64)
+    base.update(kw)
+    return sd.qsa_desc(**base)
+
+
+_QNAMES = ("trunk_gk", "trunk_raw", "x", "y", "gamma", "anchors", "parent", "pos", "sel", "score", "bkey")
+
+
+def _qcall(desc, ws_bytes=None, **over):
+    args = {n: FAKE + 16 * i for i, n in enumerate(_QNAMES)}
+    args["ws"] = FAKE + 4096
+    args.update(over)
+    if ws_bytes is None:
+        try:
+            ws_bytes = sd.specopd_qsa_workspace_size(desc)
+        except sd.SpecopdError:
+            ws_bytes = 1 << 40
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_qsa_select_fwd(ctypes.byref(desc), *[P(args[n]) for n in _QNAMES], P(args["ws"]),
+                                         ctypes.c_size_t(ws_bytes), P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("Di", 96, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("Di", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("topk", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("B", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("L", 61_440 - 9, sd.SPECOPD_ERR_UNSUPPORTED),    # (L + Wn) / 4 above the LDS bound
+    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("rope_base", float("inf"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+])
+def test_qsa_desc_errors(field, value, code):
+    d = _qdesc()
+    setattr(d, field, value)
+    assert _qcall(d) == code
+
+
+def test_qsa_largest_supported_trunk():
+    d = _qdesc(L=61_440 - 10, T=1, B=1)
+    assert sd.specopd_qsa_workspace_size(d) > 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(trunk_gk=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(gamma=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(sel=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(score=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(y=FAKE + 8), sd.SPECOPD_ERR_INVALID_ARGUMENT),       # misaligned
+    (dict(sel=FAKE + 16), sd.SPECOPD_ERR_INVALID_ARGUMENT),    # sel aliases trunk_raw
+    (dict(bkey=FAKE + 16 * 9), sd.SPECOPD_ERR_INVALID_ARGUMENT),  # bkey aliases score
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+    (dict(ws=FAKE + 4100), sd.SPECOPD_ERR_WORKSPACE),          # misaligned workspace
+])
+def test_qsa_pointer_errors(over, code):
+    assert _qcall(_qdesc(), **over) == code
+
+
+def test_qsa_workspace_and_status_errors():
+    d = _qdesc()
+    need = sd.specopd_qsa_workspace_size(d)
+    # scores of every node's candidates: rows x (L + Wn) / 4 floats, plus counts
+    assert need >= 2 * 8 * 10 * ((4096 + 10) // 4) * 4
+    assert _qcall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+    bad = ctypes.c_int32(0)
+    assert sd.LIB.specopd_qsa_device_status(ctypes.byref(d), ctypes.c_void_p(None), 0, ctypes.byref(bad),
+                                            None) == sd.SPECOPD_ERR_WORKSPACE
+    P = ctypes.c_void_p
+    assert sd.LIB.specopd_qsa_trunk_groups_fwd(ctypes.byref(d), P(FAKE), P(0), P(FAKE + 32), P(None)) \
+        == sd.SPECOPD_ERR_INVALID_ARGUMENT
+    assert sd.LIB.specopd_qsa_trunk_groups_fwd(ctypes.byref(d), P(FAKE), P(FAKE + 16), P(FAKE), P(None)) \
+        == sd.SPECOPD_ERR_INVALID_ARGUMENT  # out aliases the raw keys
