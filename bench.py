@@ -21,7 +21,9 @@ sources.  `other_workloads` repeats the measurement for the --also
 workloads.  `prefill` measures, separately, the trunk prefill that fills the
 cache (specopd_prefill_fwd) on the workload's trunks, and `gdn` the branch
 scoring of a linear-attention (GDN) target by indexed state replay
-(specopd_gdn_replay_fwd) on the workload's trunks and tree.  `cpu_baseline` times
+(specopd_gdn_replay_fwd) on the workload's trunks and tree, and `qsa` the block
+selection of a sparse-attention (QSA) target with branch-consistent indexer
+groups (specopd_qsa_select_fwd).  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same workload, on one core and
 on every usable core (reported, not a target).
 """
@@ -294,6 +296,84 @@ def _cpu_init_probe(i):
     return i
 
 
+def bench_qsa(sd, wl, seed, steps, warmup, dev, stream):
+    """Block selection of a sparse-attention (QSA) target with
+    branch-consistent indexer groups (specopd_qsa_select_fwd) on the
+    workload's trunks and tree, timed on its own: the scoring step's
+    counterpart for QSA layers.  Per launch, the scoring kernel forms one dot
+    product of Di per candidate (every group complete at a node's position)
+    and writes the candidate's fp32 score; the top-k kernel reads those
+    scores back and writes k (index, score) pairs per node."""
+    import numpy as np
+    import torch
+    from synthetic import gen_qsa
+    qc = wl.qsa
+    qi = gen_qsa(qc, seed, device=dev, cid=wl.cid)
+    out = sd.qsa_select(qi, qc.topk, want_bkey=False)
+
+    def call():
+        sd.qsa_select(qi, qc.topk, ws=out["ws"], outs=out)
+
+    for _ in range(max(1, warmup)):
+        call()
+    n = max(1, min(steps, 20))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / n
+    sd.specopd_kernel_timing(True)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    t5, c5 = sd.specopd_kernel_time(5)
+    t6, c6 = sd.specopd_kernel_time(6)
+    sd.specopd_kernel_timing(False)
+    if sd.specopd_qsa_device_status(out["desc"], out["ws"]) != 0:
+        raise SystemExit("QSA selection reported malformed branches")
+    score_ms, topk_ms = t5 / c5, t6 / c6
+    pos = qi["pos"].cpu().numpy().astype(np.int64)
+    cand = float(((pos + 1) // 4).sum())
+    rows = qc.T * qc.B * qc.Wn
+    fl = 2.0 * qc.Di * cand
+    score_bytes = 4.0 * cand + 2.0 * qc.T * (qc.L // 4) * qc.Di + 4.0 * rows * qc.Di
+    topk_bytes = 4.0 * cand + 8.0 * rows * qc.topk
+    ps = profile_summary(f"qsa_score_{wl.name}", QSA_SRC)
+    pt = profile_summary(f"qsa_topk_{wl.name}", QSA_SRC)
+
+    def roof(kind, ms, nbytes, prof, kernel):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        t = _counter(prof, "hbm_bytes_per_launch")
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS,
+                "traffic": None if t is None else t / (ms / 1e3) / 1e9, "traffic_unit": "GB/s",
+                "traffic_bytes_per_launch": t, "valu_busy_pct": _counter(prof, "valu_busy_pct"),
+                "kernel": kernel, "ms": ms, "alg_bytes_per_launch": nbytes}
+
+    rs = roof("score", score_ms, score_bytes, ps, "qsa_score_kernel (specopd_qsa_select_fwd)")
+    rs["mfma_tflops"] = fl / (score_ms / 1e3) / 1e12
+    rs["mfma_frac"] = rs["mfma_tflops"] / BF16_PEAK_TFLOPS
+    rs["alg_flops_per_launch"] = fl
+    rt = roof("topk", topk_ms, topk_bytes, pt, "qsa_topk_kernel (specopd_qsa_select_fwd)")
+    rt["candidates_per_s"] = cand / (topk_ms / 1e3)
+    res = {
+        "metric": "QSA branch rows/s (block selection, branch-consistent groups)",
+        "value": rows / (call_ms / 1e3), "unit": "rows/s", "calls": n, "call_ms": call_ms,
+        "candidates_per_row": cand / rows,
+        "config": {"T": qc.T, "L": qc.L, "B": qc.B, "Wn": qc.Wn, "Di": qc.Di, "topk": qc.topk,
+                   "dtype": qc.dtype},
+        "roofline": rt if topk_ms >= score_ms else rs,
+        "roofline_score": rs, "roofline_topk": rt,
+    }
+    del qi, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def profile_summary(tag, src_files):
     """Key/value lines of profiles/<tag>.txt when the kernel sources it names
     are unchanged since it was taken (its source_sha256), else None."""
@@ -321,6 +401,12 @@ LOSS_SRC = ["speculative_decoding_drafter_amd/csrc/e2etv.hip",
             "speculative_decoding_drafter_amd/csrc/internal.h",
             "speculative_decoding_drafter_amd/build.py"]
 GDN_SRC = ["speculative_decoding_drafter_amd/csrc/gdn.hip",
+           "speculative_decoding_drafter_amd/csrc/device_common.h",
+           "speculative_decoding_drafter_amd/csrc/internal.h",
+           "speculative_decoding_drafter_amd/build.py"]
+
+
+QSA_SRC = ["speculative_decoding_drafter_amd/csrc/qsa.hip",
            "speculative_decoding_drafter_amd/csrc/device_common.h",
            "speculative_decoding_drafter_amd/csrc/internal.h",
            "speculative_decoding_drafter_amd/build.py"]
@@ -505,6 +591,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=16.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN branch-replay measurement")
+    ap.add_argument("--no-qsa", action="store_true", help="skip the QSA block-selection measurement")
     ap.add_argument("--eager", action="store_true",
                     help="time plain calls instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -543,6 +630,8 @@ def main():
                                        torch.cuda.current_stream())
     if wl.gdn is not None and not args.no_gdn:
         res["gdn"] = bench_gdn(sd, wl, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
+    if wl.qsa is not None and not args.no_qsa:
+        res["qsa"] = bench_qsa(sd, wl, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
     others = {}
     for c in [int(x) for x in args.also.split(",") if x.strip()]:
         if c == args.workload:

@@ -14,7 +14,8 @@
 //
 // Kernels:
 //   qsa_trunk_groups_kernel  one wave per trunk group: the trunk pass's cache.
-//   qsa_score_kernel         one workgroup per branch: validates the tree,
+//   qsa_score_kernel         a few workgroups per branch (each every
+//                            nsplit-th trunk tile): validates the tree,
 //                            rotates the nodes' queries (bf16, LDS),
 //                            compresses the groups its nodes complete (one
 //                            wave per node; the boundary group's trunk tokens
@@ -47,6 +48,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr int kGroup = 4;
+// workgroups the scoring kernel aims for (branches x splits); measured: more
+// splits add their own prologues (tree walk, query rotation) for little gain
+constexpr long long kQsaScoreWgs = 1024;
 
 struct QsaKArgs {
   const uint16_t *trunk_gk, *trunk_raw, *x, *y;
@@ -59,17 +63,25 @@ struct QsaKArgs {
   int32_t* ncand;  // [rows] candidates of every node, -1 for a malformed branch
   float* sc;       // [rows][Gs] candidate scores
   int L, B, Wn, ng, Gs, topk;
+  int nsplit;  // workgroups per branch, each taking every nsplit-th trunk tile
   double log2_base;
   float eps;
 };
 
-// cos and sin of pos * base^(-2i/Di), the angle formed and reduced in fp64
-__device__ __forceinline__ void rot_cs(int pos, int i, int Di, double log2_base, float& c, float& s) {
-  const double ang = double(pos) * exp2(-(2.0 * i / Di) * log2_base);
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  c = float(cs);
-  s = float(sn);
+// Rotation frequencies theta_i = base^(-2i/Di), i < Di/2, in fp64 into an
+// LDS table (by the whole workgroup; a barrier must follow).
+template <int DI>
+__device__ __forceinline__ void fill_theta(double* s_theta, double log2_base) {
+  for (int i = threadIdx.x; i < DI / 2; i += blockDim.x) s_theta[i] = exp2(-(2.0 * i / DI) * log2_base);
+}
+
+// cos and sin of pos * theta: the angle formed and reduced modulo 2 pi in
+// fp64 (2 pi in two parts), then the fp32 functions on [-pi, pi]
+__device__ __forceinline__ void rot_cs(int pos, double theta, float& c, float& s) {
+  const double ang = double(pos) * theta;
+  const double k = rint(ang * 0.15915494309189535);  // 1 / (2 pi)
+  const double r = __builtin_fma(-k, 2.4492935982947064e-16, __builtin_fma(-k, 6.283185307179586, ang));
+  sincosf(float(r), &s, &c);
 }
 
 // One wave compresses one group: the four rows r[0..3] (bf16, DI values,
@@ -78,7 +90,7 @@ __device__ __forceinline__ void rot_cs(int pos, int i, int Di, double log2_base,
 // Lane l owns the pairs l, l + 64, ...
 template <int DI>
 __device__ void compress_group_wave(const uint16_t* const (&r)[kGroup], const float* __restrict__ gamma,
-                                    int first, double log2_base, float eps, uint16_t* out) {
+                                    int first, const double* s_theta, float eps, uint16_t* out) {
   constexpr int H = DI / 2, NP = (H + 63) / 64;
   const int lane = threadIdx.x & 63;
   float u1[NP], u2[NP];
@@ -107,7 +119,7 @@ __device__ void compress_group_wave(const uint16_t* const (&r)[kGroup], const fl
     if (i < H) {
       const float v1 = u1[m] * inv * gamma[i], v2 = u2[m] * inv * gamma[i + H];
       float c, s;
-      rot_cs(first, i, DI, log2_base, c, s);
+      rot_cs(first, s_theta[i], c, s);
       out[i] = f32_to_bf16(v1 * c - v2 * s);
       out[i + H] = f32_to_bf16(v2 * c + v1 * s);
     }
@@ -119,12 +131,15 @@ __global__ __launch_bounds__(256) void qsa_trunk_groups_kernel(const uint16_t* _
                                                                const float* __restrict__ gamma,
                                                                uint16_t* __restrict__ gk, int T, int L, int ng,
                                                                double log2_base, float eps) {
+  __shared__ double s_theta[DI / 2];
+  fill_theta<DI>(s_theta, log2_base);
+  __syncthreads();
   const long long gid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * ng + g
   if (gid >= (long long)T * ng) return;                                  // whole waves
   const int t = int(gid / ng), g = int(gid - (long long)t * ng);
   const uint16_t* b0 = raw + (size_t(t) * L + size_t(kGroup) * g) * DI;
   const uint16_t* r[kGroup] = {b0, b0 + DI, b0 + 2 * DI, b0 + 3 * DI};
-  compress_group_wave<DI>(r, gamma, kGroup * g, log2_base, eps, gk + size_t(gid) * DI);
+  compress_group_wave<DI>(r, gamma, kGroup * g, s_theta, eps, gk + size_t(gid) * DI);
 }
 
 __global__ void qsa_zero_kernel(int32_t* bad) { *bad = 0; }
@@ -140,9 +155,11 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t qsa_smem[];
   __shared__ int s_par[64], s_pos[64];
   __shared__ unsigned char s_at[64][64];  // s_at[j][d]: j's ancestor at depth d (self at depth(j))
+  __shared__ double s_theta[H];
   __shared__ int s_ok;
 
-  const int tb = blockIdx.x;  // t * B + b
+  const int tb = blockIdx.x / a.nsplit;  // t * B + b
+  const int split = blockIdx.x - tb * a.nsplit;
   const int t = tb / a.B;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Wn = a.Wn, Wp = (Wn + 31) & ~31;
@@ -152,6 +169,7 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
   const size_t node0 = size_t(tb) * Wn;
 
   if (tid == 0) s_ok = (anchor >= 0 && anchor < a.L) ? 1 : 0;
+  fill_theta<DI>(s_theta, a.log2_base);
   if (tid < Wn) {
     s_par[tid] = a.parent[node0 + tid];
     s_pos[tid] = a.pos[node0 + tid];
@@ -182,6 +200,7 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
   }
   __syncthreads();
   if (!s_ok) {
+    if (split != 0) return;  // the branch's first workgroup reports it
     if (tid == 0) atomicAdd(a.bad, 1);
     if (tid < Wn) a.ncand[node0 + tid] = -1;
     if (a.bkey)
@@ -190,25 +209,33 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
   }
 
   // rotated queries, bf16 (the operands the matrix cores see); zero rows pad
-  // the last block of 32
-  for (int e = tid; e < Wp * H; e += 256) {
-    const int j = e / H, i = e - j * H;
-    float r1 = 0.f, r2 = 0.f;
+  // the last block of 32.  A thread takes 8 pairs (i, i + H) of one node,
+  // read as two 16-byte loads.
+  for (int e = tid; e < Wp * (H / 8); e += 256) {
+    const int j = e / (H / 8), i0 = (e - j * (H / 8)) * 8;
+    u32x4 w1 = {0u, 0u, 0u, 0u}, w2 = {0u, 0u, 0u, 0u};
     if (j < Wn) {
       const uint16_t* yr = a.y + (node0 + j) * DI;
-      const float y1 = bf16_to_f32(yr[i]), y2 = bf16_to_f32(yr[i + H]);
-      float c, s;
-      rot_cs(s_pos[j], i, DI, a.log2_base, c, s);
-      r1 = y1 * c - y2 * s;
-      r2 = y2 * c + y1 * s;
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(yr + i0);
+      const u32x4 v2 = *reinterpret_cast<const u32x4*>(yr + i0 + H);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float c0, s0, c1, s1;
+        rot_cs(s_pos[j], s_theta[i0 + 2 * q], c0, s0);
+        rot_cs(s_pos[j], s_theta[i0 + 2 * q + 1], c1, s1);
+        const float a0 = bf16_lo(v1[q]), a1 = bf16_hi(v1[q]), b0 = bf16_lo(v2[q]), b1 = bf16_hi(v2[q]);
+        w1[q] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+        w2[q] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+      }
     }
-    sy[j * SY + i] = f32_to_bf16(r1);
-    sy[j * SY + i + H] = f32_to_bf16(r2);
+    *reinterpret_cast<u32x4*>(sy + j * SY + i0) = w1;
+    *reinterpret_cast<u32x4*>(sy + j * SY + i0 + H) = w2;
   }
   // keys of the groups the nodes complete: the four tokens ending at the
   // node along its own path, trunk tokens up to the anchor for the boundary
-  // group (the branch's raw slots)
-  for (int j = wave; j < Wn; j += 4) {
+  // group (the branch's raw slots); the branch's first workgroup scores the
+  // branch's own groups, the others only trunk groups
+  for (int j = wave; j < Wn && split == 0; j += 4) {
     const int p = s_pos[j];
     if ((p & 3) != 3) continue;
     const uint16_t* r[kGroup];
@@ -218,10 +245,10 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
       r[m] = q > anchor ? a.x + (node0 + s_at[j][q - anchor - 1]) * DI
                         : a.trunk_raw + (size_t(t) * a.L + q) * DI;
     }
-    compress_group_wave<DI>(r, a.gamma, p - 3, a.log2_base, a.eps, sk + j * DI);
+    compress_group_wave<DI>(r, a.gamma, p - 3, s_theta, a.eps, sk + j * DI);
   }
   __syncthreads();
-  if (a.bkey)
+  if (a.bkey && split == 0)
     for (int e = tid; e < Wn * DI; e += 256) {
       const int j = e / DI;
       a.bkey[node0 * DI + e] = (s_pos[j] & 3) == 3 ? sk[e] : (uint16_t)0;
@@ -244,18 +271,27 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
         qop[rb][s] = rb < nb ? *reinterpret_cast<const bf16x8*>(sy + (rb * 32 + r32) * SY + 16 * s + 8 * h)
                              : bf16x8{};
     const uint16_t* gkt = a.trunk_gk + size_t(t) * a.ng * DI;
-    for (int tt = wave; tt < ntile; tt += 4) {
+    // tiles split + nsplit * (wave + 4 m); the next tile's keys are loaded
+    // while the current one is multiplied
+    const int tstep = 4 * a.nsplit;
+    auto load_tile = [&](int tt, bf16x8(&kop)[NS]) {
       const int g = min(tt * 32 + r32, a.ng - 1);  // gT <= ng, so ng >= 1 here
       const bf16x8* src = reinterpret_cast<const bf16x8*>(gkt + size_t(g) * DI + 8 * h);
-      bf16x8 kop[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) kop[s] = src[2 * s];
+      for (int s2 = 0; s2 < NS; ++s2) kop[s2] = src[2 * s2];
+    };
+    int tt = split + a.nsplit * wave;
+    bf16x8 kcur[NS], knext[NS];
+    if (tt < ntile) load_tile(tt, kcur);
+    for (; tt < ntile; tt += tstep) {
+      if (tt + tstep < ntile) load_tile(tt + tstep, knext);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         if (rb >= nb) break;
         f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < NS; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s], qop[rb][s], acc, 0, 0, 0);
+        for (int s2 = 0; s2 < NS; ++s2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[s2], qop[rb][s2], acc, 0, 0, 0);
         const int row = rb * 32 + r32;
         if (row < Wn) {
           float* dst = sc0 + size_t(row) * a.Gs;
@@ -272,10 +308,13 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
           }
         }
       }
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) kcur[s2] = knext[s2];
     }
   }
   // the branch's own groups g in [gT, G_j): the key the ancestor at position
   // 4g + 3 completed
+  if (split != 0) return;
   const int maxnb = (Wn + 3) / 4 + 1;
   for (int it = wave; it < Wn * maxnb; it += 4) {
     const int j = it / maxnb, g = gT + (it - j * maxnb);
@@ -330,7 +369,20 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
     }
     return;
   }
-  for (int i = tid; i < n; i += 256) qsa_keys[i] = order_key(sc[i]);
+  constexpr int kLoadBatch = 8;  // loads in flight per thread
+  for (int i0 = tid; i0 < n; i0 += 256 * kLoadBatch) {
+    float v[kLoadBatch];
+#pragma unroll
+    for (int e = 0; e < kLoadBatch; ++e) {
+      const int i = i0 + 256 * e;
+      v[e] = i < n ? sc[i] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < kLoadBatch; ++e) {
+      const int i = i0 + 256 * e;
+      if (i < n) qsa_keys[i] = order_key(v[e]);
+    }
+  }
   // the k-th largest key, 8 bits at a time from the top
   uint32_t prefix = 0u, pmask = 0u, rem = uint32_t(k);
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -406,6 +458,17 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
   }
 }
 
+// Statically declared LDS of the two kernels (bytes), for the dynamic limit.
+constexpr size_t kScoreStaticLds = 6656;   // s_par, s_pos, s_at, s_theta, s_ok (<= 5,648 bytes as built) and room
+constexpr size_t kTopkStaticLds = 1536;    // hist, s_cnt, s_dig, s_rem (1,064 bytes as built) and room
+
+// Raises a kernel's dynamic LDS limit when static + dynamic LDS passes the
+// 64 KiB a workgroup gets without asking (gfx950 has 160 KiB per CU).
+hipError_t allow_lds(const void* kernel, size_t dyn, size_t stat) {
+  if (dyn + stat <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, int(dyn));
+}
+
 template <int DI>
 size_t score_lds_bytes(int Wn) {
   const int Wp = (Wn + 31) & ~31;
@@ -415,13 +478,10 @@ size_t score_lds_bytes(int Wn) {
 template <int DI>
 hipError_t launch_select_di(const specopd_qsa_desc& d, const QsaKArgs& k, hipStream_t s) {
   const size_t lds = score_lds_bytes<DI>(d.Wn);
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qsa_score_kernel<DI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&qsa_score_kernel<DI>), lds, kScoreStaticLds);
+  if (e != hipSuccess) return e;
   timing_mark(5, 0, s);
-  qsa_score_kernel<DI><<<dim3(unsigned(size_t(d.T) * d.B)), 256, lds, s>>>(k);
+  qsa_score_kernel<DI><<<dim3(unsigned(size_t(d.T) * d.B * k.nsplit)), 256, lds, s>>>(k);
   timing_mark(5, 1, s);
   return hipGetLastError();
 }
@@ -478,6 +538,12 @@ hipError_t launch_qsa_select(const specopd_qsa_desc& d, const QsaCallArgs& a, hi
   k.ng = d.L / kGroup;
   k.Gs = w.Gs;
   k.topk = d.topk;
+  // enough workgroups to fill the GPU several times over: the longest
+  // branch's trunk tiles, not the branch count, set the kernel's length
+  {
+    const long long br = (long long)d.T * d.B;
+    k.nsplit = int(std::min<long long>(8, std::max<long long>(1, (kQsaScoreWgs + br - 1) / br)));
+  }
   k.log2_base = log2(double(d.rope_base > 0.f ? d.rope_base : 10000.f));
   k.eps = d.eps > 0.f ? d.eps : 1e-6f;
   qsa_zero_kernel<<<1, 1, 0, s>>>(k.bad);
@@ -488,6 +554,8 @@ hipError_t launch_qsa_select(const specopd_qsa_desc& d, const QsaCallArgs& a, hi
   else e = launch_select_di<256>(d, k, s);
   if (e != hipSuccess) return e;
   const size_t rows = size_t(d.T) * d.B * d.Wn;
+  e = allow_lds(reinterpret_cast<const void*>(&qsa_topk_kernel), size_t(w.Gs) * 4, kTopkStaticLds);
+  if (e != hipSuccess) return e;
   timing_mark(6, 0, s);
   qsa_topk_kernel<<<dim3(unsigned(rows)), 256, size_t(w.Gs) * 4, s>>>(k);
   timing_mark(6, 1, s);
