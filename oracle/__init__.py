@@ -34,6 +34,7 @@ from .gdn import (gated_delta_update, gdn_read, run_tokens, trunk_checkpoints, r
                   gdn_branch_conv)
 from .qsa import (rms_norm, compress_group, sequence_group_keys, select_topk, plain_row_select,
                   branch_group_keys, qsa_branch_select, qsa_select, causal_tail, round_bf16)
+from .lmhead import lmhead_logits, lmhead_e2etv
 
 __all__ = [
     "rope", "rope_angles", "walk_ancestors", "tree_depths", "check_positions",
@@ -45,4 +46,5 @@ __all__ = [
     "gdn_replay", "update_counts", "conv_history", "branch_conv", "gdn_branch_conv",
     "rms_norm", "compress_group", "sequence_group_keys", "select_topk", "plain_row_select",
     "branch_group_keys", "qsa_branch_select", "qsa_select", "causal_tail", "round_bf16",
+    "lmhead_logits", "lmhead_e2etv",
 ]

@@ -150,6 +150,36 @@ class QsaConfig:
 
 
 @dataclass(frozen=True)
+class LmHeadConfig:
+    """LM head fused with E2E-TV: one trunk of L score rows plus R branches of
+    Wn nodes (parent map as for the loss), hidden size H, vocabulary V.
+
+    Value laws: draft and target hidden states N(0, 1) in bf16; both heads
+    N(0, (sd / sqrt(H))^2) in bf16, independent, so every logit is about
+    N(0, sd^2); anchors uniform without replacement in [P, L - 1); the target
+    row of a node is its parent's branch row, or the anchor's trunk row for a
+    node on the anchor (the score-row rule)."""
+
+    L: int
+    P: int
+    R: int
+    parent: Tuple[int, ...]
+    H: int
+    V: int
+    sd: float = 2.0
+    dtype: str = "bf16"
+    T: int = 1
+
+    @property
+    def Wn(self) -> int:
+        return len(self.parent)
+
+    @property
+    def B(self) -> int:
+        return self.R
+
+
+@dataclass(frozen=True)
 class Workload:
     cid: int
     name: str
@@ -157,6 +187,7 @@ class Workload:
     loss: Optional[LossConfig]
     gdn: Optional[GdnConfig] = None
     qsa: Optional[QsaConfig] = None
+    lmhead: Optional[LmHeadConfig] = None
 
 
 _C4P, _C4D = chain(4)
@@ -181,6 +212,7 @@ WORKLOADS = {
         LossConfig(R=64, parent=_C8P, V=VOCAB, dtype="bf16", recipe="noise"),
         GdnConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, H=32, D=128, dtype="bf16"),
         QsaConfig(T=1, L=4096, P=1024, B=64, parent=_C8P, Di=128, topk=64),
+        LmHeadConfig(L=4096, P=1024, R=64, parent=_C8P, H=4096, V=VOCAB),
     ),
     3: Workload(
         3, "batch8",
@@ -217,6 +249,10 @@ def shrink_attn(cfg: AttnConfig, **kw) -> AttnConfig:
 
 
 def shrink_loss(cfg: LossConfig, **kw) -> LossConfig:
+    return dataclasses.replace(cfg, **kw)
+
+
+def shrink_lmhead(cfg: LmHeadConfig, **kw) -> LmHeadConfig:
     return dataclasses.replace(cfg, **kw)
 
 

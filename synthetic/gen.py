@@ -29,7 +29,7 @@ from typing import Dict
 import numpy as np
 import torch
 
-from .configs import AttnConfig, GdnConfig, LossConfig, QsaConfig
+from .configs import AttnConfig, GdnConfig, LmHeadConfig, LossConfig, QsaConfig
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -41,6 +41,7 @@ _T_G_CKPT, _T_G_TK, _T_G_TV, _T_G_TA, _T_G_TB = 31, 32, 33, 34, 35
 _T_G_Q, _T_G_K, _T_G_V, _T_G_A, _T_G_B = 36, 37, 38, 39, 40
 _T_G_CX, _T_G_CTX, _T_G_CW = 41, 42, 43
 _T_Q_TRAW, _T_Q_TGK, _T_Q_X, _T_Q_Y, _T_Q_GAMMA = 51, 52, 53, 54, 55
+_T_L_HD, _T_L_HT, _T_L_WD, _T_L_WT = 61, 62, 63, 64
 
 
 def derive_seed(seed: int, cid: int, tensor: int) -> int:
@@ -283,4 +284,42 @@ def gen_qsa(cfg: QsaConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[s
     out["anchors"] = torch.from_numpy(anch).to(device)
     out["parent"] = torch.from_numpy(parent).to(device)
     out["pos"] = torch.from_numpy(np.ascontiguousarray(pos)).to(device)
+    return out
+
+
+def gen_lmhead(cfg: LmHeadConfig, seed: int = 0, device="cpu", cid: int = 0) -> Dict[str, torch.Tensor]:
+    """Inputs of the LM head fused with E2E-TV.
+
+    Layouts (row-major): h_draft [R][Wn][H]; h_target [L + R*Wn][H] (the
+    trunk's score rows, then every branch node's); w_draft, w_target [V][H]
+    (bf16); target_row [R][Wn] int32 (the parent's branch row L + r*Wn +
+    parent, or the anchor's trunk row); parent [R][Wn]; anchors [R]."""
+    dt = _DT[cfg.dtype]
+    R, Wn, H, V, L = cfg.R, cfg.Wn, cfg.H, cfg.V, cfg.L
+    g = lambda tid: _gen(device, seed, cid, tid)
+    scale = cfg.sd / float(np.sqrt(H))
+
+    def head(tid):
+        w = torch.empty((V, H), dtype=dt, device=device)
+        gw = g(tid)
+        for r0 in range(0, V, 16384):
+            r1 = min(V, r0 + 16384)
+            w[r0:r1].copy_(scale * torch.randn((r1 - r0, H), generator=gw, device=device, dtype=torch.float32))
+        return w
+
+    out = {
+        "h_draft": _normal((R * Wn, H), dt, device, g(_T_L_HD), 8192).view(R, Wn, H),
+        "h_target": _normal((L + R * Wn, H), dt, device, g(_T_L_HT), 8192),
+        "w_draft": head(_T_L_WD),
+        "w_target": head(_T_L_WT),
+    }
+    anch = anchors_for(cfg, seed, cid)[0]
+    par = np.asarray(cfg.parent, np.int64)
+    rows = np.empty((R, Wn), np.int32)
+    for r in range(R):
+        for j in range(Wn):
+            rows[r, j] = anch[r] if par[j] < 0 else L + r * Wn + par[j]
+    out["target_row"] = torch.from_numpy(rows).to(device)
+    out["parent"] = torch.from_numpy(np.broadcast_to(par.astype(np.int32), (R, Wn)).copy()).to(device)
+    out["anchors"] = torch.from_numpy(anch.astype(np.int32)).to(device)
     return out

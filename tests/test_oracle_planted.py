@@ -15,6 +15,7 @@ import pytest
 import oracle
 import test_oracle_e2etv as te
 import test_oracle_gdn as tg
+import test_oracle_lmhead as tl
 import test_oracle_prefill as tp
 import test_oracle_qsa as tq
 import test_oracle_tree_attention as tt
@@ -131,6 +132,12 @@ CASES = {
     "top-k in score order": (
         "oracle.qsa", "select_topk", "return np.sort(order[:k])", "return order[:k]",
         [lambda: tq.test_topk_matches_sorting_rule(3)]),
+    "head applied transposed": (
+        "oracle.lmhead", "lmhead_logits", "@ np.asarray(W, np.float64).T", "@ np.asarray(W, np.float64).T[::-1]",
+        [tl.test_logits_are_the_linear_map, tl.test_identity_head_is_e2etv_on_the_hidden_states]),
+    "target rows not gathered": (
+        "oracle.lmhead", "lmhead_e2etv", "ht = np.asarray(h_target, np.float64)[np.asarray(target_row).reshape(-1)]",
+        "ht = np.asarray(h_target, np.float64)[: R * Wn]", [tl.test_siblings_read_their_parents_row]),
     "bf16 rounding ties away from even": (
         "oracle.qsa", "round_bf16", "b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000",
         "b = (b + 0x8000) & 0xFFFF0000", [tq.test_round_bf16_ties_to_even]),
