@@ -23,7 +23,9 @@ cache (specopd_prefill_fwd) on the workload's trunks, and `gdn` the branch
 scoring of a linear-attention (GDN) target by indexed state replay
 (specopd_gdn_replay_fwd) on the workload's trunks and tree, and `qsa` the block
 selection of a sparse-attention (QSA) target with branch-consistent indexer
-groups (specopd_qsa_select_fwd).  `cpu_baseline` times
+groups (specopd_qsa_select_fwd), and `lmhead` the E2E-TV loss computed from
+the two models' LM heads without storing logits (specopd_lmhead_e2etv_fwd_bwd,
+on the 8B-layer shape).  `cpu_baseline` times
 the fp64 CPU oracle on a bounded sample of the same workload, on one core and
 on every usable core (reported, not a target).
 """
@@ -374,6 +376,61 @@ def bench_qsa(sd, wl, seed, steps, warmup, dev, stream):
     return res
 
 
+def bench_lmhead(sd, wl, seed, steps, warmup, dev, stream):
+    """The LM head fused with E2E-TV (specopd_lmhead_e2etv_fwd_bwd) on the
+    8B-layer shape: the branch rows' logits are formed from hidden states of
+    4096 by the drafter's and the target's heads over the 151,936-entry
+    vocabulary and never stored.  Algorithmic work: both logit matrices once,
+    2 x 2 N V H FLOPs; the call forms each three times (one per pass over
+    the vocabulary), so its executed matrix work is three times that."""
+    import torch
+    from synthetic import gen_lmhead
+    lc = wl.lmhead
+    li = gen_lmhead(lc, seed, device=dev, cid=wl.cid)
+    out = sd.lmhead_e2etv(li)
+
+    def call():
+        sd.lmhead_e2etv(li, ws=out["ws"], outs=out)
+
+    for _ in range(max(1, warmup)):
+        call()
+    n = max(1, min(steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / n
+    sd.specopd_kernel_timing(True)
+    for _ in range(n):
+        call()
+    torch.cuda.synchronize()
+    tot, cnt = sd.specopd_kernel_time(7)
+    sd.specopd_kernel_timing(False)
+    if sd.specopd_lmhead_e2etv_device_status(out["desc"], out["ws"]) != 0:
+        raise SystemExit("LM head + E2E-TV reported malformed branches")
+    ms = tot / cnt
+    N = lc.R * lc.Wn
+    alg = 2.0 * 2.0 * N * lc.V * lc.H
+    tf = alg / (ms / 1e3) / 1e12
+    res = {
+        "metric": "LM head + E2E-TV rows/s (logits never stored)", "value": N / (call_ms / 1e3),
+        "unit": "rows/s", "calls": n, "call_ms": call_ms,
+        "config": {"R": lc.R, "Wn": lc.Wn, "H": lc.H, "V": lc.V, "dtype": lc.dtype, "grad": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / BF16_PEAK_TFLOPS, "executed_tflops": 3.0 * tf,
+                     "executed_frac": 3.0 * tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "lmh_pass_kernel x3 + lse + scan (specopd_lmhead_e2etv_fwd_bwd)", "ms": ms,
+                     "alg_flops_per_launch": alg},
+    }
+    del li, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def profile_summary(tag, src_files):
     """Key/value lines of profiles/<tag>.txt when the kernel sources it names
     are unchanged since it was taken (its source_sha256), else None."""
@@ -592,6 +649,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the trunk-prefill measurement")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN branch-replay measurement")
     ap.add_argument("--no-qsa", action="store_true", help="skip the QSA block-selection measurement")
+    ap.add_argument("--no-lmhead", action="store_true",
+                    help="skip the LM head + E2E-TV measurement (8B-layer shape)")
     ap.add_argument("--eager", action="store_true",
                     help="time plain calls instead of replays of the step captured as a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -632,6 +691,9 @@ def main():
         res["gdn"] = bench_gdn(sd, wl, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
     if wl.qsa is not None and not args.no_qsa:
         res["qsa"] = bench_qsa(sd, wl, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
+    if not args.no_lmhead:
+        lw = wl if wl.lmhead is not None else WORKLOADS[2]
+        res["lmhead"] = bench_lmhead(sd, lw, args.seed, args.steps, args.warmup, dev, torch.cuda.current_stream())
     others = {}
     for c in [int(x) for x in args.also.split(",") if x.strip()]:
         if c == args.workload:

@@ -24,6 +24,11 @@
  *                           block selection of a sparse-attention (QSA)
  *                           target with branch-consistent indexer groups
  *                           (jaehun.me review, §3.2(b) and Fig. 4).
+ *   specopd_lmhead_e2etv_fwd_bwd
+ *                           the E2E-TV surrogate computed from the two
+ *                           models' LM heads without storing their logits
+ *                           (jaehun.me review, §3.3 and the §3.2(a) reading
+ *                           rule).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is DEVICE memory owned by the caller.  The library
@@ -540,6 +545,61 @@ specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const voi
                                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* LM head fused with the E2E-TV surrogate                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The E2E-TV surrogate of specopd_e2etv_fwd_bwd for logits that are the
+ * outputs of two linear LM heads (jaehun.me review, §3.3, Eqs. 8, 9, 13):
+ * z = h_draft W_draft^T and t = h_target[target_row] W_target^T, where a
+ * node is scored against the target row of its parent, or of its anchor's
+ * trunk position for a node on the anchor (the §3.2(a) reading rule, so
+ * siblings share one row; specopd_score_rows computes that index).  The
+ * logits are formed tile by tile on the matrix cores and never written: the
+ * call recomputes them in each of its three passes over the vocabulary
+ * (log-sum-exps, overlaps, gradient), three times the head products of
+ * forming them once, in exchange for no [N][V] logit traffic or storage.
+ *
+ *   h_draft    [R][Wn][H] bf16   the drafter's last hidden state per node
+ *   w_draft    [V][H] bf16       the drafter's head
+ *   h_target   [M][H] bf16       the target's last hidden state per score row
+ *   w_target   [V][H] bf16       the target's head (may equal w_draft)
+ *   target_row [R][Wn] int32     row of h_target that scores each node
+ *   parent     [R][Wn] int32     -1 on the anchor, else an earlier node
+ *   alpha_out, prefix_out [R][Wn] fp32 or NULL
+ *   loss_out   double[3]         loss, numerator, count (device memory)
+ *   grad_draft [R][Wn][V] fp32 or NULL (forward only): dLoss/dz, which a
+ *              linear head turns into the hidden-state gradient
+ *              (dLoss/dz) W_draft
+ * norm_count and grad_scale as for specopd_e2etv_desc.  Logits are fp32
+ * sums of bf16 products.  A branch with a parent that does not precede its
+ * child, or a node whose target row is outside [0, M), gets NaN outputs
+ * and is counted (specopd_lmhead_e2etv_device_status).  H must be a
+ * multiple of 16; pointers 16-byte aligned; outputs must not alias inputs.
+ */
+typedef struct {
+  int32_t R, Wn;        /* branches, nodes per branch (Wn <= 64)         */
+  int32_t V, H;         /* vocabulary, hidden size                      */
+  int32_t M;            /* rows of h_target                             */
+  double norm_count;    /* <= 0: R * Wn                                 */
+  float grad_scale;     /* 1 for the plain gradient                     */
+  uint32_t flags;       /* 0                                            */
+} specopd_lmhead_e2etv_desc;
+
+specopd_status specopd_lmhead_e2etv_workspace_size(const specopd_lmhead_e2etv_desc* desc, size_t* bytes);
+specopd_status specopd_lmhead_e2etv_fwd_bwd(const specopd_lmhead_e2etv_desc* desc, const void* h_draft,
+                                            const void* w_draft, const void* h_target,
+                                            const void* w_target, const int32_t* target_row,
+                                            const int32_t* parent, float* alpha_out, float* prefix_out,
+                                            double* loss_out, float* grad_draft, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+/* Waits for the stream; SPECOPD_ERR_DEVICE_VALIDATION with *bad > 0 when the
+ * last call on this workspace found malformed branches or target rows. */
+specopd_status specopd_lmhead_e2etv_device_status(const specopd_lmhead_e2etv_desc* desc,
+                                                  const void* workspace, size_t workspace_bytes,
+                                                  int32_t* bad, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Kernel timing, for measurement harnesses.
  *
  * specopd_kernel_timing(1) makes every later specopd_tree_attn_fwd,
@@ -549,14 +609,15 @@ specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const voi
  * E2E-TV kernel, without the small kernel that clears its counters; the
  * attention kernel of each prefilled trunk; the GDN replay kernel, without
  * the one that clears its counter; the GDN convolution kernel; the QSA
- * scoring kernel and the QSA top-k kernel), so that a harness can divide a kernel's algorithmic work
+ * scoring kernel and the QSA top-k kernel; the LM head + E2E-TV call from
+ * its first pass to its last), so that a harness can divide a kernel's algorithmic work
  * by that kernel's own duration.  specopd_kernel_timing(0) stops recording and
  * discards what was recorded.  The events belong to the library (a pool is
  * created when timing is switched on and kept for the process).
  *
  * specopd_kernel_time(which, &total_ms, &launches): which = 0 attention,
  * 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution, 5 QSA scores,
- * 6 QSA top-k.  Waits for the recorded events and returns the summed elapsed
+ * 6 QSA top-k, 7 LM head + E2E-TV.  Waits for the recorded events and returns the summed elapsed
  * milliseconds and the number of recorded launches.  Returns
  * SPECOPD_ERR_INVALID_ARGUMENT for another `which` or a null output pointer,
  * SPECOPD_ERR_HIP if an event cannot be created or read.  Not for use while

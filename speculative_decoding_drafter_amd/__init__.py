@@ -17,4 +17,6 @@ from ._lib import (  # noqa: F401
     gdn_replay, GdnConvDesc, gdn_conv_desc, specopd_gdn_conv_fwd, gdn_conv, SPECOPD_GDN_CONV_L2NORM,
     QsaDesc, qsa_desc, specopd_qsa_trunk_groups_fwd, specopd_qsa_workspace_size, specopd_qsa_select_fwd,
     specopd_qsa_device_status, qsa_trunk_groups, qsa_select,
+    LmHeadDesc, lmhead_desc, specopd_lmhead_e2etv_workspace_size, specopd_lmhead_e2etv_fwd_bwd,
+    specopd_lmhead_e2etv_device_status, lmhead_e2etv,
 )

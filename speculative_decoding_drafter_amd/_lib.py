@@ -43,6 +43,8 @@ EXPORTS = (
     "specopd_gdn_conv_fwd",
     "specopd_qsa_trunk_groups_fwd", "specopd_qsa_workspace_size", "specopd_qsa_select_fwd",
     "specopd_qsa_device_status",
+    "specopd_lmhead_e2etv_workspace_size", "specopd_lmhead_e2etv_fwd_bwd",
+    "specopd_lmhead_e2etv_device_status",
     "specopd_kernel_timing", "specopd_kernel_time",
     "specopd_status_string", "specopd_version",
 )
@@ -80,6 +82,11 @@ class QsaDesc(ctypes.Structure):
                 ("topk", c_int32), ("rope_base", c_float), ("eps", c_float), ("flags", c_uint32)]
 
 
+class LmHeadDesc(ctypes.Structure):
+    _fields_ = [("R", c_int32), ("Wn", c_int32), ("V", c_int32), ("H", c_int32), ("M", c_int32),
+                ("norm_count", c_double), ("grad_scale", c_float), ("flags", c_uint32)]
+
+
 class SpecopdError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -112,6 +119,9 @@ def _load():
     lib.specopd_qsa_workspace_size.argtypes = [POINTER(QsaDesc), POINTER(c_size_t)]
     lib.specopd_qsa_select_fwd.argtypes = [POINTER(QsaDesc)] + [P] * 11 + [P, c_size_t, P]
     lib.specopd_qsa_device_status.argtypes = [POINTER(QsaDesc), P, c_size_t, POINTER(c_int32), P]
+    lib.specopd_lmhead_e2etv_workspace_size.argtypes = [POINTER(LmHeadDesc), POINTER(c_size_t)]
+    lib.specopd_lmhead_e2etv_fwd_bwd.argtypes = [POINTER(LmHeadDesc)] + [P] * 10 + [P, c_size_t, P]
+    lib.specopd_lmhead_e2etv_device_status.argtypes = [POINTER(LmHeadDesc), P, c_size_t, POINTER(c_int32), P]
     lib.specopd_kernel_timing.argtypes = [c_int]
     lib.specopd_kernel_time.argtypes = [c_int, POINTER(c_double), POINTER(c_int)]
     lib.specopd_status_string.argtypes = [c_int]
@@ -143,7 +153,8 @@ def specopd_kernel_timing(enable: bool) -> None:
 
 def specopd_kernel_time(which: int):
     """(total ms, launches) recorded for the attention (0), E2E-TV (1), prefill (2),
-    GDN replay (3), GDN convolution (4), QSA scoring (5) or QSA top-k (6) kernel."""
+    GDN replay (3), GDN convolution (4), QSA scoring (5), QSA top-k (6) kernel, or the
+    LM head + E2E-TV call's passes (7)."""
     ms, n = c_double(0.0), c_int(0)
     st = LIB.specopd_kernel_time(int(which), ctypes.byref(ms), ctypes.byref(n))
     if st != SPECOPD_OK:
@@ -449,6 +460,62 @@ def qsa_select(inp: dict, topk: int, rope_base=10000.0, eps=0.0, ws=None, outs=N
     specopd_qsa_select_fwd(desc, inp["trunk_gk"], inp["trunk_raw"], x, inp["y"], inp["gamma"],
                            inp["anchors"], inp["parent"], inp["pos"], outs["sel"], outs["score"],
                            outs.get("bkey"), ws)
+    return dict(outs, desc=desc, ws=ws)
+
+
+def lmhead_desc(R, Wn, V, H, M, norm_count=0.0, grad_scale=1.0, flags=0):
+    return LmHeadDesc(R, Wn, V, H, M, norm_count, grad_scale, flags)
+
+
+def specopd_lmhead_e2etv_workspace_size(desc: LmHeadDesc) -> int:
+    n = c_size_t(0)
+    st = LIB.specopd_lmhead_e2etv_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_lmhead_e2etv_workspace_size")
+    return n.value
+
+
+def specopd_lmhead_e2etv_fwd_bwd(desc, h_draft, w_draft, h_target, w_target, target_row, parent, alpha,
+                                 prefix, loss, grad, ws, stream=None, raw_status=False):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = LIB.specopd_lmhead_e2etv_fwd_bwd(ctypes.byref(desc), _ptr(h_draft), _ptr(w_draft), _ptr(h_target),
+                                          _ptr(w_target), _ptr(target_row), _ptr(parent), _ptr(alpha),
+                                          _ptr(prefix), _ptr(loss), _ptr(grad), _ptr(ws), c_size_t(nbytes),
+                                          _stream(stream))
+    if raw_status:
+        return st
+    if st != SPECOPD_OK:
+        raise SpecopdError(st, "specopd_lmhead_e2etv_fwd_bwd")
+    return loss
+
+
+def specopd_lmhead_e2etv_device_status(desc, workspace, stream=None) -> int:
+    bad = c_int32(0)
+    st = LIB.specopd_lmhead_e2etv_device_status(ctypes.byref(desc), _ptr(workspace),
+                                                c_size_t(workspace.numel() * workspace.element_size()),
+                                                ctypes.byref(bad), _stream(stream))
+    if st not in (SPECOPD_OK, SPECOPD_ERR_DEVICE_VALIDATION):
+        raise SpecopdError(st, "specopd_lmhead_e2etv_device_status")
+    return bad.value
+
+
+def lmhead_e2etv(inp: dict, grad=True, norm_count=0.0, grad_scale=1.0, ws=None, outs=None):
+    """LM head + E2E-TV on generated inputs (dict of device tensors h_draft,
+    w_draft, h_target, w_target, target_row, parent); returns dict(alpha,
+    prefix, loss (double[3]), grad or None, desc, ws)."""
+    hd = inp["h_draft"]
+    R, Wn, H = hd.shape
+    V = inp["w_draft"].shape[0]
+    desc = lmhead_desc(R, Wn, V, H, inp["h_target"].shape[0], norm_count, grad_scale)
+    if ws is None:
+        ws = workspace(specopd_lmhead_e2etv_workspace_size(desc), hd.device)
+    if outs is None:
+        outs = {"alpha": torch.empty((R, Wn), dtype=torch.float32, device=hd.device),
+                "prefix": torch.empty((R, Wn), dtype=torch.float32, device=hd.device),
+                "loss": torch.zeros(4, dtype=torch.float64, device=hd.device),
+                "grad": torch.empty((R, Wn, V), dtype=torch.float32, device=hd.device) if grad else None}
+    specopd_lmhead_e2etv_fwd_bwd(desc, hd, inp["w_draft"], inp["h_target"], inp["w_target"], inp["target_row"],
+                                 inp["parent"], outs["alpha"], outs["prefix"], outs["loss"], outs.get("grad"), ws)
     return dict(outs, desc=desc, ws=ws)
 
 

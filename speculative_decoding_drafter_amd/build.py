@@ -30,7 +30,7 @@ COMMON = [
     "-I", os.path.join(HERE, "..", "include"),
 ]
 
-SOURCES = ["specopd_api.cpp", "e2etv.hip", "tree_attn.hip", "tree_attn_mfma.hip", "prefill.hip", "gdn.hip", "gdn_conv.hip", "qsa.hip"]
+SOURCES = ["specopd_api.cpp", "e2etv.hip", "tree_attn.hip", "tree_attn_mfma.hip", "prefill.hip", "gdn.hip", "gdn_conv.hip", "qsa.hip", "lmhead.hip"]
 
 # Matrix-core accumulators live in ordinary VGPRs (the AGPR half of the file
 # serves as extra room): with one wave per SIMD the attention kernel's

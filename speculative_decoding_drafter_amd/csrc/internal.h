@@ -225,12 +225,36 @@ hipError_t launch_qsa_trunk_groups(const specopd_qsa_desc& d, const void* raw, c
                                    hipStream_t s);
 hipError_t launch_qsa_select(const specopd_qsa_desc& d, const QsaCallArgs& a, hipStream_t s);
 
+// ---------------------------------------------------------------- LM head + E2E-TV
+// Workspace layout (offsets in bytes, each 256-aligned):
+//   bad    int32   [1]          malformed branches / out-of-range target rows
+//   partA  f32x4   [N][nch]     per 64-entry chunk: max and 2^x-sum of z, t
+//   nl     f32x2   [N]          log2-domain log-sum-exps
+//   partB  f32x2   [N][nch]     per chunk: alpha, G
+//   coef   f32x2   [N]          gradient coefficients
+//   numer  double  [R]          branch numerators
+struct LmhWs {
+  size_t bad, partA, nl, partB, coef, numer, total;
+  int nch;
+};
+LmhWs lmhead_ws_layout(const specopd_lmhead_e2etv_desc& d);
+struct LmhCallArgs {
+  const void *h_draft, *w_draft, *h_target, *w_target;
+  const int32_t *target_row, *parent;
+  float *alpha_out, *prefix_out;
+  double* loss_out;
+  float* grad;
+  char* ws;
+};
+hipError_t launch_lmhead_e2etv(const specopd_lmhead_e2etv_desc& d, const LmhCallArgs& a, hipStream_t s);
+
 // Kernel timing (specopd_kernel_timing): records an event on s before
 // (phase 0) or after (phase 1) the main kernel of call kind `which`
 // (0 attention, 1 E2E-TV, 2 prefill, 3 GDN replay, 4 GDN convolution,
-// 5 QSA scores, 6 QSA top-k) when timing is on;
+// 5 QSA scores, 6 QSA top-k, 7 LM head + E2E-TV from its first pass to its
+// last) when timing is on;
 // otherwise does nothing (also for a negative `which`).
-constexpr int kTimingKinds = 7;
+constexpr int kTimingKinds = 8;
 void timing_mark(int which, int phase, hipStream_t s);
 
 }  // namespace specopd

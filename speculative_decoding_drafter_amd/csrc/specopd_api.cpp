@@ -85,6 +85,21 @@ specopd_status check_qsa_desc(const specopd_qsa_desc* d) {
   return SPECOPD_OK;
 }
 
+specopd_status check_lmhead_desc(const specopd_lmhead_e2etv_desc* d) {
+  if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->R < 1 || d->Wn < 1 || d->V < 1 || d->H < 16 || d->M < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (d->H % 16 != 0) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->Wn > 64) return SPECOPD_ERR_UNSUPPORTED;
+  if (d->flags != 0) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!(isfinite(d->norm_count) && isfinite(d->grad_scale))) return SPECOPD_ERR_INVALID_ARGUMENT;
+  // grid (vocabulary tiles x row tiles) and element offsets
+  const double N = double(d->R) * d->Wn;
+  if (N > 2147483647.0 || N * d->V > 9.0e15 || double(d->V) * d->H > 9.0e15 || double(d->M) * d->H > 9.0e15 ||
+      N * d->H > 9.0e15 || ceil(double(d->V) / 128) * ceil(N / 128) * 256.0 > 2147483647.0)
+    return SPECOPD_ERR_UNSUPPORTED;  // the pass kernels' grid, in threads
+  return SPECOPD_OK;
+}
+
 specopd_status check_prefill_desc(const specopd_prefill_desc* d) {
   if (!d) return SPECOPD_ERR_INVALID_ARGUMENT;
   if (d->T < 1 || d->L < 1 || d->Hq < 1 || d->Hkv < 1 || d->D < 1) return SPECOPD_ERR_INVALID_ARGUMENT;
@@ -441,6 +456,61 @@ specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const voi
   if (hipMemcpy(&bad, static_cast<const char*>(workspace) + w.bad, sizeof(bad), hipMemcpyDeviceToHost) != hipSuccess)
     return SPECOPD_ERR_HIP;
   if (bad_branches) *bad_branches = bad;
+  return bad != 0 ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
+}
+
+specopd_status specopd_lmhead_e2etv_workspace_size(const specopd_lmhead_e2etv_desc* desc, size_t* bytes) {
+  specopd_status st = check_lmhead_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  if (!bytes) return SPECOPD_ERR_INVALID_ARGUMENT;
+  *bytes = lmhead_ws_layout(*desc).total;
+  return SPECOPD_OK;
+}
+
+specopd_status specopd_lmhead_e2etv_fwd_bwd(const specopd_lmhead_e2etv_desc* desc, const void* h_draft,
+                                            const void* w_draft, const void* h_target,
+                                            const void* w_target, const int32_t* target_row,
+                                            const int32_t* parent, float* alpha_out, float* prefix_out,
+                                            double* loss_out, float* grad_draft, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream) {
+  specopd_status st = check_lmhead_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const void* ins[] = {h_draft, w_draft, h_target, w_target, target_row, parent};
+  for (const void* p : ins)
+    if (!p || !aligned16(p)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  if (!loss_out || !aligned16(loss_out)) return SPECOPD_ERR_INVALID_ARGUMENT;
+  const void* outs[] = {alpha_out, prefix_out, loss_out, grad_draft};
+  for (int i = 0; i < 4; ++i) {
+    const void* o = outs[i];
+    if (!o) continue;
+    if (!aligned16(o)) return SPECOPD_ERR_INVALID_ARGUMENT;
+    for (const void* p : ins)
+      if (p == o) return SPECOPD_ERR_INVALID_ARGUMENT;
+    for (int j = 0; j < i; ++j)
+      if (outs[j] == o) return SPECOPD_ERR_INVALID_ARGUMENT;
+  }
+  const LmhWs w = lmhead_ws_layout(*desc);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  LmhCallArgs a{};
+  a.h_draft = h_draft; a.w_draft = w_draft; a.h_target = h_target; a.w_target = w_target;
+  a.target_row = target_row; a.parent = parent;
+  a.alpha_out = alpha_out; a.prefix_out = prefix_out; a.loss_out = loss_out; a.grad = grad_draft;
+  a.ws = static_cast<char*>(workspace);
+  return launch_lmhead_e2etv(*desc, a, stream) == hipSuccess ? SPECOPD_OK : SPECOPD_ERR_HIP;
+}
+
+specopd_status specopd_lmhead_e2etv_device_status(const specopd_lmhead_e2etv_desc* desc,
+                                                  const void* workspace, size_t workspace_bytes,
+                                                  int32_t* bad_out, hipStream_t stream) {
+  specopd_status st = check_lmhead_desc(desc);
+  if (st != SPECOPD_OK) return st;
+  const LmhWs w = lmhead_ws_layout(*desc);
+  if (!workspace || workspace_bytes < w.total || !aligned16(workspace)) return SPECOPD_ERR_WORKSPACE;
+  int32_t bad = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess) return SPECOPD_ERR_HIP;
+  if (hipMemcpy(&bad, static_cast<const char*>(workspace) + w.bad, sizeof(bad), hipMemcpyDeviceToHost) != hipSuccess)
+    return SPECOPD_ERR_HIP;
+  if (bad_out) *bad_out = bad;
   return bad != 0 ? SPECOPD_ERR_DEVICE_VALIDATION : SPECOPD_OK;
 }
 

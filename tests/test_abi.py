@@ -465,3 +465,67 @@ def test_qsa_workspace_and_status_errors():
         == sd.SPECOPD_ERR_INVALID_ARGUMENT
     assert sd.LIB.specopd_qsa_trunk_groups_fwd(ctypes.byref(d), P(FAKE), P(FAKE + 16), P(FAKE), P(None)) \
         == sd.SPECOPD_ERR_INVALID_ARGUMENT  # out aliases the raw keys
+
+
+def _ldesc(**kw):
+    base = dict(R=64, Wn=8, V=151936, H=4096, M=4608)
+    base.update(kw)
+    return sd.lmhead_desc(**base)
+
+
+_LNAMES = ("h_draft", "w_draft", "h_target", "w_target", "target_row", "parent", "alpha", "prefix", "loss", "grad")
+
+
+def _lcall(desc, ws_bytes=None, **over):
+    args = {n: FAKE + 16 * i for i, n in enumerate(_LNAMES)}
+    args["ws"] = FAKE + 4096
+    args.update(over)
+    if ws_bytes is None:
+        try:
+            ws_bytes = sd.specopd_lmhead_e2etv_workspace_size(desc)
+        except sd.SpecopdError:
+            ws_bytes = 1 << 40
+    P = ctypes.c_void_p
+    return sd.LIB.specopd_lmhead_e2etv_fwd_bwd(ctypes.byref(desc), *[P(args[n]) for n in _LNAMES], P(args["ws"]),
+                                               ctypes.c_size_t(ws_bytes), P(None))
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("H", 4100, sd.SPECOPD_ERR_UNSUPPORTED),       # not a multiple of 16
+    ("H", 8, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("V", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("M", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("Wn", 65, sd.SPECOPD_ERR_UNSUPPORTED),
+    ("R", 0, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("flags", 1, sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("norm_count", float("nan"), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    ("V", 2_000_000_000, sd.SPECOPD_ERR_UNSUPPORTED),
+])
+def test_lmhead_desc_errors(field, value, code):
+    d = _ldesc()
+    setattr(d, field, value)
+    assert _lcall(d) == code
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(h_draft=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(target_row=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),
+    (dict(loss=0), sd.SPECOPD_ERR_INVALID_ARGUMENT),           # the loss is always written
+    (dict(w_target=FAKE + 8), sd.SPECOPD_ERR_INVALID_ARGUMENT),  # misaligned
+    (dict(grad=FAKE), sd.SPECOPD_ERR_INVALID_ARGUMENT),         # grad aliases h_draft
+    (dict(prefix=FAKE + 16 * 6), sd.SPECOPD_ERR_INVALID_ARGUMENT),  # prefix aliases alpha
+    (dict(ws=0), sd.SPECOPD_ERR_WORKSPACE),
+])
+def test_lmhead_pointer_errors(over, code):
+    assert _lcall(_ldesc(), **over) == code
+
+
+def test_lmhead_workspace_and_status_errors():
+    d = _ldesc()
+    need = sd.specopd_lmhead_e2etv_workspace_size(d)
+    # per row and 64-entry chunk: 16 bytes of log-sum-exp partials and 8 of overlap partials
+    assert need >= 512 * ((151936 + 63) // 64) * 24
+    assert _lcall(d, ws_bytes=need - 1) == sd.SPECOPD_ERR_WORKSPACE
+    bad = ctypes.c_int32(0)
+    assert sd.LIB.specopd_lmhead_e2etv_device_status(ctypes.byref(d), ctypes.c_void_p(None), 0,
+                                                     ctypes.byref(bad), None) == sd.SPECOPD_ERR_WORKSPACE
