@@ -575,7 +575,9 @@ specopd_status specopd_qsa_device_status(const specopd_qsa_desc* desc, const voi
  * sums of bf16 products.  A branch with a parent that does not precede its
  * child, or a node whose target row is outside [0, M), gets NaN outputs
  * and is counted (specopd_lmhead_e2etv_device_status).  H must be a
- * multiple of 16; pointers 16-byte aligned; outputs must not alias inputs.
+ * multiple of 16 and each of V*H, M*H and R*Wn*H below 2^31 (else
+ * SPECOPD_ERR_UNSUPPORTED); pointers 16-byte aligned; outputs must not alias
+ * inputs.
  */
 typedef struct {
   int32_t R, Wn;        /* branches, nodes per branch (Wn <= 64)         */

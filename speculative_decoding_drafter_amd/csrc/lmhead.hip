@@ -27,10 +27,11 @@
 // workgroup of four waves covers 128 rows x 128 vocabulary entries, a wave
 // 64 rows x 64 entries of both z and t (eight 32 x 32 accumulators).  A = 32
 // head rows (vocabulary entries) x 16 hidden values, B = 16 hidden values x
-// 32 hidden-state rows, both loaded straight from memory in operand layout
-// (16 contiguous bytes per lane: hidden states and heads are both
-// hidden-contiguous), the next step's operands loaded while the current
-// step's products run.  Lane (r, h) then holds row r's logits for
+// 32 hidden-state rows, read from LDS in operand layout (16 contiguous
+// bytes per lane: hidden states and heads are both
+// hidden-contiguous, staged through LDS 32 hidden values at a time, the
+// next stage loading while the current one's products run).  Lane (r, h)
+// then holds row r's logits for
 // vocabulary entries 8(i/4) + 4h + i%4 of each 32-entry block, so a row's
 // reductions are in-lane sums plus one exchange with lane r + 32.
 #include <math.h>
@@ -48,6 +49,9 @@ namespace {
 constexpr int kChunk = 64;   // vocabulary entries per partial (one wave's span)
 constexpr int kTileV = 128;  // per workgroup
 constexpr int kTileR = 128;
+constexpr int kKc = 32;             // hidden values per LDS stage
+constexpr int kSrow = kKc + 8;      // LDS row stride (elements): 80 bytes, so the
+                                    // 32 rows an operand read touches spread over the banks
 
 struct LmhArgs {
   const uint16_t *hd, *wd, *ht, *wt;
@@ -77,8 +81,10 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s
   m = mm;
 }
 
+// Two workgroups per CU (2 x 80 KiB of LDS, at most 256 registers a wave),
+// so one workgroup's loads and barriers overlap the other's products.
 template <int PASS>
-__global__ __launch_bounds__(256) void lmh_pass_kernel(const LmhArgs a) {
+__global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
   const int rt = blockIdx.x % a.nrt, vt = blockIdx.x / a.nrt;
@@ -86,22 +92,36 @@ __global__ __launch_bounds__(256) void lmh_pass_kernel(const LmhArgs a) {
   const int v0 = vt * kTileV + 64 * (wave >> 1);
   const int H = a.H;
 
-  // operand rows of this lane, clamped into range (out-of-range results are
-  // never used)
-  const uint16_t *pwd[2], *pwt[2], *phd[2], *pht[2];
+  // Tiles of 128 rows x kKc hidden values of the four operands (draft and
+  // target head rows, draft and gathered target hidden-state rows) are
+  // staged in LDS, two stages deep: each thread loads 16 contiguous bytes of
+  // 8 tile rows per stage (4 lanes per 64-byte row segment), so a wave's
+  // load covers whole segments of 16 rows.  Out-of-range rows are clamped
+  // into range (their results are never used); hidden values past H load
+  // zeros.
+  __shared__ __attribute__((aligned(16))) uint16_t s_t[2][4][kTileR * kSrow];
+  // element offsets of this thread's 8 tile rows (32-bit: the host limits
+  // every operand to 2^31 elements), from the four operands' bases
+  const uint16_t* const bases[4] = {a.wd, a.wt, a.hd, a.ht};
+  uint32_t off[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int tile = q >> 1, r = (q & 1) * 64 + (tid >> 2);
+    int row;
+    if (tile < 2) {
+      row = min(vt * kTileV + r, a.V - 1);
+    } else {
+      row = min(rt * kTileR + r, a.N - 1);
+      if (tile == 3) {
+        const int tr = a.trow[row];
+        row = (tr >= 0 && tr < a.M) ? tr : 0;  // an invalid row is reported by the lse kernel
+      }
+    }
+    off[q] = uint32_t(row) * uint32_t(H) + uint32_t((tid & 3) * 8);
+  }
   int rowv[2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int v = min(v0 + 32 * x + r32, a.V - 1);
-    pwd[x] = a.wd + size_t(v) * H + 8 * h;
-    pwt[x] = a.wt + size_t(v) * H + 8 * h;
-    const int r = min(row0 + 32 * x + r32, a.N - 1);
-    rowv[x] = r;
-    int tr = a.trow[r];
-    tr = (tr >= 0 && tr < a.M) ? tr : 0;  // an invalid row is reported by the lse kernel
-    phd[x] = a.hd + size_t(r) * H + 8 * h;
-    pht[x] = a.ht + size_t(tr) * H + 8 * h;
-  }
+  for (int y = 0; y < 2; ++y) rowv[y] = min(row0 + 32 * y + r32, a.N - 1);
 
   f32x16 zacc[2][2], tacc[2][2];
 #pragma unroll
@@ -111,33 +131,50 @@ __global__ __launch_bounds__(256) void lmh_pass_kernel(const LmhArgs a) {
       zacc[x][y] = f32x16{};
       tacc[x][y] = f32x16{};
     }
-  bf16x8 Ad[2], At[2], Bd[2], Bt[2], nAd[2], nAt[2], nBd[2], nBt[2];
-  auto load = [&](int k, bf16x8(&ad)[2], bf16x8(&at)[2], bf16x8(&bd)[2], bf16x8(&bt)[2]) {
+  u32x4 st[8];
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      ad[x] = *reinterpret_cast<const bf16x8*>(pwd[x] + k);
-      at[x] = *reinterpret_cast<const bf16x8*>(pwt[x] + k);
-      bd[x] = *reinterpret_cast<const bf16x8*>(phd[x] + k);
-      bt[x] = *reinterpret_cast<const bf16x8*>(pht[x] + k);
+    for (int q = 0; q < 8; ++q)
+      st[q] = k0 + (tid & 3) * 8 < H ? *reinterpret_cast<const u32x4*>(bases[q >> 1] + off[q] + k0)
+                                     : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int tile = q >> 1, r = (q & 1) * 64 + (tid >> 2);
+      *reinterpret_cast<u32x4*>(&s_t[buf][tile][r * kSrow + (tid & 3) * 8]) = st[q];
     }
   };
-  load(0, Ad, At, Bd, Bt);
-  for (int k = 0; k < H; k += 16) {
-    if (k + 16 < H) load(k + 16, nAd, nAt, nBd, nBt);
+  const int ra = 64 * (wave >> 1) + r32;  // this lane's head row in the tile (+ 32 x)
+  const int rb = 64 * (wave & 1) + r32;   // this lane's hidden-state row (+ 32 y)
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int nst = (H + kKc - 1) / kKc;
+  for (int sidx = 0; sidx < nst; ++sidx) {
+    const int buf = sidx & 1;
+    if (sidx + 1 < nst) gload((sidx + 1) * kKc);
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
+    for (int ks = 0; ks < kKc / 16; ++ks) {
+      bf16x8 Ad[2], At[2], Bd[2], Bt[2];
+      const int ko = 16 * ks + 8 * h;
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        zacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ad[x], Bd[y], zacc[x][y], 0, 0, 0);
-        tacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[x], Bt[y], tacc[x][y], 0, 0, 0);
+      for (int x = 0; x < 2; ++x) {
+        Ad[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][0][(ra + 32 * x) * kSrow + ko]);
+        At[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][1][(ra + 32 * x) * kSrow + ko]);
+        Bd[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][2][(rb + 32 * x) * kSrow + ko]);
+        Bt[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][3][(rb + 32 * x) * kSrow + ko]);
       }
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      Ad[x] = nAd[x];
-      At[x] = nAt[x];
-      Bd[x] = nBd[x];
-      Bt[x] = nBt[x];
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          zacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ad[x], Bd[y], zacc[x][y], 0, 0, 0);
+          tacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[x], Bt[y], tacc[x][y], 0, 0, 0);
+        }
     }
+    if (sidx + 1 < nst) lstore(buf ^ 1);
+    __syncthreads();
   }
 
   const int chunk = v0 / kChunk;
