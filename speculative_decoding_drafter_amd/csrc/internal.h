@@ -233,8 +233,9 @@ hipError_t launch_qsa_select(const specopd_qsa_desc& d, const QsaCallArgs& a, hi
 //   partB  f32x2   [N][nch]     per chunk: alpha, G
 //   coef   f32x2   [N]          gradient coefficients
 //   numer  double  [R]          branch numerators
+//   bits   uint32  [N][nch][2]  the indicator [q < p] per element (pass B -> C)
 struct LmhWs {
-  size_t bad, partA, nl, partB, coef, numer, total;
+  size_t bad, partA, nl, partB, coef, numer, bits, total;
   int nch;
 };
 LmhWs lmhead_ws_layout(const specopd_lmhead_e2etv_desc& d);

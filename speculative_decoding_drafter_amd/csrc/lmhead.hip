@@ -18,10 +18,11 @@
 //   pass B       per (row, chunk): partial alpha and G;
 //   scan kernel  per branch: alpha and G summed in chunk order (fp64), prefix
 //                products, suffix sums, each row's gradient coefficients;
-//   pass C       the gradient c q_u ([q_u < p_u] - G), written once;
+//   pass C       the gradient c q_u ([q_u < p_u] - G), written once; it forms
+//                only z, reading the indicator from the bits pass B wrote;
 //   final        the loss from the branch numerators in branch order.
 // Every pass forms the same tiles in the same order, so the three passes see
-// bitwise the same logits and the indicator [q < p] is decided identically.
+// bitwise the same logits; the indicator [q < p] is decided once, in pass B.
 //
 // Matrix-core tiles (v_mfma_f32_32x32x16_bf16, lane l = r + 32h): a
 // workgroup of four waves covers 128 rows x 128 vocabulary entries, a wave
@@ -64,6 +65,7 @@ struct LmhArgs {
   f32x2* nl;     // [N] log2-domain log-sum-exps of z and t
   f32x2* partB;  // [N][nch] (alpha, G)
   f32x2* coef;   // [N] gradient coefficients for [q<p] = 1 / 0
+  uint32_t* bits;  // [N][nch][2] the indicator [q<p] of every element, from pass B
   double* numer; // [R]
   int R, Wn, V, H, M, N, nch, nrt;
   double count;
@@ -131,16 +133,21 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
       zacc[x][y] = f32x16{};
       tacc[x][y] = f32x16{};
     }
+  // pass C forms only z: the indicator [q < p] comes from pass B's bits
+  constexpr bool kT = PASS != 2;
+  auto used = [&](int q) { return kT || (q >> 1) == 0 || (q >> 1) == 2; };
   u32x4 st[8];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      st[q] = k0 + (tid & 3) * 8 < H ? *reinterpret_cast<const u32x4*>(bases[q >> 1] + off[q] + k0)
-                                     : u32x4{0u, 0u, 0u, 0u};
+      if (used(q))
+        st[q] = k0 + (tid & 3) * 8 < H ? *reinterpret_cast<const u32x4*>(bases[q >> 1] + off[q] + k0)
+                                       : u32x4{0u, 0u, 0u, 0u};
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      if (!used(q)) continue;
       const int tile = q >> 1, r = (q & 1) * 64 + (tid >> 2);
       *reinterpret_cast<u32x4*>(&s_t[buf][tile][r * kSrow + (tid & 3) * 8]) = st[q];
     }
@@ -161,16 +168,19 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         Ad[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][0][(ra + 32 * x) * kSrow + ko]);
-        At[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][1][(ra + 32 * x) * kSrow + ko]);
         Bd[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][2][(rb + 32 * x) * kSrow + ko]);
-        Bt[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][3][(rb + 32 * x) * kSrow + ko]);
+        if constexpr (kT) {
+          At[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][1][(ra + 32 * x) * kSrow + ko]);
+          Bt[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][3][(rb + 32 * x) * kSrow + ko]);
+        }
       }
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) {
           zacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ad[x], Bd[y], zacc[x][y], 0, 0, 0);
-          tacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[x], Bt[y], tacc[x][y], 0, 0, 0);
+          if constexpr (kT)
+            tacc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(At[x], Bt[y], tacc[x][y], 0, 0, 0);
         }
     }
     if (sidx + 1 < nst) lstore(buf ^ 1);
@@ -213,6 +223,7 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
       const float nlz = -l[0], nlt = -l[1];
       if constexpr (PASS == 1) {
         float al = 0.f, g = 0.f;
+        uint32_t ind = 0u;  // bit 16 x + i: [q < p] of accumulator element (x, i)
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -223,14 +234,18 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
               const float e = fast_exp2(fminf(lq, lp));
               al += e;
               g += lq < lp ? e : 0.f;
+              ind |= uint32_t(lq < lp) << (16 * x + i);
             }
         al += __shfl_xor(al, 32, 64);
         g += __shfl_xor(g, 32, 64);
+        if (rok) a.bits[(size_t(row) * a.nch + chunk) * 2 + h] = ind;
         if (rok && h == 0) a.partB[size_t(row) * a.nch + chunk] = f32x2{al, g};
       } else {
         const f32x2 c = a.coef[rowv[y]];
         float* grow = a.grad + size_t(rowv[y]) * a.V;
         const bool vec = (a.V & 3) == 0;
+        const uint32_t ind = rok ? a.bits[(size_t(row) * a.nch + chunk) * 2 + h] : 0u;
+        (void)nlt;
 #pragma unroll
         for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -239,8 +254,7 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float lq = __builtin_fmaf(zacc[x][y][4 * q4 + e], kLog2e, nlz);
-              const float lp = __builtin_fmaf(tacc[x][y][4 * q4 + e], kLog2e, nlt);
-              gv[e] = fast_exp2(lq) * (lq < lp ? c[0] : c[1]);
+              gv[e] = fast_exp2(lq) * (((ind >> (16 * x + 4 * q4 + e)) & 1u) ? c[0] : c[1]);
             }
             const int vb = vocab(x, 4 * q4);
             if (!rok) continue;
@@ -360,7 +374,8 @@ LmhWs lmhead_ws_layout(const specopd_lmhead_e2etv_desc& d) {
   w.partB = align_up(w.nl + N * 8, 256);
   w.coef = align_up(w.partB + N * w.nch * 8, 256);
   w.numer = align_up(w.coef + N * 8, 256);
-  w.total = align_up(w.numer + size_t(d.R) * 8, 256);
+  w.bits = align_up(w.numer + size_t(d.R) * 8, 256);
+  w.total = align_up(w.bits + N * w.nch * 8, 256);
   return w;
 }
 
@@ -383,6 +398,7 @@ hipError_t launch_lmhead_e2etv(const specopd_lmhead_e2etv_desc& d, const LmhCall
   a.partB = reinterpret_cast<f32x2*>(c.ws + w.partB);
   a.coef = reinterpret_cast<f32x2*>(c.ws + w.coef);
   a.numer = reinterpret_cast<double*>(c.ws + w.numer);
+  a.bits = reinterpret_cast<uint32_t*>(c.ws + w.bits);
   a.R = d.R;
   a.Wn = d.Wn;
   a.V = d.V;
