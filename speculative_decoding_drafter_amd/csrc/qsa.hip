@@ -22,7 +22,8 @@
 //                            stand in the four raw slots), scores the cached
 //                            trunk groups on the matrix cores
 //                            (v_mfma_f32_32x32x16_bf16, A = 32 group keys
-//                            straight from memory, B = the rotated queries,
+//                            staged per wave through LDS from whole-row
+//                            loads, B = the rotated queries,
 //                            32 nodes per row block) and the branch's own
 //                            groups with wave dot products; every row's
 //                            candidate scores go to the workspace.
@@ -151,7 +152,7 @@ constexpr int qsa_sy_stride() { return DI + 8; }
 
 template <int DI>
 __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
-  constexpr int H = DI / 2, NS = DI / 16, SY = qsa_sy_stride<DI>();
+  constexpr int H = DI / 2, NS = DI / 16, SY = qsa_sy_stride<DI>(), SK = qsa_sy_stride<DI>();
   extern __shared__ __attribute__((aligned(16))) uint16_t qsa_smem[];
   __shared__ int s_par[64], s_pos[64];
   __shared__ unsigned char s_at[64][64];  // s_at[j][d]: j's ancestor at depth d (self at depth(j))
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
   const int Wn = a.Wn, Wp = (Wn + 31) & ~31;
   uint16_t* const sy = qsa_smem;          // [Wp][SY] rotated queries (zero rows past Wn)
   uint16_t* const sk = sy + Wp * SY;      // [Wn][DI] keys of the groups nodes complete
+  uint16_t* const sk_tiles = sk + Wn * DI;  // [4 waves][32][SK] each wave's staged trunk tile
   const int anchor = a.anchors[tb];
   const size_t node0 = size_t(tb) * Wn;
 
@@ -271,27 +273,43 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
         qop[rb][s] = rb < nb ? *reinterpret_cast<const bf16x8*>(sy + (rb * 32 + r32) * SY + 16 * s + 8 * h)
                              : bf16x8{};
     const uint16_t* gkt = a.trunk_gk + size_t(t) * a.ng * DI;
-    // tiles split + nsplit * (wave + 4 m); the next tile's keys are loaded
-    // while the current one is multiplied
-    const int tstep = 4 * a.nsplit;
-    auto load_tile = [&](int tt, bf16x8(&kop)[NS]) {
-      const int g = min(tt * 32 + r32, a.ng - 1);  // gT <= ng, so ng >= 1 here
-      const bf16x8* src = reinterpret_cast<const bf16x8*>(gkt + size_t(g) * DI + 8 * h);
+    // tiles split + nsplit * (wave + 4 m).  A tile's 32 group keys are read
+    // with whole-row loads (DI / 8 lanes per key row, so a wave load covers
+    // 512 / DI complete rows) into registers, written to this wave's LDS
+    // block, and read back in operand layout; the next tile's rows are in
+    // flight while the current one is multiplied.  Waves run different tile
+    // counts, so the block is private to the wave and only the wave's own
+    // LDS accesses are ordered (lgkmcnt waits), never a workgroup barrier.
+    constexpr int LPR = DI / 8, RPL = 64 / LPR, NLD = 32 / RPL;  // lanes per row, rows per load, loads
+    uint16_t* const kw = sk_tiles + wave * (32 * SK);
+    const int lrow = lane / LPR, lcol = (lane % LPR) * 8;
+    u32x4 kreg[NLD];
+    auto gload = [&](int tt) {
 #pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) kop[s2] = src[2 * s2];
+      for (int j = 0; j < NLD; ++j) {
+        const int g = min(tt * 32 + j * RPL + lrow, a.ng - 1);  // gT <= ng, so ng >= 1 here
+        kreg[j] = *reinterpret_cast<const u32x4*>(gkt + size_t(g) * DI + lcol);
+      }
     };
+    const int tstep = 4 * a.nsplit;
     int tt = split + a.nsplit * wave;
-    bf16x8 kcur[NS], knext[NS];
-    if (tt < ntile) load_tile(tt, kcur);
+    if (tt < ntile) gload(tt);
     for (; tt < ntile; tt += tstep) {
-      if (tt + tstep < ntile) load_tile(tt + tstep, knext);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the previous tile's operand reads are done
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) *reinterpret_cast<u32x4*>(kw + (j * RPL + lrow) * SK + lcol) = kreg[j];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (tt + tstep < ntile) gload(tt + tstep);
+      bf16x8 kop[NS];
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) kop[s2] = *reinterpret_cast<const bf16x8*>(kw + r32 * SK + 16 * s2 + 8 * h);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         if (rb >= nb) break;
         f32x16 acc = {};
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kcur[s2], qop[rb][s2], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[s2], qop[rb][s2], acc, 0, 0, 0);
         const int row = rb * 32 + r32;
         if (row < Wn) {
           float* dst = sc0 + size_t(row) * a.Gs;
@@ -308,8 +326,6 @@ __global__ __launch_bounds__(256) void qsa_score_kernel(const QsaKArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int s2 = 0; s2 < NS; ++s2) kcur[s2] = knext[s2];
     }
   }
   // the branch's own groups g in [gT, G_j): the key the ancestor at position
@@ -472,7 +488,7 @@ hipError_t allow_lds(const void* kernel, size_t dyn, size_t stat) {
 template <int DI>
 size_t score_lds_bytes(int Wn) {
   const int Wp = (Wn + 31) & ~31;
-  return size_t(Wp) * qsa_sy_stride<DI>() * 2 + size_t(Wn) * DI * 2;
+  return size_t(Wp) * qsa_sy_stride<DI>() * 2 + size_t(Wn) * DI * 2 + size_t(4 * 32) * qsa_sy_stride<DI>() * 2;
 }
 
 template <int DI>
