@@ -416,6 +416,7 @@ def bench_lmhead(sd, wl, seed, steps, warmup, dev, stream):
     N = lc.R * lc.Wn
     alg = 2.0 * 2.0 * N * lc.V * lc.H
     tf = alg / (ms / 1e3) / 1e12
+    pl = profile_summary("lmhead_pass_layer8b", LMH_SRC)
     res = {
         "metric": "LM head + E2E-TV rows/s (logits never stored)", "value": N / (call_ms / 1e3),
         "unit": "rows/s", "calls": n, "call_ms": call_ms,
@@ -423,6 +424,8 @@ def bench_lmhead(sd, wl, seed, steps, warmup, dev, stream):
         "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / BF16_PEAK_TFLOPS, "executed_tflops": 2.5 * tf,
                      "executed_frac": 2.5 * tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "pass_b_hbm_bytes": _counter(pl, "hbm_bytes_per_launch"),
+                     "pass_b_mfma_util_pct": _counter(pl, "mfma_util_pct"),
                      "kernel": "lmh_pass_kernel x3 + lse + scan (specopd_lmhead_e2etv_fwd_bwd)", "ms": ms,
                      "alg_flops_per_launch": alg},
     }
@@ -465,6 +468,12 @@ GDN_SRC = ["speculative_decoding_drafter_amd/csrc/gdn.hip",
 
 
 QSA_SRC = ["speculative_decoding_drafter_amd/csrc/qsa.hip",
+           "speculative_decoding_drafter_amd/csrc/device_common.h",
+           "speculative_decoding_drafter_amd/csrc/internal.h",
+           "speculative_decoding_drafter_amd/build.py"]
+
+
+LMH_SRC = ["speculative_decoding_drafter_amd/csrc/lmhead.hip",
            "speculative_decoding_drafter_amd/csrc/device_common.h",
            "speculative_decoding_drafter_amd/csrc/internal.h",
            "speculative_decoding_drafter_amd/build.py"]
