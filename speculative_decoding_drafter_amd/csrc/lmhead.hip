@@ -89,7 +89,12 @@ template <int PASS>
 __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
-  const int rt = blockIdx.x % a.nrt, vt = blockIdx.x / a.nrt;
+  // Workgroup b runs on XCD b mod 8.  The row tiles of one vocabulary tile
+  // get consecutive slots of one XCD, so they run side by side and share the
+  // head tile through that XCD's L2 instead of each fetching it.
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int rt = slot % a.nrt, vt = 8 * (slot / a.nrt) + xcd;
+  if (vt * kTileV >= a.V) return;  // padding of the vocabulary tiles to a multiple of 8
   const int row0 = rt * kTileR + 64 * (wave & 1);
   const int v0 = vt * kTileV + 64 * (wave >> 1);
   const int H = a.H;
@@ -410,7 +415,7 @@ hipError_t launch_lmhead_e2etv(const specopd_lmhead_e2etv_desc& d, const LmhCall
   a.count = d.norm_count > 0.0 ? d.norm_count : double(a.N);
   a.grad_scale = d.grad_scale;
   const int nvt = (d.V + kTileV - 1) / kTileV;
-  const dim3 grid(unsigned(size_t(nvt) * a.nrt));
+  const dim3 grid(unsigned(size_t((nvt + 7) / 8 * 8) * a.nrt));
   lmh_zero_kernel<<<1, 1, 0, s>>>(a.bad);
   timing_mark(7, 0, s);
   lmh_pass_kernel<0><<<grid, 256, 0, s>>>(a);

@@ -95,7 +95,7 @@ specopd_status check_lmhead_desc(const specopd_lmhead_e2etv_desc* d) {
   // grid (vocabulary tiles x row tiles) and element offsets
   const double N = double(d->R) * d->Wn;
   if (N > 2147483647.0 || N * d->V > 9.0e15 || double(d->V) * d->H > 9.0e15 || double(d->M) * d->H > 9.0e15 ||
-      N * d->H > 9.0e15 || ceil(double(d->V) / 128) * ceil(N / 128) * 256.0 > 2147483647.0)
+      N * d->H > 9.0e15 || (ceil(double(d->V) / 128) + 8) * ceil(N / 128) * 256.0 > 2147483647.0)
     return SPECOPD_ERR_UNSUPPORTED;  // the pass kernels' grid, in threads
   // the pass kernels address each operand with 32-bit element offsets
   if (double(d->V) * d->H >= 2147483648.0 || double(d->M) * d->H >= 2147483648.0 || N * d->H >= 2147483648.0)
