@@ -63,6 +63,26 @@ int main(void) {
   EXPECT(specopd_prefill_workspace_size(&pd, &bytes), SPECOPD_ERR_INVALID_ARGUMENT);
 
   EXPECT(specopd_kernel_time(3, NULL, NULL), SPECOPD_ERR_INVALID_ARGUMENT);
+  EXPECT(specopd_kernel_time(8, NULL, NULL), SPECOPD_ERR_INVALID_ARGUMENT);
+
+  specopd_qsa_desc qd = {1, 4096, 8, 10, 128, 64, 10000.0f, 0.0f, 0u};
+  EXPECT(specopd_qsa_workspace_size(&qd, &bytes), SPECOPD_OK);
+  EXPECT(specopd_qsa_select_fwd(&qd, fake, fake, fake, fake, (const float*)fake, (const int32_t*)fake,
+                                (const int32_t*)fake, (const int32_t*)fake, NULL, (float*)fake, NULL,
+                                fake, bytes, NULL),
+         SPECOPD_ERR_INVALID_ARGUMENT); /* no selection output */
+  EXPECT(specopd_qsa_trunk_groups_fwd(&qd, fake, (const float*)fake, fake, NULL),
+         SPECOPD_ERR_INVALID_ARGUMENT); /* the cache aliases the raw keys */
+  qd.Di = 96;
+  EXPECT(specopd_qsa_workspace_size(&qd, &bytes), SPECOPD_ERR_UNSUPPORTED);
+
+  specopd_lmhead_e2etv_desc ld = {64, 8, 151936, 4096, 4608, 0.0, 1.0f, 0u};
+  EXPECT(specopd_lmhead_e2etv_workspace_size(&ld, &bytes), SPECOPD_OK);
+  EXPECT(specopd_lmhead_e2etv_fwd_bwd(&ld, fake, fake, fake, fake, (const int32_t*)fake,
+                                      (const int32_t*)fake, NULL, NULL, NULL, NULL, fake, bytes, NULL),
+         SPECOPD_ERR_INVALID_ARGUMENT); /* no loss output */
+  ld.H = 4100;
+  EXPECT(specopd_lmhead_e2etv_workspace_size(&ld, &bytes), SPECOPD_ERR_UNSUPPORTED);
 
   if (fails) fprintf(stderr, "%d mismatches\n", fails);
   return fails ? 1 : 0;
