@@ -86,7 +86,7 @@ __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s
 // Two workgroups per CU (2 x 80 KiB of LDS, at most 256 registers a wave),
 // so one workgroup's loads and barriers overlap the other's products.
 template <int PASS>
-__global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
+__global__ __launch_bounds__(256, PASS == 2 ? 3 : 2) void lmh_pass_kernel(const LmhArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, r32 = lane & 31;
   // Workgroup b runs on XCD b mod 8.  The row tiles of one vocabulary tile
@@ -106,7 +106,14 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
   // load covers whole segments of 16 rows.  Out-of-range rows are clamped
   // into range (their results are never used); hidden values past H load
   // zeros.
-  __shared__ __attribute__((aligned(16))) uint16_t s_t[2][4][kTileR * kSrow];
+  // pass C forms only z: the indicator [q < p] comes from pass B's bits, so
+  // it stages two operands (half the LDS: three workgroups per CU)
+  constexpr bool kT = PASS != 2;
+  constexpr int NT = kT ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t s_t[2][NT][kTileR * kSrow];
+  // LDS slot of operand tile 0..3 (draft head, target head, draft hidden,
+  // target hidden)
+  auto lslot = [](int tile) { return kT ? tile : (tile == 0 ? 0 : 1); };
   // element offsets of this thread's 8 tile rows (32-bit: the host limits
   // every operand to 2^31 elements), from the four operands' bases
   const uint16_t* const bases[4] = {a.wd, a.wt, a.hd, a.ht};
@@ -138,8 +145,6 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
       zacc[x][y] = f32x16{};
       tacc[x][y] = f32x16{};
     }
-  // pass C forms only z: the indicator [q < p] comes from pass B's bits
-  constexpr bool kT = PASS != 2;
   auto used = [&](int q) { return kT || (q >> 1) == 0 || (q >> 1) == 2; };
   u32x4 st[8];
   auto gload = [&](int k0) {
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
     for (int q = 0; q < 8; ++q) {
       if (!used(q)) continue;
       const int tile = q >> 1, r = (q & 1) * 64 + (tid >> 2);
-      *reinterpret_cast<u32x4*>(&s_t[buf][tile][r * kSrow + (tid & 3) * 8]) = st[q];
+      *reinterpret_cast<u32x4*>(&s_t[buf][lslot(tile)][r * kSrow + (tid & 3) * 8]) = st[q];
     }
   };
   const int ra = 64 * (wave >> 1) + r32;  // this lane's head row in the tile (+ 32 x)
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void lmh_pass_kernel(const LmhArgs a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         Ad[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][0][(ra + 32 * x) * kSrow + ko]);
-        Bd[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][2][(rb + 32 * x) * kSrow + ko]);
+        Bd[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][lslot(2)][(rb + 32 * x) * kSrow + ko]);
         if constexpr (kT) {
           At[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][1][(ra + 32 * x) * kSrow + ko]);
           Bt[x] = *reinterpret_cast<const bf16x8*>(&s_t[buf][3][(rb + 32 * x) * kSrow + ko]);
