@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
   extern __shared__ uint32_t qsa_keys[];  // [Gs]
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_cnt[2][4];
-  __shared__ uint32_t s_dig, s_rem;
+  __shared__ uint32_t s_dig, s_rem, s_all;
   const size_t row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k = a.topk;
@@ -399,7 +399,9 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
       if (i < n) qsa_keys[i] = order_key(v[e]);
     }
   }
-  // the k-th largest key, 8 bits at a time from the top
+  // the k-th largest key, 8 bits at a time from the top; when every key of
+  // the bin that holds it is kept, its lower bits do not matter and the
+  // passes stop
   uint32_t prefix = 0u, pmask = 0u, rem = uint32_t(k);
   for (int shift = 24; shift >= 0; shift -= 8) {
     hist[tid] = 0u;
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
         if (cum < rem && rem <= cum + c[b]) {
           s_dig = uint32_t(4 * lane + b);
           s_rem = rem - cum;
+          s_all = rem == cum + c[b];
         }
         cum += c[b];
       }
@@ -436,15 +439,17 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
     prefix |= s_dig << shift;
     pmask |= 0xffu << shift;
     rem = s_rem;
+    if (s_all) break;
   }
-  const uint32_t tau = prefix;
-  // keys above tau, then the first `rem` keys equal to it, in group order
+  // keys whose resolved bits are above prefix, then the first `rem` keys
+  // whose resolved bits equal it, in group order: k in all
   uint32_t gt_seen = 0u, eq_seen = 0u;
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int c0 = 0; c0 < n; c0 += 256) {
     const int i = c0 + tid;
     const uint32_t u = i < n ? qsa_keys[i] : 0u;
-    const bool gt = i < n && u > tau, eq = i < n && u == tau;
+    const uint32_t um = u & pmask;
+    const bool gt = i < n && um > prefix, eq = i < n && um == prefix;
     const unsigned long long bg = __ballot(gt), be = __ballot(eq);
     if (lane == 0) {
       s_cnt[0][wave] = uint32_t(__popcll(bg));
@@ -464,7 +469,9 @@ __global__ __launch_bounds__(256) void qsa_topk_kernel(const QsaKArgs a) {
     const uint32_t gb = gt_seen + og + uint32_t(__popcll(bg & below));
     const uint32_t eb = eq_seen + oe + uint32_t(__popcll(be & below));
     if (gt || (eq && eb < rem)) {
-      const uint32_t o = gb + (eb < rem ? eb : rem);
+      // below k by construction; the bound keeps a row's writes in its own
+      // k slots whatever the keys
+      const uint32_t o = min(gb + (eb < rem ? eb : rem), uint32_t(k - 1));
       so[o] = i;
       vo[o] = key_value(u);
     }
