@@ -29,7 +29,7 @@
 //                            candidate scores go to the workspace.
 //   qsa_topk_kernel          one workgroup per node: the row's scores into LDS
 //                            as order-preserving integer keys, the k-th
-//                            largest key by four 8-bit radix passes
+//                            largest key by up to four 8-bit radix passes
 //                            (histograms with LDS atomics, digit found by a
 //                            wave suffix scan), then the kept groups written
 //                            in increasing group order by ballot prefix sums
